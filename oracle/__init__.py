@@ -1,0 +1,30 @@
+"""CPU oracle for the FlashAttention forward path -- TEST INFRASTRUCTURE ONLY.
+
+This package is a plain, slow, obviously correct fp64 NumPy implementation of
+what the GPU library computes.  It exists to check the GPU path.  Only the test
+suite, the smoke check and the benchmark's CPU-baseline leg may import it; the
+product library and its Python binding never do, and the oracle imports
+nothing from them.
+
+Definition followed (page "Intro to FlashAttention on Ascend CANN", sections
+"where the traditional implementation is slow" and "the first pitfall"):
+attention is softmax(Q K^T * scale) V computed with the full score matrix
+materialised; the tiled method with an online softmax is stated there to reach
+the same result as the standard softmax.  The causal mask (same page, the
+paragraph on fusing the causal mask) lets each query see only keys at or before
+its own position.
+
+Every function in this package is pinned by CPU tests against closed forms,
+invariants and a brute-force per-query loop; none is "parity unpinned".
+"""
+
+from .attention import (  # noqa: F401
+    bf16_bits_to_f64,
+    visible_mask,
+    softmax_probs,
+    attention_one,
+    attention_dense,
+    attention_varlen,
+    attention_query,
+)
+from .layout import unpad_gather, pad_scatter  # noqa: F401
