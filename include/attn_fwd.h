@@ -1,0 +1,162 @@
+/*
+ * attn_fwd.h -- C ABI of the MI355X (gfx950) FlashAttention forward library.
+ *
+ * The library computes O = softmax(scale * Q K^T) V per (sequence, query head)
+ * without materialising the score matrix, for dense batched inputs and for
+ * variable-length packed inputs, plus the row gather/scatter that moves packed
+ * rows between the padded and the compact layouts.
+ *
+ * Sources of the operations (web pages, cited by title and section):
+ *  - "Intro to FlashAttention on Ascend CANN" (ai6s.net): the standard
+ *    definition (section on where the traditional implementation is slow), the
+ *    blockwise computation with an online softmax that keeps a running row max
+ *    m and row sum d (sections "tiled computation" and "the first pitfall"),
+ *    and the fused causal mask that skips masked positions (paragraph on the
+ *    ops-transformer source).
+ *  - "Lesson 5: IAW model FA2 vs FA3 measured": the packed path of section 1
+ *    (padded (B, total_len, H, D) -> unpad gather by indices -> varlen
+ *    attention on (total_valid, H, D) -> pad scatter by indices) and the
+ *    kernels of section 2 and section 6 that perform those moves.
+ *
+ * Conventions shared by every entry point:
+ *  - Every tensor pointer is a DEVICE pointer owned by the caller.  The library
+ *    allocates nothing, frees nothing and never synchronises the stream.
+ *  - bfloat16 tensors are passed as raw 16-bit storage (const void*).
+ *  - `stream` is a hipStream_t cast to void*; NULL means the default stream.
+ *    Work is enqueued asynchronously on it.
+ *  - All argument checks run on the host before anything is enqueued.  On any
+ *    error nothing is launched and the status says why.  Device-side faults (for
+ *    example cu_seqlens that do not match the tensors) surface at the caller's
+ *    next synchronisation; the preconditions below say what must hold.
+ *  - Zero work (no sequences, no rows, zero-length tensors) returns ATTN_OK
+ *    without launching.
+ *  - No exception crosses the ABI.  The library keeps no per-call state; calls
+ *    on different streams from different host threads are safe.
+ */
+#ifndef ATTN_FWD_H
+#define ATTN_FWD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL = 1,        /* a required pointer is NULL */
+  ATTN_ERR_SHAPE = 2,       /* a size is negative or sizes disagree */
+  ATTN_ERR_UNSUPPORTED = 3, /* head_dim not in {32,64,128,256}, scale <= 0 or not finite, ... */
+  ATTN_ERR_ALIGN = 4,       /* a pointer or row size is not 16-byte aligned */
+  ATTN_ERR_HIP = 5          /* the HIP runtime rejected the launch */
+} attn_status_t;
+
+/*
+ * attn_fwd_varlen -- attention over variable-length sequences packed back to back.
+ *
+ * Passage: page "Lesson 5: IAW model FA2 vs FA3 measured", section 1 (the
+ * varlen attention on the compact tensor); the computation is the one of page
+ * "Intro to FlashAttention on Ascend CANN" named in the file header.
+ *
+ * q    (total_q, num_heads_q, head_dim) bf16, row-major, contiguous.
+ * k, v (total_k, num_heads_k, head_dim) bf16, row-major, contiguous.
+ * cu_seqlens_q, cu_seqlens_k: device int32 arrays of num_seqs+1 offsets;
+ *      sequence s owns query rows [cu_seqlens_q[s], cu_seqlens_q[s+1]) and key
+ *      rows [cu_seqlens_k[s], cu_seqlens_k[s+1]).  Preconditions: element 0 is
+ *      0, offsets never decrease, the last equals total_q (resp. total_k), and
+ *      no query length exceeds max_seqlen.  Zero-length sequences are allowed.
+ * max_seqlen: an upper bound on every query length (host value; sizes the grid).
+ * scale: multiplies the raw scores q.k (use 1/sqrt(head_dim)); must be > 0 and finite.
+ * causal: nonzero => key j is visible to query i when j <= i + (Lk - Lq)
+ *      (bottom-right alignment; with Lq == Lk this is j <= i).
+ * out  (total_q, num_heads_q, head_dim) fp32, written once per element.
+ * lse  (num_heads_q, total_q) fp32 natural-log log-sum-exp of the scaled
+ *      visible scores, or NULL to skip it.  A query that sees no key gets out
+ *      = 0 and lse = -inf.
+ * Grouped-query attention: num_heads_q must be a multiple of num_heads_k;
+ * query head h reads key/value head h / (num_heads_q / num_heads_k).
+ * head_dim must be 32, 64, 128 or 256.  Every pointer must be 16-byte aligned.
+ */
+attn_status_t attn_fwd_varlen(const void* q, const void* k, const void* v,
+                              const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                              int32_t num_seqs, int32_t total_q, int32_t total_k,
+                              int32_t num_heads_q, int32_t num_heads_k, int32_t head_dim,
+                              int32_t max_seqlen, float scale, int32_t causal,
+                              float* out, float* lse, void* stream);
+
+/*
+ * attn_fwd_dense -- attention over a dense batch of equal-length sequences.
+ *
+ * Passage: page "Intro to FlashAttention on Ascend CANN", section "how to use
+ * it" (dense q, k, v with an is_causal flag) and the definition named in the
+ * file header; page "Lesson 5: IAW model FA2 vs FA3 measured", section 7 (the
+ * dense ViT attention).
+ *
+ * q   (batch, seqlen_q, num_heads_q, head_dim) bf16
+ * k,v (batch, seqlen_k, num_heads_k, head_dim) bf16
+ * out (batch, seqlen_q, num_heads_q, head_dim) fp32
+ * strides: NULL for contiguous tensors in the layouts above, else a host array
+ *      of 12 element strides {q_b, q_s, q_h, k_b, k_s, k_h, v_b, v_s, v_h,
+ *      o_b, o_s, o_h}; the head_dim stride is always 1, every stride must be a
+ *      multiple of 8 elements (16 bytes of bf16) and of 4 for out.
+ * lse (batch, num_heads_q, seqlen_q) fp32 contiguous, or NULL.
+ * scale, causal, head_dim, grouped-query heads and the fully-masked-row rule
+ * are as for attn_fwd_varlen.
+ */
+attn_status_t attn_fwd_dense(const void* q, const void* k, const void* v,
+                             int32_t batch, int32_t seqlen_q, int32_t seqlen_k,
+                             int32_t num_heads_q, int32_t num_heads_k, int32_t head_dim,
+                             const int64_t* strides, float scale, int32_t causal,
+                             float* out, float* lse, void* stream);
+
+/*
+ * attn_unpad_gather -- copy the rows named by `indices` into a compact tensor.
+ *
+ * Passage: page "Lesson 5: IAW model FA2 vs FA3 measured", section 1 (unpad:
+ * gather rows by indices into (total_valid, H, D)) and section 2 (the gather
+ * kernels that perform it).
+ *
+ * For each of the n_tensors (1..3) pairs: dst[t] row r = src[t] row indices[r],
+ * for r < n_valid.  A row is row_bytes bytes (H * D * element size); src[t]
+ * holds n_rows_src rows, dst[t] holds n_valid rows.  `src` and `dst` are HOST
+ * arrays of n_tensors device pointers; every tensor shares `indices` (device
+ * int32, n_valid entries).  All q, k and v of one packed batch move in one
+ * launch.  row_bytes must be a positive multiple of 16; pointers 16-byte
+ * aligned.  An index outside [0, n_rows_src) yields a zero row (never an
+ * out-of-bounds read).  The copy is bit-exact.
+ */
+attn_status_t attn_unpad_gather(const void* const* src, void* const* dst, int32_t n_tensors,
+                                const int32_t* indices, int32_t n_valid, int32_t n_rows_src,
+                                int64_t row_bytes, void* stream);
+
+/*
+ * attn_pad_scatter -- put compact rows back into the padded layout.
+ *
+ * Passage: page "Lesson 5: IAW model FA2 vs FA3 measured", section 1 (pad:
+ * scatter rows back to (B, total_len, H, D) by indices) and section 6 (the
+ * fill and index kernels of the pad step).
+ *
+ * dst row indices[r] = src row r for r < n_valid; every other dst row (of
+ * n_rows_total) is written with +0.0 bytes.  One pass writes each dst byte
+ * exactly once, so no separate fill is needed.  Precondition: `indices`
+ * (device int32, n_valid entries) is strictly increasing; entries outside
+ * [0, n_rows_total) are ignored.  row_bytes must be a positive multiple of
+ * 16; pointers 16-byte aligned.  The copy is bit-exact.
+ */
+attn_status_t attn_pad_scatter(const void* src, void* dst, const int32_t* indices,
+                               int32_t n_valid, int32_t n_rows_total, int64_t row_bytes,
+                               void* stream);
+
+/* Human-readable text of a status code (static storage, never NULL). */
+const char* attn_status_str(attn_status_t s);
+
+/* ABI version of this header; bumped on any incompatible change. */
+int32_t attn_abi_version(void);
+
+#define ATTN_FWD_ABI_VERSION 1
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_FWD_H */

@@ -15,8 +15,8 @@ from __future__ import annotations
 import numpy as np
 
 
-def _rows(x: np.ndarray, n_rows: int) -> np.ndarray:
-    return np.ascontiguousarray(x).reshape(n_rows, -1)
+def _rows(x: np.ndarray, n_rows: int, row_elems: int) -> np.ndarray:
+    return np.ascontiguousarray(x).reshape(n_rows, row_elems)
 
 
 def unpad_gather(src: np.ndarray, indices: np.ndarray, row_shape) -> np.ndarray:
@@ -27,7 +27,7 @@ def unpad_gather(src: np.ndarray, indices: np.ndarray, row_shape) -> np.ndarray:
     """
     row_elems = int(np.prod(row_shape))
     n_rows = src.size // row_elems
-    rows = _rows(src, n_rows)
+    rows = _rows(src, n_rows, row_elems)
     out = np.empty((len(indices), row_elems), dtype=src.dtype)
     for r, idx in enumerate(np.asarray(indices, dtype=np.int64)):
         out[r] = rows[idx]
@@ -38,8 +38,9 @@ def pad_scatter(src: np.ndarray, indices: np.ndarray, n_rows_total: int) -> np.n
     """dst = zeros(n_rows_total rows); dst[indices[r]] = src[r] for every r."""
     n_valid = len(indices)
     row_shape = src.shape[1:]
-    rows = _rows(src, n_valid)
-    out = np.zeros((n_rows_total, rows.shape[1]), dtype=src.dtype)
+    row_elems = int(np.prod(row_shape))
+    rows = _rows(src, n_valid, row_elems)
+    out = np.zeros((n_rows_total, row_elems), dtype=src.dtype)
     for r, idx in enumerate(np.asarray(indices, dtype=np.int64)):
         out[idx] = rows[r]
     return out.reshape((n_rows_total,) + tuple(row_shape))

@@ -1,0 +1,53 @@
+"""Helpers shared by the GPU tests: device transfer and the parity bar."""
+
+from __future__ import annotations
+
+import numpy as np
+
+# Parity bar for floating point outputs (bf16 inputs, fp32 outputs):
+# max |O - O_ref| <= 2e-2, mean |O - O_ref| <= 2e-3, |LSE - LSE_ref| <= 1e-3.
+O_MAX_ABS = 2e-2
+O_MEAN_ABS = 2e-3
+LSE_MAX_ABS = 1e-3
+
+
+def dev_bf16(bits: np.ndarray):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.to("cuda").view(torch.bfloat16)
+
+
+def dev_i32(x: np.ndarray):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).to("cuda")
+
+
+def host(t) -> np.ndarray:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def check_o(o_gpu: np.ndarray, o_ref: np.ndarray, what: str = "O") -> dict:
+    assert o_gpu.shape == o_ref.shape, (o_gpu.shape, o_ref.shape)
+    assert not np.isnan(o_gpu).any(), f"{what}: NaN in GPU output"
+    err = np.abs(o_gpu.astype(np.float64) - o_ref)
+    mx = float(err.max()) if err.size else 0.0
+    mean = float(err.mean()) if err.size else 0.0
+    assert mx <= O_MAX_ABS, f"{what}: max abs err {mx:.3e} > {O_MAX_ABS}"
+    assert mean <= O_MEAN_ABS, f"{what}: mean abs err {mean:.3e} > {O_MEAN_ABS}"
+    return {"max": mx, "mean": mean}
+
+
+def check_lse(l_gpu: np.ndarray, l_ref: np.ndarray, what: str = "LSE") -> float:
+    assert l_gpu.shape == l_ref.shape, (l_gpu.shape, l_ref.shape)
+    assert not np.isnan(l_gpu).any(), f"{what}: NaN"
+    fin = np.isfinite(l_ref)
+    assert np.array_equal(np.isfinite(l_gpu), fin), f"{what}: finiteness differs"
+    assert np.array_equal(l_gpu[~fin], l_ref[~fin].astype(np.float32)), f"{what}: -inf rows differ"
+    if not fin.any():
+        return 0.0
+    e = float(np.abs(l_gpu[fin].astype(np.float64) - l_ref[fin]).max())
+    assert e <= LSE_MAX_ABS, f"{what}: max abs err {e:.3e} > {LSE_MAX_ABS}"
+    return e

@@ -1,0 +1,121 @@
+"""C ABI checks that need no GPU: the library loads, exports every entry point
+declared in include/attn_fwd.h, and rejects bad arguments with the documented
+status codes before touching the device."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from tiled_attention_fwd_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn_fwd.h")
+
+OK, NULL, SHAPE, UNSUP, ALIGN = 0, 1, 2, 3, 4
+P = 0x100000  # a 16-byte aligned fake device address: never dereferenced by these calls
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(attn_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_header_declares_the_four_calls():
+    names = declared_functions()
+    for n in ("attn_fwd_varlen", "attn_fwd_dense", "attn_unpad_gather", "attn_pad_scatter"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(declared_functions()) <= set(_lib.SIGNATURES)
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lib.attn_abi_version() == 1
+    for s in range(6):
+        assert lib.attn_status_str(s)
+    assert b"unknown" in lib.attn_status_str(99)
+
+
+def varlen(lib, **kw):
+    a = dict(q=P, k=P, v=P, cq=P, ck=P, nseq=2, tq=64, tk=64, hq=4, hkv=2, d=128, maxs=32,
+             scale=0.125, causal=1, out=P, lse=P)
+    a.update(kw)
+    return lib.attn_fwd_varlen(a["q"], a["k"], a["v"], a["cq"], a["ck"], a["nseq"], a["tq"], a["tk"],
+                               a["hq"], a["hkv"], a["d"], a["maxs"], a["scale"], a["causal"],
+                               a["out"], a["lse"], None)
+
+
+def test_varlen_validation(lib):
+    assert varlen(lib, d=48) == UNSUP
+    assert varlen(lib, d=16) == UNSUP
+    assert varlen(lib, scale=0.0) == UNSUP
+    assert varlen(lib, scale=-1.0) == UNSUP
+    assert varlen(lib, scale=float("inf")) == UNSUP
+    assert varlen(lib, scale=float("nan")) == UNSUP
+    assert varlen(lib, hq=6, hkv=4) == SHAPE
+    assert varlen(lib, hkv=0) == SHAPE
+    assert varlen(lib, nseq=-1) == SHAPE
+    assert varlen(lib, tq=-5) == SHAPE
+    assert varlen(lib, maxs=0) == SHAPE
+    assert varlen(lib, q=None) == NULL
+    assert varlen(lib, out=None) == NULL
+    assert varlen(lib, cq=None) == NULL
+    assert varlen(lib, k=None) == NULL
+    assert varlen(lib, q=P + 2) == ALIGN
+    assert varlen(lib, out=P + 8) == ALIGN
+    assert varlen(lib, lse=P + 2) == ALIGN
+    # zero work succeeds without launching (no device needed)
+    assert varlen(lib, nseq=0) == OK
+    assert varlen(lib, tq=0) == OK
+    assert varlen(lib, hq=0) == OK
+
+
+def dense(lib, strides=None, **kw):
+    a = dict(q=P, k=P, v=P, b=2, sq=16, sk=16, hq=4, hkv=4, d=64, scale=0.125, causal=0, out=P, lse=P)
+    a.update(kw)
+    return lib.attn_fwd_dense(a["q"], a["k"], a["v"], a["b"], a["sq"], a["sk"], a["hq"], a["hkv"],
+                              a["d"], strides, a["scale"], a["causal"], a["out"], a["lse"], None)
+
+
+def test_dense_validation(lib):
+    assert dense(lib, d=96) == UNSUP
+    assert dense(lib, hq=4, hkv=3) == SHAPE
+    assert dense(lib, b=-1) == SHAPE
+    assert dense(lib, q=None) == NULL
+    assert dense(lib, v=None) == NULL
+    assert dense(lib, k=P + 4) == ALIGN
+    bad = (ctypes.c_int64 * 12)(*([8] * 8 + [4] + [4] * 3))
+    assert dense(lib, strides=ctypes.cast(bad, ctypes.c_void_p)) == ALIGN
+    neg = (ctypes.c_int64 * 12)(*([8] * 11 + [-4]))
+    assert dense(lib, strides=ctypes.cast(neg, ctypes.c_void_p)) == SHAPE
+    assert dense(lib, b=0) == OK
+    assert dense(lib, sq=0) == OK
+
+
+def test_gather_scatter_validation(lib):
+    arr = (ctypes.c_void_p * 3)(P, P, P)
+    pa = ctypes.cast(arr, ctypes.c_void_p)
+    assert lib.attn_unpad_gather(pa, pa, 0, P, 4, 8, 256, None) == SHAPE
+    assert lib.attn_unpad_gather(pa, pa, 4, P, 4, 8, 256, None) == SHAPE
+    assert lib.attn_unpad_gather(pa, pa, 3, P, 4, 8, 100, None) == ALIGN
+    assert lib.attn_unpad_gather(pa, pa, 3, P, -1, 8, 256, None) == SHAPE
+    assert lib.attn_unpad_gather(pa, pa, 3, None, 4, 8, 256, None) == NULL
+    assert lib.attn_unpad_gather(pa, pa, 3, P, 0, 8, 256, None) == OK
+    mis = (ctypes.c_void_p * 3)(P, P + 8, P)
+    assert lib.attn_unpad_gather(pa, ctypes.cast(mis, ctypes.c_void_p), 3, P, 4, 8, 256, None) == ALIGN
+    assert lib.attn_pad_scatter(P, P, P, 5, 4, 256, None) == SHAPE
+    assert lib.attn_pad_scatter(P, P, P, 4, 8, 72, None) == ALIGN
+    assert lib.attn_pad_scatter(P, None, P, 4, 8, 256, None) == NULL
+    assert lib.attn_pad_scatter(None, P, P, 4, 8, 256, None) == NULL
+    assert lib.attn_pad_scatter(P, P, P, 0, 0, 256, None) == OK

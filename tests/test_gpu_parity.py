@@ -1,0 +1,341 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Sizes span several query and key tiles and leave ragged tails.  Every case
+uses seeded synthetic inputs from synth/; expected values come only from
+oracle/.
+"""
+
+from __future__ import annotations
+
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from synth import gen
+from tests.gpu_util import check_lse, check_o, dev_bf16, dev_i32, host
+
+pytestmark = pytest.mark.gpu
+
+D_ALL = [32, 64, 128, 256]
+
+
+def api():
+    import tiled_attention_fwd_amd as t
+    return t
+
+
+def run_varlen(w, causal=None, return_lse=True):
+    t = api()
+    causal = w.causal if causal is None else causal
+    o, lse = t.attn_fwd_varlen(dev_bf16(w.q), dev_bf16(w.k), dev_bf16(w.v),
+                               dev_i32(w.cu_seqlens_q), dev_i32(w.cu_seqlens_k), w.max_seqlen,
+                               scale=float(w.scale), causal=causal, return_lse=return_lse)
+    return host(o), (host(lse) if lse is not None else None)
+
+
+def run_dense(w, return_lse=True):
+    t = api()
+    o, lse = t.attn_fwd_dense(dev_bf16(w.q), dev_bf16(w.k), dev_bf16(w.v), scale=float(w.scale),
+                              causal=w.causal, return_lse=return_lse)
+    return host(o), (host(lse) if lse is not None else None)
+
+
+# ----------------------------------------------------------------------------- varlen
+@pytest.mark.parametrize("d", D_ALL)
+@pytest.mark.parametrize("causal", [True, False])
+def test_varlen_ragged_gqa(d, causal):
+    lens = [1, 7, 64, 100, 129, 300, 33]
+    w = gen.make_varlen(f"vr{d}", 100 + d, lens, 4, 2, d, causal)
+    o, lse = run_varlen(w)
+    o_ref, lse_ref = oracle.attention_varlen(w.q, w.k, w.v, w.cu_seqlens_q, w.cu_seqlens_k,
+                                             w.scale, causal)
+    print(d, causal, check_o(o, o_ref), check_lse(lse, lse_ref))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [True, False])
+def test_varlen_lq_ne_lk_and_empty_sequences(d, causal):
+    lq = [5, 130, 0, 64, 3, 0]
+    lk = [9, 70, 12, 200, 0, 0]
+    w = gen.make_varlen("ne", 200 + d, lq, 2, 2, d, causal, lengths_k=lk)
+    o, lse = run_varlen(w)
+    o_ref, lse_ref = oracle.attention_varlen(w.q, w.k, w.v, w.cu_seqlens_q, w.cu_seqlens_k,
+                                             w.scale, causal)
+    print(check_o(o, o_ref), check_lse(lse, lse_ref))
+
+
+def test_varlen_without_lse():
+    w = gen.make_varlen("nolse", 301, [70, 5], 2, 1, 128, True)
+    o, lse = run_varlen(w, return_lse=False)
+    assert lse is None
+    o_ref, _ = oracle.attention_varlen(w.q, w.k, w.v, w.cu_seqlens_q, w.cu_seqlens_k, w.scale, True)
+    check_o(o, o_ref)
+
+
+def test_varlen_32x64_full_size():
+    w = gen.build_workload("varlen_32x64")
+    o, lse = run_varlen(w)
+    o_ref, lse_ref = oracle.attention_varlen(w.q, w.k, w.v, w.cu_seqlens_q, w.cu_seqlens_k,
+                                             w.scale, True)
+    print(check_o(o, o_ref), check_lse(lse, lse_ref))
+
+
+# ----------------------------------------------------------------------------- dense
+@pytest.mark.parametrize("d", D_ALL)
+@pytest.mark.parametrize("causal", [True, False])
+def test_dense_ragged(d, causal):
+    w = gen.make_dense(f"dn{d}", 400 + d, 2, 200, 200, 3, 3, d, causal)
+    o, lse = run_dense(w)
+    o_ref, lse_ref = oracle.attention_dense(w.q, w.k, w.v, w.scale, causal)
+    print(check_o(o, o_ref), check_lse(lse, lse_ref))
+
+
+def test_dense_gqa_lq_ne_lk():
+    w = gen.make_dense("dg", 501, 2, 77, 190, 8, 2, 128, True)
+    o, lse = run_dense(w)
+    o_ref, lse_ref = oracle.attention_dense(w.q, w.k, w.v, w.scale, True)
+    print(check_o(o, o_ref), check_lse(lse, lse_ref))
+
+
+def test_dense_strided_views():
+    import torch
+    t = api()
+    w = gen.make_dense("st", 502, 2, 150, 150, 4, 4, 64, False)
+    # BHSD storage viewed as BSHD: non-contiguous seq/head strides
+    q = dev_bf16(np.ascontiguousarray(w.q.transpose(0, 2, 1, 3))).permute(0, 2, 1, 3)
+    k = dev_bf16(np.ascontiguousarray(w.k.transpose(0, 2, 1, 3))).permute(0, 2, 1, 3)
+    v = dev_bf16(np.ascontiguousarray(w.v.transpose(0, 2, 1, 3))).permute(0, 2, 1, 3)
+    out = torch.empty((2, 4, 150, 64), dtype=torch.float32, device="cuda").permute(0, 2, 1, 3)
+    o, lse = t.attn_fwd_dense(q, k, v, scale=float(w.scale), causal=False, out=out)
+    o_ref, lse_ref = oracle.attention_dense(w.q, w.k, w.v, w.scale, False)
+    check_o(host(o.contiguous()), o_ref)
+    check_lse(host(lse), lse_ref)
+
+
+# ----------------------------------------------------------------------------- closed forms on GPU
+@pytest.mark.parametrize("d", [64, 128])
+def test_zero_query_gives_prefix_mean_and_log_count(d):
+    w = gen.make_varlen("z", 600 + d, [300, 17], 2, 2, d, True)
+    w.q[:] = 0
+    o, lse = run_varlen(w)
+    v = oracle.bf16_bits_to_f64(w.v)
+    c = w.cu_seqlens_q
+    for s in range(2):
+        n = np.arange(1, c[s + 1] - c[s] + 1)
+        np.testing.assert_allclose(lse[:, c[s]:c[s + 1]], np.log(n)[None, :].repeat(2, 0),
+                                   rtol=0, atol=1e-5)
+        pref = np.cumsum(v[c[s]:c[s + 1]], axis=0) / n[:, None, None]
+        check_o(o[c[s]:c[s + 1]], pref)
+
+
+def test_onehot_future_target_is_masked():
+    # Hadamard keys: each query's dominant key is in its future; a leaking mask
+    # would return that key's value row instead of the prefix mean.
+    d, L = 64, 64
+    h = np.array([[1.0]])
+    while h.shape[0] < d:
+        h = np.block([[h, h], [h, -h]])
+    kbits = gen.bf16_bits_from_f32((3.0 * h[:L]).astype(np.float32))
+    tgt = [min(i + 1 + (i % 5), L - 1) for i in range(L)]
+    qf = 3.0 * h[tgt]
+    qf[L - 1] = 0.0
+    w = gen.make_varlen("oh", 700, [L], 1, 1, d, True)
+    w.q[:, 0] = gen.bf16_bits_from_f32(qf.astype(np.float32))
+    w.k[:, 0] = kbits
+    o, lse = run_varlen(w)
+    v = oracle.bf16_bits_to_f64(w.v)[:, 0]
+    pref = np.cumsum(v, axis=0) / np.arange(1, L + 1)[:, None]
+    check_o(o[:, 0], pref)
+    np.testing.assert_allclose(lse[0], np.log(np.arange(1, L + 1)), rtol=0, atol=1e-4)
+
+
+# ----------------------------------------------------------------------------- scheduling invariance
+def test_sequence_alone_equals_sequence_in_pack_bitwise():
+    os.environ["ATTN_FWD_TILE"] = "0"
+    try:
+        lens = [100, 257, 31, 512]
+        w = gen.make_varlen("pk", 800, lens, 4, 4, 128, True)
+        o_pack, l_pack = run_varlen(w)
+        c = w.cu_seqlens_q
+        for s, L in enumerate(lens):
+            ws = gen.make_varlen("one", 1, [L], 4, 4, 128, True)
+            ws.q[:] = w.q[c[s]:c[s + 1]]
+            ws.k[:] = w.k[c[s]:c[s + 1]]
+            ws.v[:] = w.v[c[s]:c[s + 1]]
+            o1, l1 = run_varlen(ws)
+            assert np.array_equal(o1, o_pack[c[s]:c[s + 1]])
+            assert np.array_equal(l1, l_pack[:, c[s]:c[s + 1]])
+            # dense path on the same sequence gives the same bits too
+            wd = gen.make_dense("dd", 1, 1, L, L, 4, 4, 128, True)
+            wd.q[0] = ws.q
+            wd.k[0] = ws.k
+            wd.v[0] = ws.v
+            od, ld = run_dense(wd)
+            assert np.array_equal(od[0], o1) and np.array_equal(ld[0], l1)
+    finally:
+        del os.environ["ATTN_FWD_TILE"]
+
+
+def test_repeat_runs_are_bitwise_identical():
+    w = gen.make_varlen("rep", 900, [1000, 3, 600], 8, 2, 128, True)
+    a = run_varlen(w)
+    b = run_varlen(w)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_future_perturbation_leaves_prefix_bitwise():
+    w = gen.make_varlen("fp", 901, [400], 2, 2, 128, True)
+    o1, l1 = run_varlen(w)
+    w.k[250:] = gen.bf16_bits_from_f32(np.full(w.k[250:].shape, 7.0, np.float32))
+    w.v[250:] = gen.bf16_bits_from_f32(np.full(w.v[250:].shape, -3.0, np.float32))
+    o2, l2 = run_varlen(w)
+    assert np.array_equal(o1[:250], o2[:250]) and np.array_equal(l1[:, :250], l2[:, :250])
+
+
+@pytest.mark.parametrize("policy", ["0", "1"])
+def test_every_compiled_tile_policy(policy):
+    os.environ["ATTN_FWD_TILE"] = policy
+    try:
+        for d in D_ALL:
+            w = gen.make_varlen("pol", 1000 + d, [150, 64, 1, 90], 2, 1, d, True)
+            o, lse = run_varlen(w)
+            o_ref, lse_ref = oracle.attention_varlen(w.q, w.k, w.v, w.cu_seqlens_q,
+                                                     w.cu_seqlens_k, w.scale, True)
+            check_o(o, o_ref)
+            check_lse(lse, lse_ref)
+    finally:
+        del os.environ["ATTN_FWD_TILE"]
+
+
+# ----------------------------------------------------------------------------- gather / scatter
+def test_gather_scatter_bit_exact_with_nan_bits_and_bad_index():
+    import torch
+    t = api()
+    r = np.random.Generator(np.random.PCG64(1100))
+    n_rows, hd = 300, (3, 40)
+    srcs = [r.integers(0, 2 ** 16, size=(n_rows,) + hd, dtype=np.uint16) for _ in range(3)]
+    srcs[0][5] = 0x7FC1  # NaN bit patterns copy unchanged
+    idx = np.sort(r.choice(n_rows, size=123, replace=False)).astype(np.int32)
+    outs = t.attn_unpad_gather([dev_bf16(s) for s in srcs], dev_i32(idx))
+    for s, o in zip(srcs, outs):
+        assert np.array_equal(host(o), oracle.unpad_gather(s, idx, hd))
+    back = t.attn_pad_scatter(outs[1], dev_i32(idx), n_rows)
+    assert np.array_equal(host(back), oracle.pad_scatter(oracle.unpad_gather(srcs[1], idx, hd),
+                                                         idx, n_rows))
+    # an out-of-range gather index yields a zero row, never a fault
+    bad = idx.copy()
+    bad[7] = n_rows + 5
+    bad[8] = -3
+    o1 = t.attn_unpad_gather([dev_bf16(srcs[2])], dev_i32(bad))[0]
+    h1 = host(o1)
+    assert np.all(h1[7] == 0) and np.all(h1[8] == 0)
+    keep = np.ones(len(idx), bool)
+    keep[[7, 8]] = False
+    assert np.array_equal(h1[keep], srcs[2][idx[keep]])
+    # fp32 rows too (the scatter's main use is the fp32 attention output)
+    f = torch.randn(123, 16, 32, device="cuda")
+    fs = t.attn_pad_scatter(f, dev_i32(idx), n_rows)
+    assert np.array_equal(host(fs), oracle.pad_scatter(host(f), idx, n_rows))
+
+
+@pytest.mark.parametrize("n_valid,n_rows", [(0, 50), (1, 1), (4096, 4096), (2000, 65536), (7, 9)])
+def test_scatter_search_sizes(n_valid, n_rows):
+    import torch
+    t = api()
+    r = np.random.Generator(np.random.PCG64(1200 + n_rows))
+    idx = np.sort(r.choice(n_rows, size=n_valid, replace=False)).astype(np.int32)
+    src = torch.randn(n_valid, 4, 4, device="cuda")
+    out = t.attn_pad_scatter(src, dev_i32(idx), n_rows)
+    assert np.array_equal(host(out), oracle.pad_scatter(host(src), idx, n_rows))
+
+
+# ----------------------------------------------------------------------------- the padded path end to end
+@pytest.mark.parametrize("name", ["padded_32x128_random", "padded_32x128_exact", "padded_1x2048"])
+def test_padded_path_full_size(name):
+    t = api()
+    w = gen.build_workload(name)
+    idx = dev_i32(w.indices)
+    qc, kc, vc = t.attn_unpad_gather([dev_bf16(w.q), dev_bf16(w.k), dev_bf16(w.v)], idx)
+    o, lse = t.attn_fwd_varlen(qc, kc, vc, dev_i32(w.cu_seqlens_q), dev_i32(w.cu_seqlens_k),
+                               w.max_seqlen, scale=float(w.scale), causal=True)
+    padded = t.attn_pad_scatter(o, idx, w.q.shape[1], out_shape=(1,) + w.q.shape[1:])
+    # the oracle: gather, attention, scatter
+    hd = w.q.shape[2:]
+    gq, gk, gv = (oracle.unpad_gather(x, w.indices, hd) for x in (w.q, w.k, w.v))
+    assert np.array_equal(host(qc), gq) and np.array_equal(host(kc), gk)
+    o_ref, lse_ref = oracle.attention_varlen(gq, gk, gv, w.cu_seqlens_q, w.cu_seqlens_k, w.scale, True)
+    p_ref = oracle.pad_scatter(o_ref, w.indices, w.q.shape[1]).reshape((1,) + w.q.shape[1:])
+    ph = host(padded)
+    pad_rows = np.ones(w.q.shape[1], bool)
+    pad_rows[w.indices] = False
+    assert np.all(ph[0, pad_rows].view(np.uint32) == 0)  # +0.0 bits
+    print(check_o(ph, p_ref), check_lse(host(lse), lse_ref))
+
+
+def test_padded_path_nan_padding_does_not_leak():
+    t = api()
+    w = gen.make_padded("nan", 1300, 1024, [128] * 8, 4, 64, True, random_max=128,
+                        pad_value=float("nan"))
+    idx = dev_i32(w.indices)
+    qc, kc, vc = t.attn_unpad_gather([dev_bf16(w.q), dev_bf16(w.k), dev_bf16(w.v)], idx)
+    o, lse = t.attn_fwd_varlen(qc, kc, vc, dev_i32(w.cu_seqlens_q), dev_i32(w.cu_seqlens_k),
+                               w.max_seqlen, scale=float(w.scale), causal=True)
+    padded = host(t.attn_pad_scatter(o, idx, 1024))
+    assert not np.isnan(padded).any()
+    hd = w.q.shape[2:]
+    gq, gk, gv = (oracle.unpad_gather(x, w.indices, hd) for x in (w.q, w.k, w.v))
+    o_ref, _ = oracle.attention_varlen(gq, gk, gv, w.cu_seqlens_q, w.cu_seqlens_k, w.scale, True)
+    check_o(padded, oracle.pad_scatter(o_ref, w.indices, 1024))
+
+
+# ----------------------------------------------------------------------------- full-size configs, sampled
+SAMPLED = ["vit_dense_b149", "hdim_sweep_d32", "hdim_sweep_d64", "hdim_sweep_d128",
+           "hdim_sweep_d256", "varlen_1x8192", "gqa_dense_s8192", "pack_64k"]
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", SAMPLED)
+def test_full_size_sampled_rows(name):
+    w = gen.build_workload(name)
+    r = np.random.Generator(np.random.PCG64(77))
+    if w.kind == "dense":
+        o, lse = run_dense(w)
+    else:
+        o, lse = run_varlen(w)
+    assert not np.isnan(o).any()
+    q = w.q
+    errs = []
+    n_samples = 160
+    for n in range(n_samples):
+        s = int(r.integers(0, len(w.lengths_q)))
+        L = w.lengths_q[s]
+        if L == 0:
+            continue
+        # bias half the samples to the ends of the sequence (first/last tiles)
+        i = int(r.integers(0, L)) if n % 2 == 0 else int((L - 1 - r.integers(0, 64)) % L)
+        h = int(r.integers(0, w.hq))
+        g = h // (w.hq // w.hkv)
+        if w.kind == "dense":
+            qr = oracle.bf16_bits_to_f64(q[s, i, h])
+            ks = oracle.bf16_bits_to_f64(w.k[s, :, g])
+            vs = oracle.bf16_bits_to_f64(w.v[s, :, g])
+            og, lg = o[s, i, h], lse[s, h, i]
+        else:
+            c0, k0, k1 = w.cu_seqlens_q[s], w.cu_seqlens_k[s], w.cu_seqlens_k[s + 1]
+            qr = oracle.bf16_bits_to_f64(q[c0 + i, h])
+            ks = oracle.bf16_bits_to_f64(w.k[k0:k1, g])
+            vs = oracle.bf16_bits_to_f64(w.v[k0:k1, g])
+            og, lg = o[c0 + i, h], lse[h, c0 + i]
+        oref, lref = oracle.attention_query(qr, ks, vs, w.scale, w.causal, i, L)
+        errs.append(float(np.abs(og - oref).max()))
+        assert abs(float(lg) - lref) <= 1e-3, (s, i, h, lg, lref)
+    errs = np.array(errs)
+    assert errs.max() <= 2e-2 and errs.mean() <= 2e-3, (errs.max(), errs.mean())
+    # property at any size: each output row is a convex combination of value
+    # rows, so no output element exceeds the largest value magnitude
+    vmax = float(np.abs(oracle.bf16_bits_to_f64(w.v)).max())
+    assert float(np.abs(o).max()) <= vmax + 2e-2
+    print(name, "max", errs.max(), "mean", errs.mean())

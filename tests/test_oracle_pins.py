@@ -424,3 +424,11 @@ def test_pins_accept_oracle_and_reject_mutants():
     assert _pins_pass(oatt.attention_one)
     for m in _mutants():
         assert not _pins_pass(m), m.__name__
+
+
+def test_gather_scatter_empty_index_list():
+    src = np.arange(24, dtype=np.float32).reshape(6, 2, 2)
+    g = oracle.unpad_gather(src, np.zeros(0, np.int32), (2, 2))
+    assert g.shape == (0, 2, 2)
+    s = oracle.pad_scatter(np.zeros((0, 2, 2), np.float32), np.zeros(0, np.int32), 5)
+    assert s.shape == (5, 2, 2) and np.all(s == 0)

@@ -1,0 +1,184 @@
+"""MI355X (gfx950) FlashAttention forward: thin PyTorch binding over libattnfwd.so.
+
+The four calls carry the names of the C ABI (include/attn_fwd.h).  This module
+only marshals arguments: it checks tensor placement and layout, allocates the
+outputs with torch.empty, and passes raw device pointers plus the current HIP
+stream to the library.  Every step of the computation runs in the library's
+kernels; there is no other implementation to fall back to.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+from typing import List, Optional, Sequence, Tuple
+
+from . import _lib
+
+__all__ = ["attn_fwd_varlen", "attn_fwd_dense", "attn_unpad_gather", "attn_pad_scatter",
+           "abi_version", "AttnError"]
+
+AttnError = _lib.AttnError
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_ptr(device, stream) -> int:
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return int(s.cuda_stream)
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else int(t.data_ptr())
+
+
+def _check_bf16(name, t):
+    torch = _torch()
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise ValueError(f"{name} must hold bfloat16 (or its 16-bit storage), got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def abi_version() -> int:
+    return int(_lib.load().attn_abi_version())
+
+
+def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen: int,
+                    scale: Optional[float] = None, causal: bool = False,
+                    out=None, lse=None, return_lse: bool = True, stream=None):
+    """Packed variable-length attention.  q (Tq, Hq, D), k/v (Tk, Hkv, D) bf16.
+
+    Returns (out (Tq, Hq, D) fp32, lse (Hq, Tq) fp32 or None).
+    """
+    torch = _torch()
+    lib = _lib.load()
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _check_bf16(n, t)
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3 or k.shape != v.shape:
+        raise ValueError("q must be (Tq, Hq, D) and k, v (Tk, Hkv, D)")
+    for n, t in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{n} must be a contiguous int32 GPU tensor")
+    if cu_seqlens_q.numel() != cu_seqlens_k.numel():
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+    tq, hq, d = q.shape
+    tk, hkv, dk = k.shape
+    if dk != d:
+        raise ValueError("head_dim of q and k differ")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((tq, hq, d), dtype=torch.float32, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty((hq, tq), dtype=torch.float32, device=q.device)
+    st = lib.attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+                             cu_seqlens_q.numel() - 1, tq, tk, hq, hkv, d, int(max_seqlen),
+                             float(scale), int(bool(causal)), _ptr(out), _ptr(lse),
+                             _stream_ptr(q.device, stream))
+    _lib.check("attn_fwd_varlen", st)
+    return out, lse
+
+
+def attn_fwd_dense(q, k, v, scale: Optional[float] = None, causal: bool = False,
+                   out=None, lse=None, return_lse: bool = True, stream=None):
+    """Dense batched attention.  q (B, Sq, Hq, D), k/v (B, Sk, Hkv, D) bf16.
+
+    Non-contiguous q/k/v/out are accepted when the head_dim stride is 1 (their
+    strides are passed through).  Returns (out (B, Sq, Hq, D) fp32, lse
+    (B, Hq, Sq) fp32 or None).
+    """
+    torch = _torch()
+    lib = _lib.load()
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda or t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+            raise ValueError(f"{n} must be a bfloat16 GPU tensor")
+        if t.dim() != 4 or t.stride(3) != 1:
+            raise ValueError(f"{n} must be 4-D with a unit head_dim stride")
+    b, sq, hq, d = q.shape
+    _, sk, hkv, _ = k.shape
+    if k.shape != v.shape or k.shape[0] != b or k.shape[3] != d:
+        raise ValueError("k and v must be (B, Sk, Hkv, D) matching q")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((b, sq, hq, d), dtype=torch.float32, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty((b, hq, sq), dtype=torch.float32, device=q.device)
+    strides = (ctypes.c_int64 * 12)(*(list(q.stride()[:3]) + list(k.stride()[:3]) +
+                                      list(v.stride()[:3]) + list(out.stride()[:3])))
+    st = lib.attn_fwd_dense(_ptr(q), _ptr(k), _ptr(v), b, sq, sk, hq, hkv, d,
+                            ctypes.cast(strides, ctypes.c_void_p), float(scale),
+                            int(bool(causal)), _ptr(out), _ptr(lse),
+                            _stream_ptr(q.device, stream))
+    _lib.check("attn_fwd_dense", st)
+    return out, lse
+
+
+def attn_unpad_gather(srcs: Sequence, indices, row_dims: int = 2, outs=None,
+                      stream=None) -> List:
+    """Gathers rows of 1..3 tensors by one shared int32 index list.
+
+    A row is the trailing ``row_dims`` dimensions (H, D by default), so a
+    (B, total_len, H, D) tensor has B * total_len rows.  Returns one
+    (n_valid, *row_shape) tensor per source.
+    """
+    torch = _torch()
+    lib = _lib.load()
+    srcs = list(srcs)
+    if not 1 <= len(srcs) <= 3:
+        raise ValueError("between 1 and 3 tensors per call")
+    if indices.dtype != torch.int32 or not indices.is_cuda or not indices.is_contiguous():
+        raise ValueError("indices must be a contiguous int32 GPU tensor")
+    row_shape = tuple(srcs[0].shape[-row_dims:])
+    row_bytes = int(math.prod(row_shape)) * srcs[0].element_size()
+    n_rows = srcs[0].numel() // max(1, int(math.prod(row_shape)))
+    for s in srcs:
+        if not s.is_cuda or not s.is_contiguous():
+            raise ValueError("sources must be contiguous GPU tensors")
+        if tuple(s.shape[-row_dims:]) != row_shape or s.dtype != srcs[0].dtype \
+                or s.numel() != srcs[0].numel():
+            raise ValueError("all sources must share shape and dtype")
+    n_valid = indices.numel()
+    if outs is None:
+        outs = [torch.empty((n_valid,) + row_shape, dtype=s.dtype, device=s.device) for s in srcs]
+    src_arr = (ctypes.c_void_p * len(srcs))(*[_ptr(s) for s in srcs])
+    dst_arr = (ctypes.c_void_p * len(outs))(*[_ptr(o) for o in outs])
+    st = lib.attn_unpad_gather(ctypes.cast(src_arr, ctypes.c_void_p),
+                               ctypes.cast(dst_arr, ctypes.c_void_p), len(srcs), _ptr(indices),
+                               n_valid, n_rows, row_bytes, _stream_ptr(srcs[0].device, stream))
+    _lib.check("attn_unpad_gather", st)
+    return outs
+
+
+def attn_pad_scatter(src, indices, n_rows_total: int, out_shape: Optional[Tuple[int, ...]] = None,
+                     out=None, stream=None):
+    """Scatters compact rows (n_valid, *row_shape) back to n_rows_total rows.
+
+    Rows that no index names are written as zeros.  ``out_shape`` (default
+    (n_rows_total, *row_shape)) reshapes the result, e.g. to (B, total_len, H, D).
+    """
+    torch = _torch()
+    lib = _lib.load()
+    if not src.is_cuda or not src.is_contiguous():
+        raise ValueError("src must be a contiguous GPU tensor")
+    if indices.dtype != torch.int32 or not indices.is_cuda or not indices.is_contiguous():
+        raise ValueError("indices must be a contiguous int32 GPU tensor")
+    n_valid = indices.numel()
+    if src.shape[0] != n_valid:
+        raise ValueError("src must have one row per index")
+    row_shape = tuple(src.shape[1:])
+    row_bytes = int(math.prod(row_shape)) * src.element_size()
+    if out is None:
+        shape = out_shape if out_shape is not None else (n_rows_total,) + row_shape
+        out = torch.empty(shape, dtype=src.dtype, device=src.device)
+    st = lib.attn_pad_scatter(_ptr(src), _ptr(out), _ptr(indices), n_valid, int(n_rows_total),
+                              row_bytes, _stream_ptr(src.device, stream))
+    _lib.check("attn_pad_scatter", st)
+    return out

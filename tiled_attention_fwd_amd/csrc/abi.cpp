@@ -1,0 +1,211 @@
+// C ABI of the attention library: argument checks, tile-policy choice and
+// launch.  Every check runs on the host before anything is enqueued; nothing
+// here allocates device memory or synchronises.
+
+#include "../../include/attn_fwd.h"
+#include "attn_internal.h"
+
+#include <math.h>
+#include <stdlib.h>
+
+using attnfwd::AttnArgs;
+using attnfwd::TilePolicy;
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+bool head_dim_ok(int d) { return d == 32 || d == 64 || d == 128 || d == 256; }
+
+// ATTN_FWD_TILE=<policy id> forces a compiled tile policy (used by tile sweeps).
+int tile_override() {
+  const char* s = getenv("ATTN_FWD_TILE");
+  if (s == nullptr || *s == '\0') return -1;
+  char* end = nullptr;
+  long v = strtol(s, &end, 10);
+  if (end == s || v < 0 || v > 1000) return -1;
+  return (int)v;
+}
+
+// scale * log2(e), the factor that turns scores into base-2 exponents.
+float base2_factor(float scale) { return (float)((double)scale * 1.4426950408889634074); }
+
+attn_status_t check_common(int32_t hq, int32_t hkv, int32_t d, float scale) {
+  if (hq < 0 || hkv < 0) return ATTN_ERR_SHAPE;
+  if (!head_dim_ok(d)) return ATTN_ERR_UNSUPPORTED;
+  if (!(scale > 0.f) || !isfinite(scale)) return ATTN_ERR_UNSUPPORTED;
+  if (hq > 0 && (hkv <= 0 || hq % hkv != 0)) return ATTN_ERR_SHAPE;
+  return ATTN_OK;
+}
+
+attn_status_t launch(AttnArgs& a, int d, bool varlen, int max_q, hipStream_t stream) {
+  TilePolicy pol;
+  int pid;
+  if (!attnfwd::select_policy(d, max_q, tile_override(), &pol, &pid)) return ATTN_ERR_UNSUPPORTED;
+  a.n_qb = (max_q + pol.bm() - 1) / pol.bm();
+  const int64_t rows = (int64_t)a.nseq * a.hq;
+  if (rows * a.n_qb > 0x7fffffffLL) return ATTN_ERR_SHAPE;
+  a.xcd_remap = (rows % 8 == 0) ? 1 : 0;
+  hipError_t e = attnfwd::launch_attention(a, d, varlen, pid, stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status_t attn_fwd_varlen(const void* q, const void* k, const void* v,
+                              const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                              int32_t num_seqs, int32_t total_q, int32_t total_k,
+                              int32_t num_heads_q, int32_t num_heads_k, int32_t head_dim,
+                              int32_t max_seqlen, float scale, int32_t causal, float* out,
+                              float* lse, void* stream) {
+  if (num_seqs < 0 || total_q < 0 || total_k < 0 || max_seqlen < 0) return ATTN_ERR_SHAPE;
+  attn_status_t st = check_common(num_heads_q, num_heads_k, head_dim, scale);
+  if (st != ATTN_OK) return st;
+  if (num_seqs == 0 || total_q == 0 || num_heads_q == 0) return ATTN_OK;
+  if (max_seqlen == 0) return ATTN_ERR_SHAPE;  // some sequence has queries
+  if (q == nullptr || out == nullptr || cu_seqlens_q == nullptr || cu_seqlens_k == nullptr)
+    return ATTN_ERR_NULL;
+  if (total_k > 0 && (k == nullptr || v == nullptr)) return ATTN_ERR_NULL;
+  if (!aligned16(q) || !aligned16(out) || (total_k > 0 && (!aligned16(k) || !aligned16(v))))
+    return ATTN_ERR_ALIGN;
+  if (!aligned4(cu_seqlens_q) || !aligned4(cu_seqlens_k) || (lse && !aligned4(lse)))
+    return ATTN_ERR_ALIGN;
+
+  AttnArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = out;
+  a.lse = lse;
+  a.cu_q = cu_seqlens_q;
+  a.cu_k = cu_seqlens_k;
+  a.q_ss = (int64_t)num_heads_q * head_dim;
+  a.q_hs = head_dim;
+  a.k_ss = (int64_t)num_heads_k * head_dim;
+  a.k_hs = head_dim;
+  a.v_ss = a.k_ss;
+  a.v_hs = head_dim;
+  a.o_ss = a.q_ss;
+  a.o_hs = head_dim;
+  a.lse_hs = total_q;
+  a.nseq = num_seqs;
+  a.hq = num_heads_q;
+  a.hkv = num_heads_k;
+  a.group = num_heads_q / num_heads_k;
+  a.c = base2_factor(scale);
+  a.causal = causal ? 1 : 0;
+  const int max_q = max_seqlen < total_q ? max_seqlen : total_q;
+  return launch(a, head_dim, true, max_q, static_cast<hipStream_t>(stream));
+}
+
+attn_status_t attn_fwd_dense(const void* q, const void* k, const void* v, int32_t batch,
+                             int32_t seqlen_q, int32_t seqlen_k, int32_t num_heads_q,
+                             int32_t num_heads_k, int32_t head_dim, const int64_t* strides,
+                             float scale, int32_t causal, float* out, float* lse, void* stream) {
+  if (batch < 0 || seqlen_q < 0 || seqlen_k < 0) return ATTN_ERR_SHAPE;
+  attn_status_t st = check_common(num_heads_q, num_heads_k, head_dim, scale);
+  if (st != ATTN_OK) return st;
+  if (batch == 0 || seqlen_q == 0 || num_heads_q == 0) return ATTN_OK;
+  if (q == nullptr || out == nullptr) return ATTN_ERR_NULL;
+  if (seqlen_k > 0 && (k == nullptr || v == nullptr)) return ATTN_ERR_NULL;
+  if (!aligned16(q) || !aligned16(out) || (seqlen_k > 0 && (!aligned16(k) || !aligned16(v))))
+    return ATTN_ERR_ALIGN;
+  if (lse && !aligned4(lse)) return ATTN_ERR_ALIGN;
+
+  AttnArgs a{};
+  const int64_t d = head_dim;
+  if (strides == nullptr) {
+    a.q_hs = d;
+    a.q_ss = num_heads_q * d;
+    a.q_bs = a.q_ss * seqlen_q;
+    a.k_hs = d;
+    a.k_ss = num_heads_k * d;
+    a.k_bs = a.k_ss * seqlen_k;
+    a.v_hs = a.k_hs;
+    a.v_ss = a.k_ss;
+    a.v_bs = a.k_bs;
+    a.o_hs = d;
+    a.o_ss = num_heads_q * d;
+    a.o_bs = a.o_ss * seqlen_q;
+  } else {
+    for (int i = 0; i < 12; ++i) {
+      if (strides[i] < 0) return ATTN_ERR_SHAPE;
+      if (i < 9 && strides[i] % 8 != 0) return ATTN_ERR_ALIGN;
+      if (i >= 9 && strides[i] % 4 != 0) return ATTN_ERR_ALIGN;
+    }
+    a.q_bs = strides[0]; a.q_ss = strides[1]; a.q_hs = strides[2];
+    a.k_bs = strides[3]; a.k_ss = strides[4]; a.k_hs = strides[5];
+    a.v_bs = strides[6]; a.v_ss = strides[7]; a.v_hs = strides[8];
+    a.o_bs = strides[9]; a.o_ss = strides[10]; a.o_hs = strides[11];
+  }
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = out;
+  a.lse = lse;
+  a.lse_hs = seqlen_q;
+  a.lse_bs = (int64_t)num_heads_q * seqlen_q;
+  a.nseq = batch;
+  a.hq = num_heads_q;
+  a.hkv = num_heads_k;
+  a.group = num_heads_q / num_heads_k;
+  a.sq = seqlen_q;
+  a.sk = seqlen_k;
+  a.c = base2_factor(scale);
+  a.causal = causal ? 1 : 0;
+  return launch(a, head_dim, false, seqlen_q, static_cast<hipStream_t>(stream));
+}
+
+attn_status_t attn_unpad_gather(const void* const* src, void* const* dst, int32_t n_tensors,
+                                const int32_t* indices, int32_t n_valid, int32_t n_rows_src,
+                                int64_t row_bytes, void* stream) {
+  if (n_tensors < 1 || n_tensors > 3) return ATTN_ERR_SHAPE;
+  if (n_valid < 0 || n_rows_src < 0 || row_bytes <= 0) return ATTN_ERR_SHAPE;
+  if (row_bytes % 16 != 0) return ATTN_ERR_ALIGN;
+  if (n_valid == 0) return ATTN_OK;
+  if (src == nullptr || dst == nullptr || indices == nullptr) return ATTN_ERR_NULL;
+  for (int t = 0; t < n_tensors; ++t) {
+    if (dst[t] == nullptr || (n_rows_src > 0 && src[t] == nullptr)) return ATTN_ERR_NULL;
+    if (!aligned16(dst[t]) || !aligned16(src[t])) return ATTN_ERR_ALIGN;
+  }
+  if (!aligned4(indices)) return ATTN_ERR_ALIGN;
+  if ((int64_t)n_valid * (row_bytes / 16) >= (1LL << 32)) return ATTN_ERR_SHAPE;
+  hipError_t e = attnfwd::launch_gather(src, dst, n_tensors, indices, n_valid, n_rows_src,
+                                        row_bytes, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+attn_status_t attn_pad_scatter(const void* src, void* dst, const int32_t* indices, int32_t n_valid,
+                               int32_t n_rows_total, int64_t row_bytes, void* stream) {
+  if (n_valid < 0 || n_rows_total < 0 || row_bytes <= 0) return ATTN_ERR_SHAPE;
+  if (row_bytes % 16 != 0) return ATTN_ERR_ALIGN;
+  if (n_valid > n_rows_total) return ATTN_ERR_SHAPE;
+  if (n_rows_total == 0) return ATTN_OK;
+  if (dst == nullptr) return ATTN_ERR_NULL;
+  if (n_valid > 0 && (src == nullptr || indices == nullptr)) return ATTN_ERR_NULL;
+  if (!aligned16(dst) || (n_valid > 0 && (!aligned16(src) || !aligned4(indices))))
+    return ATTN_ERR_ALIGN;
+  if ((int64_t)n_rows_total * (row_bytes / 16) >= (1LL << 31)) return ATTN_ERR_SHAPE;
+  hipError_t e = attnfwd::launch_scatter(src, dst, indices, n_valid, n_rows_total, row_bytes,
+                                         static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+const char* attn_status_str(attn_status_t s) {
+  switch (s) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_NULL: return "a required pointer is NULL";
+    case ATTN_ERR_SHAPE: return "invalid or inconsistent sizes";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported argument (head_dim must be 32/64/128/256; scale > 0 and finite)";
+    case ATTN_ERR_ALIGN: return "pointer, stride or row size not 16-byte aligned";
+    case ATTN_ERR_HIP: return "HIP runtime rejected the launch";
+    default: return "unknown status";
+  }
+}
+
+int32_t attn_abi_version(void) { return ATTN_FWD_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,58 @@
+// Internal interface between the C ABI layer and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attnfwd {
+
+// Everything one attention launch needs.  Strides are in elements.
+// Dense: sequence `b` starts at b * *_bs.  Varlen: sequence `s` starts at row
+// cu_*[s], so the *_bs strides are unused and rows advance by *_ss.
+struct AttnArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  float* o;
+  float* lse;  // may be null
+  const int32_t* cu_q;  // varlen only
+  const int32_t* cu_k;  // varlen only
+  int64_t q_bs, q_ss, q_hs;
+  int64_t k_bs, k_ss, k_hs;
+  int64_t v_bs, v_ss, v_hs;
+  int64_t o_bs, o_ss, o_hs;
+  int64_t lse_bs, lse_hs;  // dense: (B, Hq, Sq); varlen: (Hq, Tq) with hs = Tq
+  int32_t nseq, hq, hkv, group;
+  int32_t sq, sk;    // dense sequence lengths
+  int32_t n_qb;      // query blocks per (sequence, head) in the grid
+  float c;           // scale * log2(e): scores enter exp2 in base-2 units
+  int32_t causal;
+  int32_t xcd_remap; // 1: spread (sequence, head) rows so each XCD gets a contiguous slice
+};
+
+// Tile policies: the query block BM = waves * 32 * qcols, key block BN.
+struct TilePolicy {
+  int waves;   // wavefronts per workgroup
+  int qcols;   // 32-query column blocks per wave
+  int bn;      // keys per LDS tile
+  int bm() const { return waves * 32 * qcols; }
+};
+
+// Picks the policy for a head_dim and the longest query length.  `override_id`
+// (>= 0) forces one of the compiled policies for sweeps.
+bool select_policy(int head_dim, int max_seqlen_q, int override_id, TilePolicy* out, int* policy_id);
+
+// Enqueues one attention launch.  Returns hipSuccess or the launch error.
+hipError_t launch_attention(const AttnArgs& a, int head_dim, bool varlen, int policy_id,
+                            hipStream_t stream);
+
+// Row gather of up to three tensors sharing one index list.
+hipError_t launch_gather(const void* const* src, void* const* dst, int n_tensors,
+                         const int32_t* indices, int n_valid, int n_rows_src, int64_t row_bytes,
+                         hipStream_t stream);
+
+// Row scatter with zero fill of the rows no index names.
+hipError_t launch_scatter(const void* src, void* dst, const int32_t* indices, int n_valid,
+                          int n_rows_total, int64_t row_bytes, hipStream_t stream);
+
+}  // namespace attnfwd

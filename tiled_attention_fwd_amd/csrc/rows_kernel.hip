@@ -1,0 +1,152 @@
+// Row gather (unpad) and row scatter (pad) for the packed attention path.
+//
+// Page "Lesson 5: IAW model FA2 vs FA3 measured", section 1: the padded
+// (B, total_len, H, D) tensor is compacted by gathering the rows named by
+// `indices`, attention runs on the compact rows, and the result is scattered
+// back to the padded positions.  Sections 2 and 6 show these moves as one
+// gather per tensor and a fill kernel followed by an index-put kernel.  Here
+// one launch gathers q, k and v together, and one launch writes every padded
+// output row exactly once (copied row or zeros), so no separate fill runs.
+//
+// Both kernels are pure HBM streams: 16-byte vector loads and stores, each
+// lane moving consecutive 16-byte chunks of a row so a wave covers 1 KiB of
+// contiguous bytes per instruction.
+
+#include "attn_internal.h"
+
+namespace attnfwd {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 4;  // 16-byte chunks per thread per pass
+
+struct GatherArgs {
+  const uint4* src[3];
+  uint4* dst[3];
+  const int32_t* indices;
+  int32_t n_valid;
+  int32_t n_rows_src;
+  int32_t cpr;      // 16-byte chunks per row
+  int64_t total;    // n_valid * cpr chunks per tensor
+};
+
+__global__ __launch_bounds__(kThreads) void gather_rows_kernel(const GatherArgs a) {
+  const int t = blockIdx.y;
+  const uint4* __restrict__ src = a.src[t];
+  uint4* __restrict__ dst = a.dst[t];
+  const int64_t base = (int64_t)blockIdx.x * kThreads * kUnroll + threadIdx.x;
+  uint4 val[kUnroll];
+  int64_t out_at[kUnroll];
+#pragma unroll
+  for (int i = 0; i < kUnroll; ++i) {
+    const int64_t g = base + (int64_t)i * kThreads;
+    out_at[i] = -1;
+    if (g < a.total) {
+      // total < 2^32 is checked on the host, so 32-bit division is exact here
+      const uint32_t row = (uint32_t)g / (uint32_t)a.cpr;
+      const uint32_t col = (uint32_t)g - row * (uint32_t)a.cpr;
+      const int idx = a.indices[row];
+      val[i] = (idx >= 0 && idx < a.n_rows_src) ? src[(int64_t)idx * a.cpr + col]
+                                                : make_uint4(0, 0, 0, 0);
+      out_at[i] = g;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kUnroll; ++i)
+    if (out_at[i] >= 0) dst[out_at[i]] = val[i];
+}
+
+// Scatter: each workgroup owns kRows consecutive destination rows.  Because
+// `indices` is strictly increasing, the source rows that land in
+// [r0, r0 + kRows) are the (at most kRows) entries starting at the first
+// position whose index is >= r0.  Wave 0 finds that position with a 64-way
+// search (each round probes 64 evenly spaced entries, so 65536 entries take
+// three dependent rounds), then the workgroup builds a row -> source map in
+// LDS and streams the rows.
+constexpr int kRows = 8;
+
+__device__ int lower_bound_wave(const int32_t* idx, int n, int key, int lane) {
+  int lo = 0, hi = n;  // answer in [lo, hi]
+  while (hi - lo > 0) {
+    const int span = hi - lo;
+    const int step = (span + 63) / 64;
+    const int pos = lo + lane * step;
+    const bool probe = pos < hi;
+    const bool less = probe && idx[pos] < key;
+    const uint64_t m = __ballot(less);
+    const int cnt = __popcll(m);
+    // Probes 0..cnt-1 are < key, so the answer is in (lo + (cnt-1)*step, lo + cnt*step].
+    const int new_lo = cnt > 0 ? lo + (cnt - 1) * step + 1 : lo;
+    const int new_hi = min(hi, lo + cnt * step);
+    if (step == 1) return min(hi, lo + cnt);
+    lo = new_lo;
+    hi = new_hi;
+  }
+  return lo;
+}
+
+__global__ __launch_bounds__(kThreads) void scatter_rows_kernel(
+    const uint4* __restrict__ src, uint4* __restrict__ dst, const int32_t* __restrict__ indices,
+    int n_valid, int n_rows_total, int cpr) {
+  __shared__ int pos0_s;
+  __shared__ int srcpos[kRows];
+  const int r0 = blockIdx.x * kRows;
+  const int tid = threadIdx.x;
+  if (tid < 64) {
+    const int p0 = lower_bound_wave(indices, n_valid, r0, tid);
+    if (tid == 0) pos0_s = p0;
+  }
+  if (tid < kRows) srcpos[tid] = -1;
+  __syncthreads();
+  if (tid < kRows) {
+    const int p = pos0_s + tid;
+    if (p < n_valid) {
+      const int r = indices[p];
+      if (r >= r0 && r < r0 + kRows && r < n_rows_total) srcpos[r - r0] = p;
+    }
+  }
+  __syncthreads();
+  const int nrows = min(kRows, n_rows_total - r0);
+  const int total = nrows * cpr;
+  for (int g = tid; g < total; g += kThreads) {
+    const int row = g / cpr;
+    const int col = g - row * cpr;
+    const int sp = srcpos[row];
+    const uint4 v = sp >= 0 ? src[(int64_t)sp * cpr + col] : make_uint4(0, 0, 0, 0);
+    dst[(int64_t)(r0 + row) * cpr + col] = v;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gather(const void* const* src, void* const* dst, int n_tensors,
+                         const int32_t* indices, int n_valid, int n_rows_src, int64_t row_bytes,
+                         hipStream_t stream) {
+  GatherArgs a{};
+  for (int t = 0; t < n_tensors; ++t) {
+    a.src[t] = static_cast<const uint4*>(src[t]);
+    a.dst[t] = static_cast<uint4*>(dst[t]);
+  }
+  a.indices = indices;
+  a.n_valid = n_valid;
+  a.n_rows_src = n_rows_src;
+  a.cpr = (int32_t)(row_bytes / 16);
+  a.total = (int64_t)n_valid * a.cpr;
+  const int64_t blocks = (a.total + kThreads * kUnroll - 1) / (kThreads * kUnroll);
+  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(gather_rows_kernel, dim3((unsigned)blocks, n_tensors), dim3(kThreads), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_scatter(const void* src, void* dst, const int32_t* indices, int n_valid,
+                          int n_rows_total, int64_t row_bytes, hipStream_t stream) {
+  const int cpr = (int)(row_bytes / 16);
+  const int blocks = (n_rows_total + kRows - 1) / kRows;
+  hipLaunchKernelGGL(scatter_rows_kernel, dim3(blocks), dim3(kThreads), 0, stream,
+                     static_cast<const uint4*>(src), static_cast<uint4*>(dst), indices, n_valid,
+                     n_rows_total, cpr);
+  return hipGetLastError();
+}
+
+}  // namespace attnfwd
