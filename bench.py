@@ -1,0 +1,404 @@
+#!/usr/bin/env python3
+"""Benchmark of the FlashAttention forward hot path on one MI355X.
+
+One step = the packed LLM path with padding (page "Lesson 5: IAW model FA2 vs
+FA3 measured", section 1) over both input variants of that workload:
+  (a) B=1, total_len 4096, 32 slots of 128 positions, valid lengths U{1..128}
+  (b) B=1, total_len 4096, one sequence of 2048 valid rows, 2048 padding rows
+each as unpad gather of q, k, v (one launch) -> causal varlen attention
+(H=16, D=128, bf16) -> pad scatter of the fp32 output (one launch).
+
+Printed: ONE JSON line.  `value` is attention TFLOP/s of the whole step (exact
+causal FLOPs = 4 * D * H * visible (query, key) pairs, divided by the wall time
+of K back-to-back steps with inputs resident in HBM).  `roofline` reports the
+kernel that takes the most time per step, measured with HIP events recorded
+on the launch stream around each of its launches inside the timed region.
+`cpu_baseline` times the fp64 oracle on the host for the same step.
+`configs` adds one row per listed workload (cold-cache per-call timing).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ["tiled_attention_fwd_amd/csrc/attn_kernel.hip",
+                  "tiled_attention_fwd_amd/csrc/rows_kernel.hip"]
+
+
+# ------------------------------------------------------------------------- work accounting
+def visible_pairs(lengths_q, lengths_k, causal):
+    tot = 0
+    for lq, lk in zip(lengths_q, lengths_k):
+        if not causal:
+            tot += lq * lk
+        else:
+            off = lk - lq
+            # rows i see min(lk, max(0, i + off + 1)) keys
+            for i in range(lq):
+                tot += min(lk, max(0, i + off + 1))
+    return tot
+
+
+def attn_flops(w):
+    return 4 * w.d * w.hq * visible_pairs(w.lengths_q, w.lengths_k, w.causal)
+
+
+def attn_bytes(w):
+    tq, tk = sum(w.lengths_q), sum(w.lengths_k)
+    return (tq * w.hq * w.d * 2 + 2 * tk * w.hkv * w.d * 2 + tq * w.hq * w.d * 4 + tq * w.hq * 4)
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel_tag):
+    """HBM bytes per launch from a committed rocprofv3 --pmc summary, if it
+    was taken on the current kernel sources; else None."""
+    path = os.path.join(PROFILES, f"traffic_{kernel_tag}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if "=" in line and not line.startswith("#"):
+                k, v = line.split("=", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_hash") != source_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ------------------------------------------------------------------------- GPU plumbing
+class PaddedPath:
+    """Device buffers for one padded-path input, allocated once."""
+
+    def __init__(self, w, torch, t):
+        import numpy as np
+        self.w, self.t = w, t
+        dev = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to("cuda").view(torch.bfloat16)
+        self.q, self.k, self.v = dev(w.q), dev(w.k), dev(w.v)
+        self.idx = torch.from_numpy(w.indices).to("cuda")
+        self.cu = torch.from_numpy(w.cu_seqlens_q).to("cuda")
+        n = len(w.indices)
+        h, d = w.hq, w.d
+        self.qc = torch.empty((n, h, d), dtype=torch.bfloat16, device="cuda")
+        self.kc = torch.empty_like(self.qc)
+        self.vc = torch.empty_like(self.qc)
+        self.o = torch.empty((n, h, d), dtype=torch.float32, device="cuda")
+        self.lse = torch.empty((h, n), dtype=torch.float32, device="cuda")
+        self.total_len = w.q.shape[1]
+        self.out = torch.empty((1, self.total_len, h, d), dtype=torch.float32, device="cuda")
+        self.n_valid = n
+
+    def gather(self):
+        self.t.attn_unpad_gather([self.q, self.k, self.v], self.idx, outs=[self.qc, self.kc, self.vc])
+
+    def attention(self):
+        self.t.attn_fwd_varlen(self.qc, self.kc, self.vc, self.cu, self.cu, self.w.max_seqlen,
+                               scale=float(self.w.scale), causal=True, out=self.o, lse=self.lse)
+
+    def scatter(self):
+        self.t.attn_pad_scatter(self.o, self.idx, self.total_len, out=self.out)
+
+    def bytes_gather(self):
+        return 3 * 2 * self.n_valid * self.w.hq * self.w.d * 2
+
+    def bytes_scatter(self):
+        row = self.w.hq * self.w.d * 4
+        return self.n_valid * row + self.total_len * row
+
+
+def spin(torch):
+    """Queues ~0.5 ms of GPU spinning so that the host can enqueue the next
+    launches before the GPU reaches them (event pairs then bracket kernels only)."""
+    try:
+        torch.cuda._sleep(1_200_000)
+    except Exception:  # pragma: no cover
+        x = torch.empty((4096, 4096), device="cuda", dtype=torch.bfloat16)
+        x @ x
+
+
+def time_calls(torch, fn, iters, warmup, flush=None):
+    """Per-call device time (us) with events.  Before each call either `flush`
+    (a 1 GiB write that evicts L2 and MALL: cold) or a spin kernel (warm) runs."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    times = []
+    s = torch.cuda.current_stream()
+    for _ in range(iters):
+        if flush is not None:
+            flush()
+        else:
+            spin(torch)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(s)
+        fn()
+        b.record(s)
+        b.synchronize()
+        times.append(a.elapsed_time(b) * 1000.0)
+    return times
+
+
+def run_configs(torch, t, names, flush):
+    import numpy as np
+    from synth import gen
+    rows = []
+    for name in names:
+        w = gen.build_workload(name)
+        dev = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to("cuda").view(torch.bfloat16)
+        q, k, v = dev(w.q), dev(w.k), dev(w.v)
+        if w.kind == "dense":
+            o = torch.empty(w.q.shape, dtype=torch.float32, device="cuda")
+            lse = torch.empty((w.q.shape[0], w.hq, w.q.shape[1]), dtype=torch.float32, device="cuda")
+            fn = lambda: t.attn_fwd_dense(q, k, v, scale=float(w.scale), causal=w.causal, out=o, lse=lse)
+        else:
+            cq = torch.from_numpy(w.cu_seqlens_q).to("cuda")
+            ck = torch.from_numpy(w.cu_seqlens_k).to("cuda")
+            o = torch.empty(w.q.shape, dtype=torch.float32, device="cuda")
+            lse = torch.empty((w.hq, w.q.shape[0]), dtype=torch.float32, device="cuda")
+            fn = lambda: t.attn_fwd_varlen(q, k, v, cq, ck, w.max_seqlen, scale=float(w.scale),
+                                           causal=w.causal, out=o, lse=lse)
+        fl, by = attn_flops(w), attn_bytes(w)
+        probe = time_calls(torch, fn, 3, 2)
+        iters = int(min(50, max(5, 0.25e6 / max(1.0, statistics.median(probe)))))
+        cold = time_calls(torch, fn, iters, 1, flush=flush)
+        warm = time_calls(torch, fn, iters, 1)
+        med = statistics.median(cold)
+        tf = fl / (med * 1e-6) / 1e12
+        gbs = by / (med * 1e-6) / 1e9
+        t_mfma = fl / (PEAK_BF16_TFLOPS * 1e12) * 1e6
+        t_hbm = by / (PEAK_HBM_GBS * 1e9) * 1e6
+        rows.append({
+            "workload": name, "us_median_cold": round(med, 2),
+            "us_p10": round(sorted(cold)[len(cold) // 10], 2),
+            "us_p90": round(sorted(cold)[(len(cold) * 9) // 10], 2),
+            "us_median_warm": round(statistics.median(warm), 2),
+            "gflop": round(fl / 1e9, 3), "tflops": round(tf, 1),
+            "pct_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 1),
+            "gbs": round(gbs, 1), "pct_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 1),
+            "bound": "mfma" if t_mfma >= t_hbm else "hbm",
+            "pct_of_bound": round(100 * max(t_mfma, t_hbm) / med, 1),
+        })
+        del q, k, v, o, lse
+        torch.cuda.empty_cache()
+    return rows
+
+
+# ------------------------------------------------------------------------- CPU baseline
+def cpu_baseline(step_workloads, budget_s=20.0):
+    """The fp64 oracle on the host, for the same padded-path step."""
+    import numpy as np
+    import oracle
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    flops = sum(attn_flops(w) for w in step_workloads)
+    t0 = time.perf_counter()
+    steps = 0
+    while True:
+        for w in step_workloads:
+            hd = w.q.shape[2:]
+            g = [oracle.unpad_gather(x, w.indices, hd) for x in (w.q, w.k, w.v)]
+            o, _ = oracle.attention_varlen(*g, w.cu_seqlens_q, w.cu_seqlens_k, w.scale, True)
+            oracle.pad_scatter(o, w.indices, w.q.shape[1])
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or steps >= 5:
+            break
+    per_step = el / steps
+    return {"value": round(flops / per_step / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{steps} full step(s) of the same padded-path workload ((a) and (b)): NumPy fp64 "
+                      f"gather, attention_varlen, scatter; {per_step * 1e3:.0f} ms per step"}
+
+
+# ------------------------------------------------------------------------- main
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--configs", default="all",
+                    help="comma list of extra workloads to time per call, 'all' or 'none'")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--only-configs", action="store_true",
+                    help="time only the per-workload rows (no step, no JSON contract line)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(the forward shards by heads or sequences with no communication; see the design notes).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import tiled_attention_fwd_amd as t
+    from synth import gen
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    print(f"[bench] device {torch.cuda.get_device_name(0)}", file=sys.stderr, flush=True)
+
+    if args.only_configs:
+        flush_buf = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        cfg_names = list(gen.WORKLOADS) if args.configs == "all" else args.configs.split(",")
+        for row in run_configs(torch, t, cfg_names, lambda: flush_buf.zero_()):
+            print(json.dumps(row), flush=True)
+        return
+
+    names = ["padded_32x128_random", "padded_1x2048"]
+    wls = [gen.build_workload(n) for n in names]
+    paths = [PaddedPath(w, torch, t) for w in wls]
+    flops_step = sum(attn_flops(w) for w in wls)
+
+    def busy():
+        spin(torch)
+
+    def step():
+        for p in paths:
+            p.gather()
+            p.attention()
+            p.scatter()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # The step is captured once as a HIP graph so that host launch overhead
+    # (the Python binding) does not starve the GPU between the six launches.
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    print("[bench] warmup done", file=sys.stderr, flush=True)
+
+    # Timed region 1: K graph replays back to back (wall clock -> value).
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    value = flops_step / (ms_per_step * 1e-3) / 1e12
+
+    # Timed region 2: K eager steps with HIP events on the launch stream around
+    # every launch.  A spin kernel queued first keeps the GPU busy while the
+    # host enqueues the step, so each event pair brackets only its kernel.
+    s = torch.cuda.current_stream()
+    kinds = [(pi, k) for pi in range(len(paths)) for k in ("gather", "attention", "scatter")]
+    ev = {kk: [] for kk in kinds}
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        busy()
+        for pi, p in enumerate(paths):
+            for kname in ("gather", "attention", "scatter"):
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record(s)
+                getattr(p, kname)()
+                b.record(s)
+                ev[(pi, kname)].append((a, b))
+    torch.cuda.synchronize()
+    avg_us = {kk: statistics.mean(a.elapsed_time(b) for a, b in lst) * 1e3 for kk, lst in ev.items()}
+    print(f"[bench] {ms_per_step * 1e3:.1f} us/step (graph replay); per launch: " +
+          ", ".join(f"{names[pi]}:{k}={v:.1f}us" for (pi, k), v in avg_us.items()),
+          file=sys.stderr, flush=True)
+
+    # Dominant kernel: the launch kind with the largest time per step.
+    dom = max(avg_us, key=lambda kk: avg_us[kk])
+    pi, kname = dom
+    w, p = wls[pi], paths[pi]
+    if kname == "attention":
+        fl, by = attn_flops(w), attn_bytes(w)
+        t_m, t_h = fl / (PEAK_BF16_TFLOPS * 1e12), by / (PEAK_HBM_GBS * 1e9)
+        if t_m >= t_h:
+            roof = {"bound": "mfma", "achieved": fl / (avg_us[dom] * 1e-6) / 1e12,
+                    "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+        else:
+            roof = {"bound": "hbm", "achieved": by / (avg_us[dom] * 1e-6) / 1e9,
+                    "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+        tag = f"attn_fwd_{names[pi]}"
+    else:
+        by = p.bytes_gather() if kname == "gather" else p.bytes_scatter()
+        roof = {"bound": "hbm", "achieved": by / (avg_us[dom] * 1e-6) / 1e9, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s"}
+        tag = f"{kname}_{names[pi]}"
+    roof["achieved"] = round(roof["achieved"], 2)
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = read_traffic(tag)
+    roof["kernel"] = f"{kname} ({names[pi]})"
+    roof["avg_launch_us"] = round(avg_us[dom], 2)
+
+    cfg_rows = []
+    if args.configs != "none":
+        flush_buf = torch.empty(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB > MALL + L2
+        flush = lambda: flush_buf.zero_()
+        cfg_names = list(gen.WORKLOADS) if args.configs == "all" else args.configs.split(",")
+        cfg_names = [n for n in cfg_names if not n.startswith("padded_")]
+        print(f"[bench] timing {len(cfg_names)} workloads", file=sys.stderr, flush=True)
+        cfg_rows = run_configs(torch, t, cfg_names, flush)
+        del flush_buf
+
+    cpu = None
+    if not args.no_cpu:
+        print("[bench] oracle CPU baseline", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(wls)
+
+    line = {
+        "metric": "fwd attention TFLOP/s & % bf16 MFMA peak; us/call varlen 32x64..1x8192",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"timing": "value: K replays of the step captured as a HIP graph; per_launch_us: HIP events per launch", "workload": "packed LLM path with padding: B=1 total_len=4096 H=16 D=128 causal, "
+                               "(a) 32 slots x 128 with valid lengths U{1..128} + (b) 1x2048 valid "
+                               "+ 2048 padding; unpad gather -> varlen attention -> pad scatter",
+                   "global_batch": 2, "seq_len": 4096, "parallelism": "none (1 GPU)",
+                   "per_launch_us": {f"{names[pi]}:{k}": round(v, 2) for (pi, k), v in avg_us.items()},
+                   "pct_bf16_peak_step": round(100 * value / PEAK_BF16_TFLOPS, 2)},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "configs": cfg_rows,
+        "kernel_source_hash": source_hash(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

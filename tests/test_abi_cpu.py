@@ -119,3 +119,10 @@ def test_gather_scatter_validation(lib):
     assert lib.attn_pad_scatter(P, None, P, 4, 8, 256, None) == NULL
     assert lib.attn_pad_scatter(None, P, P, 4, 8, 256, None) == NULL
     assert lib.attn_pad_scatter(P, P, P, 0, 0, 256, None) == OK
+
+
+def test_tile_override_rejects_uncompiled_policy(lib, monkeypatch):
+    monkeypatch.setenv("ATTN_FWD_TILE", "2")
+    assert varlen(lib, d=256) == UNSUP
+    monkeypatch.setenv("ATTN_FWD_TILE", "9")
+    assert varlen(lib, d=128) == UNSUP

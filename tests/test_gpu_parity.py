@@ -195,12 +195,14 @@ def test_future_perturbation_leaves_prefix_bitwise():
     assert np.array_equal(o1[:250], o2[:250]) and np.array_equal(l1[:, :250], l2[:, :250])
 
 
-@pytest.mark.parametrize("policy", ["0", "1"])
+@pytest.mark.parametrize("policy", ["0", "1", "2", "3"])
 def test_every_compiled_tile_policy(policy):
     os.environ["ATTN_FWD_TILE"] = policy
     try:
         for d in D_ALL:
-            w = gen.make_varlen("pol", 1000 + d, [150, 64, 1, 90], 2, 1, d, True)
+            if d == 256 and policy == "2":
+                continue  # not compiled: the register file cannot hold it
+            w = gen.make_varlen("pol", 1000 + d, [150, 64, 1, 90, 700], 2, 1, d, True)
             o, lse = run_varlen(w)
             o_ref, lse_ref = oracle.attention_varlen(w.q, w.k, w.v, w.cu_seqlens_q,
                                                      w.cu_seqlens_k, w.scale, True)

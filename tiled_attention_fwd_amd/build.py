@@ -17,6 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libattnfwd.so")
+MICROBENCH = os.path.join(PKG, "microbench")  # bench-only executable (unit rates, copy bandwidth)
 SOURCES = ["attn_kernel.hip", "rows_kernel.hip", "abi.cpp"]
 ARCH = "gfx950"
 
@@ -56,8 +57,14 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    cmd = [hipcc(), *COMMON_FLAGS, "-x", "hip", os.path.join(CSRC, "microbench.hip"), "-o",
+           MICROBENCH + ".tmp"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for microbench.hip:\n{r.stdout}\n{r.stderr}")
+    os.replace(MICROBENCH + ".tmp", MICROBENCH)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {MICROBENCH}")
     return LIB
 
 

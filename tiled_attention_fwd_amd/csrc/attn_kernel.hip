@@ -60,6 +60,24 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) {
   return __builtin_bit_cast(bf16x8, u);
 }
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource over [base, base + bytes): loads at offsets >= bytes return
+// zero, which is how rows past the end of a sequence read as zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+__device__ __forceinline__ uint32_t span_bytes(int rows, int64_t row_stride) {
+  const int64_t b = (int64_t)rows * row_stride * 2;
+  return b > 0xffffffffLL ? 0xffffffffu : (uint32_t)b;
+}
+
 // Key held by accumulator row i of a 32-key block (see the header comment).
 __device__ __forceinline__ int key_of_row(int i) {
   return ((i >> 4) << 4) + (((i >> 2) & 1) << 3) + (((i >> 3) & 1) << 2) + (i & 3);
@@ -80,13 +98,23 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-template <int D, int BN, int WAVES, int QC, bool VARLEN>
-__global__ __launch_bounds__(WAVES * 64) void attn_fwd_kernel(const AttnArgs a) {
+// Online-softmax rescale threshold in base-2 units.  The running row
+// maximum m used as the exp2 reference is only raised when a new tile's
+// maximum exceeds it by more than this; until then p = 2^(c*s - m) stays below
+// 2^8, far inside fp32 and bf16 range.  The final O / l and LSE = m + log2 l
+// are exact for whatever m was used, so skipping small rescales changes no
+// result beyond rounding, and it removes the per-tile pass over O.
+constexpr float kRescaleThreshold = 8.0f;
+
+template <int D, int BN, int WAVES, int QC, int MINW, bool VARLEN>
+__global__ __launch_bounds__(WAVES * 64, MINW) void attn_fwd_kernel(const AttnArgs a) {
   constexpr int NT = WAVES * 64;
   constexpr int BM = WAVES * 32 * QC;
   constexpr int PAD = 8;            // bf16 elements of padding per LDS row
   constexpr int KS = D + PAD;       // K tile row stride (keys are rows)
   constexpr int VS = BN + PAD;      // V^T tile row stride (dims are rows)
+  constexpr int KT_ELEMS = BN * KS;
+  constexpr int VT_ELEMS = D * VS;
   constexpr int NKB = BN / 32;      // 32-key blocks per tile
   constexpr int NDS = D / 16;       // 16-dim slices of one key row
   constexpr int NDB = D / 32;       // 32-dim blocks of the output
@@ -96,8 +124,9 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_kernel(const AttnArgs a) 
   constexpr int V_PER = (V_UNITS + NT - 1) / NT;
   static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
 
-  __shared__ __attribute__((aligned(16))) uint16_t ks[BN * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t vt[D * VS];
+  // Two K/V^T buffers: tile kt+1 is written while tile kt is read.
+  __shared__ __attribute__((aligned(16))) uint16_t ks[2 * KT_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t vt[2 * VT_ELEMS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -152,20 +181,34 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_kernel(const AttnArgs a) 
   const int qw0 = q0 + wave * 32 * QC;  // first query of this wave
   int kend_w = lk;
   if (a.causal) kend_w = min(lk, qw0 + 32 * QC + off);
+  if (qw0 >= lq) kend_w = 0;  // a wave made only of padding rows does no math
 
   // ---- Q^T fragments (B operand), kept in registers ----------------------
-  bf16x8 qf[QC][NDS];
+  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(qbase, span_bytes(lq, a.q_ss));
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase, span_bytes(lk, a.k_ss));
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase, span_bytes(lk, a.v_ss));
+  const uint32_t k_row_bytes = (uint32_t)a.k_ss * 2;
+  const uint32_t v_row_bytes = (uint32_t)a.v_ss * 2;
+  u32x4 qraw[QC][NDS];
 #pragma unroll
   for (int c = 0; c < QC; ++c) {
-    const int qrow = qw0 + c * 32 + l32;
-    const bool ok = qrow < lq;
-    const uint16_t* qp = qbase + (int64_t)(ok ? qrow : 0) * a.q_ss + hh * 8;
+    const int qrow = qw0 + c * 32 + l32;  // rows past lq read as zeros
+    const uint32_t qoff_b = (uint32_t)qrow * (uint32_t)a.q_ss * 2 + hh * 16;
+#pragma unroll
+    for (int s = 0; s < NDS; ++s)
+      qraw[c][s] = __builtin_amdgcn_raw_buffer_load_b128(qrs, (int)(qoff_b + 32 * s), 0, 0);
+  }
+  // Empty asm that "redefines" the loaded registers: the compiler waits for the
+  // Q loads once, here, instead of treating Q as in flight inside the key loop
+  // (where its wait would also drain the K/V prefetch on every iteration).
+  bf16x8 qf[QC][NDS];
+#pragma unroll
+  for (int c = 0; c < QC; ++c)
 #pragma unroll
     for (int s = 0; s < NDS; ++s) {
-      uint4 u = ok ? ld16(qp + 16 * s) : make_uint4(0, 0, 0, 0);
-      qf[c][s] = as_bf16x8(u);
+      asm volatile("" : "+v"(qraw[c][s]));
+      qf[c][s] = __builtin_bit_cast(bf16x8, qraw[c][s]);
     }
-  }
 
   f32x16 oacc[QC][NDB];
   float m_run[QC], l_run[QC];
@@ -182,41 +225,39 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_kernel(const AttnArgs a) 
   uint4 vreg[V_PER][4];
 
   auto fetch = [&](int kt) {
-    const int kbeg = kt * BN;
+    const uint32_t kbeg = kt * BN;
 #pragma unroll
     for (int i = 0; i < K_PER; ++i) {
       const int u = tid + i * NT;
       if (K_UNITS % NT == 0 || u < K_UNITS) {
-        const int row = u / (D / 8);
-        const int col = (u % (D / 8)) * 8;
-        const int key = kbeg + row;
-        kreg[i] = key < lk ? ld16(kbase + (int64_t)key * a.k_ss + col) : make_uint4(0, 0, 0, 0);
+        const uint32_t row = u / (D / 8);
+        const uint32_t col = (u % (D / 8)) * 8;
+        kreg[i] = buf_ld16(krs, (kbeg + row) * k_row_bytes + col * 2);
       }
     }
 #pragma unroll
     for (int i = 0; i < V_PER; ++i) {
       const int u = tid + i * NT;
       if (V_UNITS % NT == 0 || u < V_UNITS) {
-        const int kq = u % (BN / 4);
-        const int dq = u / (BN / 4);
+        const uint32_t kq = u % (BN / 4);
+        const uint32_t dq = u / (BN / 4);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int key = kbeg + kq * 4 + j;
-          vreg[i][j] = key < lk ? ld16(vbase + (int64_t)key * a.v_ss + dq * 8)
-                                : make_uint4(0, 0, 0, 0);
-        }
+        for (int j = 0; j < 4; ++j)
+          vreg[i][j] = buf_ld16(vrs, (kbeg + kq * 4 + j) * v_row_bytes + dq * 16);
       }
     }
   };
 
-  auto stage = [&]() {
+  auto stage = [&](int buf) {
+    uint16_t* kd = ks + buf * KT_ELEMS;
+    uint16_t* vd = vt + buf * VT_ELEMS;
 #pragma unroll
     for (int i = 0; i < K_PER; ++i) {
       const int u = tid + i * NT;
       if (K_UNITS % NT == 0 || u < K_UNITS) {
         const int row = u / (D / 8);
         const int col = (u % (D / 8)) * 8;
-        *reinterpret_cast<uint4*>(ks + row * KS + col) = kreg[i];
+        *reinterpret_cast<uint4*>(kd + row * KS + col) = kreg[i];
       }
     }
 #pragma unroll
@@ -231,39 +272,43 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_kernel(const AttnArgs a) 
         const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&vreg[i][3]);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          // dims dq*8+e of keys kq*4 .. kq*4+3 -> 4 consecutive bf16 of V^T row
+          // dims dq*8+e of keys kq*4 .. kq*4+3 -> 4 consecutive bf16 of a V^T row
           const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
           uint2 out;
           out.x = __builtin_amdgcn_perm(w1[e >> 1], w0[e >> 1], sel);
           out.y = __builtin_amdgcn_perm(w3[e >> 1], w2[e >> 1], sel);
-          *reinterpret_cast<uint2*>(vt + (dq * 8 + e) * VS + kq * 4) = out;
+          *reinterpret_cast<uint2*>(vd + (dq * 8 + e) * VS + kq * 4) = out;
         }
       }
     }
   };
 
-  if (n_kt > 0) fetch(0);
+  if (n_kt > 0) {
+    fetch(0);
+    stage(0);
+  }
+  __syncthreads();
 
   for (int kt = 0; kt < n_kt; ++kt) {
-    stage();
-    __syncthreads();
+    const int buf = kt & 1;
     if (kt + 1 < n_kt) fetch(kt + 1);
 
     const int kbeg = kt * BN;
-    if (qw0 < lq && kbeg < kend_w) {
+    if (kbeg < kend_w) {
+      const uint16_t* kd = ks + buf * KT_ELEMS;
+      const uint16_t* vd = vt + buf * VT_ELEMS;
       // ---- S^T = K Q^T ------------------------------------------------------
       f32x16 sacc[QC][NKB];
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-        for (int c = 0; c < QC; ++c) sacc[c][kb] = f32x16{};
-        const uint16_t* kr = ks + (kb * 32 + key_of_row(l32)) * KS + hh * 8;
+        const uint16_t* kr = kd + (kb * 32 + key_of_row(l32)) * KS + hh * 8;
 #pragma unroll
         for (int s = 0; s < NDS; ++s) {
           const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kr + 16 * s);
 #pragma unroll
           for (int c = 0; c < QC; ++c)
-            sacc[c][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c][s], sacc[c][kb], 0, 0, 0);
+            sacc[c][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                kf, qf[c][s], s == 0 ? f32x16{} : sacc[c][kb], 0, 0, 0);
         }
       }
 
@@ -285,7 +330,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_kernel(const AttnArgs a) 
         }
       }
 
-      // ---- online softmax (base 2) -----------------------------------------
+      // ---- online softmax (base 2, lazy rescale) ----------------------------
       bf16x8 pf[QC][NKB][2];
 #pragma unroll
       for (int c = 0; c < QC; ++c) {
@@ -295,18 +340,29 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_kernel(const AttnArgs a) 
 #pragma unroll
           for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[c][kb][r]);
         mx = half_max(mx);
-        const float m_new = fmaxf(m_run[c], mx * a.c);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run[c] - m_use);
-        m_run[c] = m_new;
-        float rs = 0.f;
+        const float cand = mx * a.c;
+        const bool grow = cand > m_run[c] + kRescaleThreshold;
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+          // Only lanes whose own maximum grew move their reference; the others
+          // scale by exactly 1, so a row's result never depends on its
+          // neighbours in the wave.  A lane can only grow from a finite cand,
+          // and m_run = -inf then gives alpha = 0.
+          const float m_new = grow ? cand : m_run[c];
+          const float alpha = grow ? __builtin_amdgcn_exp2f(m_run[c] - m_new) : 1.0f;
+          m_run[c] = m_new;
+          l_run[c] *= alpha;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) oacc[c][db] *= alpha;
+        }
+        const float m_use = (m_run[c] == -INFINITY) ? 0.f : m_run[c];
+        float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[c][kb][r], a.c, -m_use));
             sacc[c][kb][r] = pv;
-            rs += pv;
+            if (r & 1) rs1 += pv; else rs0 += pv;
           }
 #pragma unroll
           for (int t = 0; t < 2; ++t) {
@@ -318,15 +374,13 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_kernel(const AttnArgs a) 
             pf[c][kb][t] = as_bf16x8(u);
           }
         }
-        l_run[c] = l_run[c] * alpha + rs;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) oacc[c][db] *= alpha;
+        l_run[c] += rs0 + rs1;
       }
 
       // ---- O^T += V^T P^T ---------------------------------------------------
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const uint16_t* vr = vt + (db * 32 + l32) * VS + hh * 8;
+        const uint16_t* vr = vd + (db * 32 + l32) * VS + hh * 8;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
@@ -339,6 +393,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_kernel(const AttnArgs a) 
         }
       }
     }
+    if (kt + 1 < n_kt) stage(buf ^ 1);
     __syncthreads();
   }
 
@@ -370,13 +425,20 @@ __global__ __launch_bounds__(WAVES * 64) void attn_fwd_kernel(const AttnArgs a) 
   }
 }
 
-// Compiled policies.  id 0: 4 waves x 32 queries (BM 128); id 1: 2 waves x 32
-// queries (BM 64) for short sequences.  Keys per tile: 64 (32 at head_dim 256,
-// where the output accumulator alone takes 128 registers per lane).
-constexpr int kNumPolicies = 2;
+// Compiled tile policies (id: waves x 32-query columns per wave, min waves
+// per SIMD).  Keys per tile: 64 (32 at head_dim 256, whose output
+// accumulator alone takes 128 registers per lane).
+//   0: 4 waves x 1 column  (BM 128), 2 waves/SIMD -> two workgroups per CU
+//   1: 2 waves x 1 column  (BM  64), for short sequences
+//   2: 4 waves x 2 columns (BM 256), 1 wave/SIMD: each K/V fragment read from
+//      LDS feeds two MFMAs
+//   3: 8 waves x 1 column  (BM 256), 2 waves/SIMD in one workgroup
+constexpr int kNumPolicies = 4;
 
 template <int D>
 constexpr int bn_for() { return D == 256 ? 32 : 64; }
+template <int D>
+constexpr int minw_for() { return D == 256 ? 1 : 2; }
 
 template <int D, bool VARLEN>
 hipError_t launch_d(const AttnArgs& a, int policy_id, hipStream_t stream) {
@@ -384,14 +446,27 @@ hipError_t launch_d(const AttnArgs& a, int policy_id, hipStream_t stream) {
   const int64_t grid = rows * a.n_qb;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  const dim3 g((unsigned)grid);
   switch (policy_id) {
     case 0:
-      hipLaunchKernelGGL((attn_fwd_kernel<D, bn_for<D>(), 4, 1, VARLEN>), dim3((unsigned)grid),
+      hipLaunchKernelGGL((attn_fwd_kernel<D, bn_for<D>(), 4, 1, minw_for<D>(), VARLEN>), g,
                          dim3(256), 0, stream, a);
       break;
     case 1:
-      hipLaunchKernelGGL((attn_fwd_kernel<D, bn_for<D>(), 2, 1, VARLEN>), dim3((unsigned)grid),
+      hipLaunchKernelGGL((attn_fwd_kernel<D, bn_for<D>(), 2, 1, minw_for<D>(), VARLEN>), g,
                          dim3(128), 0, stream, a);
+      break;
+    case 2:
+      if constexpr (D == 256) {
+        return hipErrorInvalidValue;
+      } else {
+        hipLaunchKernelGGL((attn_fwd_kernel<D, bn_for<D>(), 4, 2, 1, VARLEN>), g, dim3(256), 0,
+                           stream, a);
+      }
+      break;
+    case 3:
+      hipLaunchKernelGGL((attn_fwd_kernel<D, bn_for<D>(), 8, 1, minw_for<D>(), VARLEN>), g,
+                         dim3(512), 0, stream, a);
       break;
     default:
       return hipErrorInvalidValue;
@@ -407,15 +482,17 @@ hipError_t launch_v(const AttnArgs& a, bool varlen, int policy_id, hipStream_t s
 }  // namespace
 
 bool select_policy(int head_dim, int max_seqlen_q, int override_id, TilePolicy* out, int* policy_id) {
+  static const TilePolicy kTable[kNumPolicies] = {{4, 1, 64}, {2, 1, 64}, {4, 2, 64}, {8, 1, 64}};
   int id;
   if (override_id >= 0) {
     if (override_id >= kNumPolicies) return false;
+    if (head_dim == 256 && override_id == 2) return false;  // would not fit the register file
     id = override_id;
   } else {
     id = max_seqlen_q <= 64 ? 1 : 0;
   }
-  const int bn = head_dim == 256 ? 32 : 64;
-  *out = (id == 0) ? TilePolicy{4, 1, bn} : TilePolicy{2, 1, bn};
+  *out = kTable[id];
+  if (head_dim == 256) out->bn = 32;
   *policy_id = id;
   return true;
 }

@@ -1,0 +1,172 @@
+// Microbenchmarks that ground the roofline figures used for the attention
+// kernel on gfx950: MFMA bf16 32x32x16 rate, v_exp_f32 and v_fma_f32 issue
+// rates, LDS 16-byte read bandwidth, and a plain 16-byte copy kernel (its
+// known byte count calibrates the HBM traffic counters).
+//
+// Prints one JSON object.  Every kernel only touches buffers it allocates, with
+// indices bounded by the launch shape.
+
+#include <hip/hip_runtime.h>
+#include <stdio.h>
+#include <stdlib.h>
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+#define CHECK(x)                                                             \
+  do {                                                                       \
+    hipError_t e_ = (x);                                                     \
+    if (e_ != hipSuccess) {                                                  \
+      fprintf(stderr, "HIP error %s at %s:%d\n", hipGetErrorString(e_), __FILE__, __LINE__); \
+      exit(1);                                                               \
+    }                                                                        \
+  } while (0)
+
+constexpr int kIters = 2048;
+
+__global__ __launch_bounds__(256) void mfma_kernel(float* out, float seed) {
+  bf16x8 a, b;
+  for (int e = 0; e < 8; ++e) {
+    a[e] = (__bf16)(seed * (threadIdx.x + e));
+    b[e] = (__bf16)(seed * (e + 1));
+  }
+  f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  for (int i = 0; i < kIters; ++i) {
+    c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c1, 0, 0, 0);
+    c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c2, 0, 0, 0);
+    c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c3, 0, 0, 0);
+  }
+  float s = 0.f;
+  for (int r = 0; r < 16; ++r) s += c0[r] + c1[r] + c2[r] + c3[r];
+  out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+__global__ __launch_bounds__(256) void exp_kernel(float* out, float seed) {
+  float x[8];
+  for (int j = 0; j < 8; ++j) x[j] = seed * (threadIdx.x + j) * 1e-6f;
+  for (int i = 0; i < kIters; ++i) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = __builtin_amdgcn_exp2f(x[j]) - 1.0f;
+  }
+  float s = 0.f;
+  for (int j = 0; j < 8; ++j) s += x[j];
+  out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+__global__ __launch_bounds__(256) void exp_only_kernel(float* out, float seed) {
+  // exp2 of exp2: no extra VALU op between transcendental instructions
+  float x[8];
+  for (int j = 0; j < 8; ++j) x[j] = -seed * (threadIdx.x + j);
+  for (int i = 0; i < kIters; ++i) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = -__builtin_amdgcn_exp2f(x[j]);
+  }
+  float s = 0.f;
+  for (int j = 0; j < 8; ++j) s += x[j];
+  out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+__global__ __launch_bounds__(256) void fma_kernel(float* out, float seed) {
+  float x[8];
+  for (int j = 0; j < 8; ++j) x[j] = seed * (threadIdx.x + j);
+  for (int i = 0; i < kIters; ++i) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = fmaf(x[j], 0.999f, 0.001f);
+  }
+  float s = 0.f;
+  for (int j = 0; j < 8; ++j) s += x[j];
+  out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+__global__ __launch_bounds__(256) void lds_kernel(float* out) {
+  __shared__ __attribute__((aligned(16))) uint4 buf[4096];  // 64 KiB
+  for (int i = threadIdx.x; i < 4096; i += 256) buf[i] = make_uint4(i, i + 1, i + 2, i + 3);
+  __syncthreads();
+  uint4 acc = make_uint4(0, 0, 0, 0);
+  int idx = threadIdx.x;
+  for (int i = 0; i < kIters; ++i) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint4 v = buf[(idx + j * 256) & 4095];
+      acc.x ^= v.x; acc.y ^= v.y; acc.z ^= v.z; acc.w ^= v.w;
+    }
+    idx = (idx + 64 + (acc.x & 1)) & 4095;
+  }
+  out[blockIdx.x * blockDim.x + threadIdx.x] = (float)(acc.x ^ acc.y ^ acc.z ^ acc.w);
+}
+
+__global__ __launch_bounds__(256) void copy_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                                                  long n) {
+  long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  long stride = (long)gridDim.x * blockDim.x;
+  for (; i < n; i += stride) dst[i] = src[i];
+}
+
+template <typename F>
+float time_ms(F launch, int reps) {
+  hipEvent_t a, b;
+  CHECK(hipEventCreate(&a));
+  CHECK(hipEventCreate(&b));
+  launch();
+  CHECK(hipDeviceSynchronize());
+  CHECK(hipEventRecord(a, 0));
+  for (int i = 0; i < reps; ++i) launch();
+  CHECK(hipEventRecord(b, 0));
+  CHECK(hipEventSynchronize(b));
+  float ms = 0.f;
+  CHECK(hipEventElapsedTime(&ms, a, b));
+  CHECK(hipEventDestroy(a));
+  CHECK(hipEventDestroy(b));
+  return ms / reps;
+}
+
+int main(int argc, char** argv) {
+  long copy_bytes = argc > 1 ? atol(argv[1]) : (1L << 30);
+  hipDeviceProp_t prop;
+  CHECK(hipGetDeviceProperties(&prop, 0));
+  const int cus = prop.multiProcessorCount;
+  const int blocks = cus * 8;  // 8 workgroups of 4 waves per CU: 8 waves per SIMD
+  float* out;
+  CHECK(hipMalloc(&out, (size_t)blocks * 256 * sizeof(float)));
+
+  const double waves = (double)blocks * 4;
+  double ms;
+
+  ms = time_ms([&] { hipLaunchKernelGGL(mfma_kernel, dim3(blocks), dim3(256), 0, 0, out, 1e-3f); }, 5);
+  const double mfma_flops = waves * kIters * 4 * 32.0 * 32 * 16 * 2;
+  const double mfma_tflops = mfma_flops / (ms * 1e-3) / 1e12;
+
+  ms = time_ms([&] { hipLaunchKernelGGL(exp_kernel, dim3(blocks), dim3(256), 0, 0, out, 1.0f); }, 5);
+  const double exp_sub_ops = waves * 64.0 * kIters * 8;  // lane-ops of exp (+ one sub each)
+  const double exp_sub_rate = exp_sub_ops / (ms * 1e-3) / 1e12;
+
+  ms = time_ms([&] { hipLaunchKernelGGL(exp_only_kernel, dim3(blocks), dim3(256), 0, 0, out, 1.0f); }, 5);
+  const double exp_rate = exp_sub_ops / (ms * 1e-3) / 1e12;
+
+  ms = time_ms([&] { hipLaunchKernelGGL(fma_kernel, dim3(blocks), dim3(256), 0, 0, out, 1.0f); }, 5);
+  const double fma_rate = waves * 64.0 * kIters * 8 / (ms * 1e-3) / 1e12;
+
+  ms = time_ms([&] { hipLaunchKernelGGL(lds_kernel, dim3(cus * 2), dim3(256), 0, 0, out); }, 5);
+  const double lds_bytes = (double)cus * 2 * 256 * kIters * 4 * 16;
+  const double lds_tbs = lds_bytes / (ms * 1e-3) / 1e12;
+
+  uint4 *src, *dst;
+  const long n = copy_bytes / 16;
+  CHECK(hipMalloc(&src, n * 16));
+  CHECK(hipMalloc(&dst, n * 16));
+  CHECK(hipMemset(src, 1, n * 16));
+  ms = time_ms([&] { hipLaunchKernelGGL(copy_kernel, dim3(cus * 16), dim3(256), 0, 0, src, dst, n); }, 10);
+  const double copy_gbs = 2.0 * n * 16 / (ms * 1e-3) / 1e9;
+
+  printf("{\"device\": \"%s\", \"cus\": %d, \"clock_mhz\": %d, "
+         "\"mfma_bf16_32x32x16_tflops\": %.1f, \"exp2_plus_sub_tops\": %.3f, "
+         "\"exp2_tops\": %.3f, \"fma_tops\": %.3f, \"lds_read_tbs\": %.2f, "
+         "\"copy_gbs\": %.1f, \"copy_bytes_each_way\": %ld}\n",
+         prop.name, cus, prop.clockRate / 1000, mfma_tflops, exp_sub_rate, exp_rate, fma_rate,
+         lds_tbs, copy_gbs, n * 16);
+  CHECK(hipFree(src));
+  CHECK(hipFree(dst));
+  CHECK(hipFree(out));
+  return 0;
+}
