@@ -195,7 +195,7 @@ def test_future_perturbation_leaves_prefix_bitwise():
     assert np.array_equal(o1[:250], o2[:250]) and np.array_equal(l1[:, :250], l2[:, :250])
 
 
-@pytest.mark.parametrize("policy", ["0", "1", "2", "3"])
+@pytest.mark.parametrize("policy", [str(i) for i in range(8)])
 def test_every_compiled_tile_policy(policy):
     os.environ["ATTN_FWD_TILE"] = policy
     try:

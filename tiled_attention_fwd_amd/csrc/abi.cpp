@@ -42,7 +42,8 @@ attn_status_t check_common(int32_t hq, int32_t hkv, int32_t d, float scale) {
 attn_status_t launch(AttnArgs& a, int d, bool varlen, int max_q, hipStream_t stream) {
   TilePolicy pol;
   int pid;
-  if (!attnfwd::select_policy(d, max_q, tile_override(), &pol, &pid)) return ATTN_ERR_UNSUPPORTED;
+  if (!attnfwd::select_policy(d, max_q, a.causal != 0, tile_override(), &pol, &pid))
+    return ATTN_ERR_UNSUPPORTED;
   a.n_qb = (max_q + pol.bm() - 1) / pol.bm();
   const int64_t rows = (int64_t)a.nseq * a.hq;
   if (rows * a.n_qb > 0x7fffffffLL) return ATTN_ERR_SHAPE;

@@ -106,16 +106,22 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 // result beyond rounding, and it removes the per-tile pass over O.
 constexpr float kRescaleThreshold = 8.0f;
 
-template <int D, int BN, int WAVES, int QC, int MINW, bool VARLEN>
+// Kernel variant flags.
+constexpr int kPrio = 1;  // raise wave priority while issuing MFMA blocks
+
+template <int D, int BN, int WAVES, int QC, int MINW, bool VARLEN, int FLAGS = 0>
 __global__ __launch_bounds__(WAVES * 64, MINW) void attn_fwd_kernel(const AttnArgs a) {
   constexpr int NT = WAVES * 64;
+  constexpr int SUB = D == 256 ? 32 : 64;  // keys per softmax sub-block (bounds live registers)
+  constexpr int NSB = BN / SUB;
+  static_assert(BN % SUB == 0, "tile must hold whole sub-blocks");
   constexpr int BM = WAVES * 32 * QC;
   constexpr int PAD = 8;            // bf16 elements of padding per LDS row
   constexpr int KS = D + PAD;       // K tile row stride (keys are rows)
   constexpr int VS = BN + PAD;      // V^T tile row stride (dims are rows)
   constexpr int KT_ELEMS = BN * KS;
   constexpr int VT_ELEMS = D * VS;
-  constexpr int NKB = BN / 32;      // 32-key blocks per tile
+  constexpr int NKB = SUB / 32;     // 32-key blocks per sub-block
   constexpr int NDS = D / 16;       // 16-dim slices of one key row
   constexpr int NDB = D / 32;       // 32-dim blocks of the output
   constexpr int K_UNITS = BN * D / 8;          // 16-byte chunks of a K tile
@@ -293,11 +299,14 @@ __global__ __launch_bounds__(WAVES * 64, MINW) void attn_fwd_kernel(const AttnAr
     const int buf = kt & 1;
     if (kt + 1 < n_kt) fetch(kt + 1);
 
-    const int kbeg = kt * BN;
+#pragma unroll
+    for (int sb = 0; sb < NSB; ++sb) {
+    const int kbeg = kt * BN + sb * SUB;
     if (kbeg < kend_w) {
-      const uint16_t* kd = ks + buf * KT_ELEMS;
-      const uint16_t* vd = vt + buf * VT_ELEMS;
+      const uint16_t* kd = ks + buf * KT_ELEMS + sb * SUB * KS;
+      const uint16_t* vd = vt + buf * VT_ELEMS + sb * SUB;
       // ---- S^T = K Q^T ------------------------------------------------------
+      if constexpr (FLAGS & kPrio) __builtin_amdgcn_s_setprio(1);
       f32x16 sacc[QC][NKB];
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
@@ -311,9 +320,10 @@ __global__ __launch_bounds__(WAVES * 64, MINW) void attn_fwd_kernel(const AttnAr
                 kf, qf[c][s], s == 0 ? f32x16{} : sacc[c][kb], 0, 0, 0);
         }
       }
+      if constexpr (FLAGS & kPrio) __builtin_amdgcn_s_setprio(0);
 
-      // ---- mask (only tiles crossing the diagonal or the sequence end) -------
-      const bool need_mask = (kbeg + BN > lk) || (a.causal && kbeg + BN - 1 > qw0 + off);
+      // ---- mask (only sub-blocks crossing the diagonal or the sequence end) --
+      const bool need_mask = (kbeg + SUB > lk) || (a.causal && kbeg + SUB - 1 > qw0 + off);
       if (need_mask) {
 #pragma unroll
         for (int c = 0; c < QC; ++c) {
@@ -378,6 +388,7 @@ __global__ __launch_bounds__(WAVES * 64, MINW) void attn_fwd_kernel(const AttnAr
       }
 
       // ---- O^T += V^T P^T ---------------------------------------------------
+      if constexpr (FLAGS & kPrio) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
         const uint16_t* vr = vd + (db * 32 + l32) * VS + hh * 8;
@@ -392,6 +403,8 @@ __global__ __launch_bounds__(WAVES * 64, MINW) void attn_fwd_kernel(const AttnAr
           }
         }
       }
+      if constexpr (FLAGS & kPrio) __builtin_amdgcn_s_setprio(0);
+    }
     }
     if (kt + 1 < n_kt) stage(buf ^ 1);
     __syncthreads();
@@ -433,7 +446,11 @@ __global__ __launch_bounds__(WAVES * 64, MINW) void attn_fwd_kernel(const AttnAr
 //   2: 4 waves x 2 columns (BM 256), 1 wave/SIMD: each K/V fragment read from
 //      LDS feeds two MFMAs
 //   3: 8 waves x 1 column  (BM 256), 2 waves/SIMD in one workgroup
-constexpr int kNumPolicies = 4;
+//   4: as 3, with raised wave priority while a wave issues its MFMA blocks
+//   5: as 3, with 2x longer key tiles (one barrier per two sub-blocks)
+//   6: as 5, with raised priority around MFMA blocks
+//   7: as 0, with raised priority around MFMA blocks
+constexpr int kNumPolicies = 8;
 
 template <int D>
 constexpr int bn_for() { return D == 256 ? 32 : 64; }
@@ -468,6 +485,22 @@ hipError_t launch_d(const AttnArgs& a, int policy_id, hipStream_t stream) {
       hipLaunchKernelGGL((attn_fwd_kernel<D, bn_for<D>(), 8, 1, minw_for<D>(), VARLEN>), g,
                          dim3(512), 0, stream, a);
       break;
+    case 4:
+      hipLaunchKernelGGL((attn_fwd_kernel<D, bn_for<D>(), 8, 1, minw_for<D>(), VARLEN, kPrio>), g,
+                         dim3(512), 0, stream, a);
+      break;
+    case 5:
+      hipLaunchKernelGGL((attn_fwd_kernel<D, 2 * bn_for<D>(), 8, 1, minw_for<D>(), VARLEN>), g,
+                         dim3(512), 0, stream, a);
+      break;
+    case 6:
+      hipLaunchKernelGGL((attn_fwd_kernel<D, 2 * bn_for<D>(), 8, 1, minw_for<D>(), VARLEN, kPrio>),
+                         g, dim3(512), 0, stream, a);
+      break;
+    case 7:
+      hipLaunchKernelGGL((attn_fwd_kernel<D, bn_for<D>(), 4, 1, minw_for<D>(), VARLEN, kPrio>), g,
+                         dim3(256), 0, stream, a);
+      break;
     default:
       return hipErrorInvalidValue;
   }
@@ -481,18 +514,26 @@ hipError_t launch_v(const AttnArgs& a, bool varlen, int policy_id, hipStream_t s
 
 }  // namespace
 
-bool select_policy(int head_dim, int max_seqlen_q, int override_id, TilePolicy* out, int* policy_id) {
-  static const TilePolicy kTable[kNumPolicies] = {{4, 1, 64}, {2, 1, 64}, {4, 2, 64}, {8, 1, 64}};
+bool select_policy(int head_dim, int max_seqlen_q, bool causal, int override_id, TilePolicy* out,
+                   int* policy_id) {
+  static const TilePolicy kTable[kNumPolicies] = {{4, 1, 64}, {2, 1, 64}, {4, 2, 64}, {8, 1, 64},
+                                                  {8, 1, 64}, {8, 1, 128}, {8, 1, 128}, {4, 1, 64}};
   int id;
   if (override_id >= 0) {
     if (override_id >= kNumPolicies) return false;
     if (head_dim == 256 && override_id == 2) return false;  // would not fit the register file
     id = override_id;
+  } else if (max_seqlen_q <= 64) {
+    id = 1;  // one 64-query block covers every sequence
+  } else if (head_dim == 128 && max_seqlen_q >= 256) {
+    id = 3;  // 256-query blocks: one K/V staging feeds eight waves
+  } else if (head_dim == 64 && !causal && max_seqlen_q >= 256) {
+    id = 3;
   } else {
-    id = max_seqlen_q <= 64 ? 1 : 0;
+    id = 0;
   }
   *out = kTable[id];
-  if (head_dim == 256) out->bn = 32;
+  if (head_dim == 256) out->bn /= 2;
   *policy_id = id;
   return true;
 }

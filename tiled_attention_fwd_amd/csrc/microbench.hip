@@ -84,14 +84,13 @@ __global__ __launch_bounds__(256) void lds_kernel(float* out) {
   for (int i = threadIdx.x; i < 4096; i += 256) buf[i] = make_uint4(i, i + 1, i + 2, i + 3);
   __syncthreads();
   uint4 acc = make_uint4(0, 0, 0, 0);
-  int idx = threadIdx.x;
+  // independent 16-byte reads: addresses depend on the loop counter only
   for (int i = 0; i < kIters; ++i) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint4 v = buf[(idx + j * 256) & 4095];
+    for (int j = 0; j < 8; ++j) {
+      const uint4 v = buf[(threadIdx.x + j * 256 + i * 64) & 4095];
       acc.x ^= v.x; acc.y ^= v.y; acc.z ^= v.z; acc.w ^= v.w;
     }
-    idx = (idx + 64 + (acc.x & 1)) & 4095;
   }
   out[blockIdx.x * blockDim.x + threadIdx.x] = (float)(acc.x ^ acc.y ^ acc.z ^ acc.w);
 }
@@ -148,7 +147,7 @@ int main(int argc, char** argv) {
   const double fma_rate = waves * 64.0 * kIters * 8 / (ms * 1e-3) / 1e12;
 
   ms = time_ms([&] { hipLaunchKernelGGL(lds_kernel, dim3(cus * 2), dim3(256), 0, 0, out); }, 5);
-  const double lds_bytes = (double)cus * 2 * 256 * kIters * 4 * 16;
+  const double lds_bytes = (double)cus * 2 * 256 * kIters * 8 * 16;
   const double lds_tbs = lds_bytes / (ms * 1e-3) / 1e12;
 
   uint4 *src, *dst;
