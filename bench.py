@@ -11,8 +11,8 @@ each as unpad gather of q, k, v (one launch) -> causal varlen attention
 Printed: ONE JSON line.  `value` is attention TFLOP/s of the whole step (exact
 causal FLOPs = 4 * D * H * visible (query, key) pairs, divided by the wall time
 of K back-to-back steps with inputs resident in HBM).  `roofline` reports the
-kernel that takes the most time per step, measured with HIP events recorded
-on the launch stream around each of its launches inside the timed region.
+kernel that takes the most time per step; its average launch duration comes
+from HIP events on the launch stream around batches of its launches.
 `cpu_baseline` times the fp64 oracle on the host for the same step.
 `configs` adds one row per listed workload (cold-cache per-call timing).
 """
@@ -171,7 +171,16 @@ def run_configs(torch, t, names, flush):
         w = gen.build_workload(name)
         dev = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to("cuda").view(torch.bfloat16)
         q, k, v = dev(w.q), dev(w.k), dev(w.v)
-        if w.kind == "dense":
+        if w.kind == "padded":
+            # the whole padded path as one span: gather q,k,v -> attention -> scatter
+            pp = PaddedPath(w, torch, t)
+            o, lse = pp.o, pp.lse
+
+            def fn(pp=pp):
+                pp.gather()
+                pp.attention()
+                pp.scatter()
+        elif w.kind == "dense":
             o = torch.empty(w.q.shape, dtype=torch.float32, device="cuda")
             lse = torch.empty((w.q.shape[0], w.hq, w.q.shape[1]), dtype=torch.float32, device="cuda")
             fn = lambda: t.attn_fwd_dense(q, k, v, scale=float(w.scale), causal=w.causal, out=o, lse=lse)
@@ -183,6 +192,8 @@ def run_configs(torch, t, names, flush):
             fn = lambda: t.attn_fwd_varlen(q, k, v, cq, ck, w.max_seqlen, scale=float(w.scale),
                                            causal=w.causal, out=o, lse=lse)
         fl, by = attn_flops(w), attn_bytes(w)
+        if w.kind == "padded":
+            by = by + pp.bytes_gather() + pp.bytes_scatter()
         probe = time_calls(torch, fn, 3, 2)
         iters = int(min(50, max(5, 0.25e6 / max(1.0, statistics.median(probe)))))
         cold = time_calls(torch, fn, iters, 1, flush=flush)
@@ -280,7 +291,9 @@ def main():
     flops_step = sum(attn_flops(w) for w in wls)
 
     def busy():
-        spin(torch)
+        # ~1.5 ms of spinning: room for a batch of 20 launches to be enqueued
+        for _ in range(3):
+            spin(torch)
 
     def step():
         for p in paths:
@@ -318,25 +331,34 @@ def main():
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     value = flops_step / (ms_per_step * 1e-3) / 1e12
 
-    # Timed region 2: K eager steps with HIP events on the launch stream around
-    # every launch.  A spin kernel queued first keeps the GPU busy while the
-    # host enqueues the step, so each event pair brackets only its kernel.
+    # Timed region 2: per-launch device time of each kernel of the step.  For
+    # each launch kind, a spin kernel is queued first so the host can enqueue a
+    # batch of identical launches (same inputs and outputs, so idempotent)
+    # before the GPU reaches them; one pair of HIP events on the launch stream
+    # brackets the batch, and the average per launch is elapsed / batch.
     s = torch.cuda.current_stream()
     kinds = [(pi, k) for pi in range(len(paths)) for k in ("gather", "attention", "scatter")]
-    ev = {kk: [] for kk in kinds}
+    batch = 20
+    avg_us = {}
+    busy()  # first use of the spin kernel loads its code; keep that out of the timing
     torch.cuda.synchronize()
-    for _ in range(args.steps):
-        busy()
-        for pi, p in enumerate(paths):
-            for kname in ("gather", "attention", "scatter"):
-                a = torch.cuda.Event(enable_timing=True)
-                b = torch.cuda.Event(enable_timing=True)
-                a.record(s)
-                getattr(p, kname)()
-                b.record(s)
-                ev[(pi, kname)].append((a, b))
-    torch.cuda.synchronize()
-    avg_us = {kk: statistics.mean(a.elapsed_time(b) for a, b in lst) * 1e3 for kk, lst in ev.items()}
+    for kk in kinds:
+        pi, kname = kk
+        fn = getattr(paths[pi], kname)
+        samples = []
+        for it in range(1 + max(1, args.steps // batch)):
+            torch.cuda.synchronize()
+            busy()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(s)
+            for _ in range(batch):
+                fn()
+            b.record(s)
+            b.synchronize()
+            if it > 0:  # the first batch is an untimed warm-up
+                samples.append(a.elapsed_time(b) * 1e3 / batch)
+        avg_us[kk] = statistics.median(samples)
     print(f"[bench] {ms_per_step * 1e3:.1f} us/step (graph replay); per launch: " +
           ", ".join(f"{names[pi]}:{k}={v:.1f}us" for (pi, k), v in avg_us.items()),
           file=sys.stderr, flush=True)
@@ -371,7 +393,6 @@ def main():
         flush_buf = torch.empty(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB > MALL + L2
         flush = lambda: flush_buf.zero_()
         cfg_names = list(gen.WORKLOADS) if args.configs == "all" else args.configs.split(",")
-        cfg_names = [n for n in cfg_names if not n.startswith("padded_")]
         print(f"[bench] timing {len(cfg_names)} workloads", file=sys.stderr, flush=True)
         cfg_rows = run_configs(torch, t, cfg_names, flush)
         del flush_buf
@@ -386,7 +407,7 @@ def main():
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"timing": "value: K replays of the step captured as a HIP graph; per_launch_us: HIP events per launch", "workload": "packed LLM path with padding: B=1 total_len=4096 H=16 D=128 causal, "
+        "config": {"timing": "value: K replays of the step captured as a HIP graph; per_launch_us: HIP events around batches of 20 identical launches, queue pre-filled by a spin kernel", "workload": "packed LLM path with padding: B=1 total_len=4096 H=16 D=128 causal, "
                                "(a) 32 slots x 128 with valid lengths U{1..128} + (b) 1x2048 valid "
                                "+ 2048 padding; unpad gather -> varlen attention -> pad scatter",
                    "global_batch": 2, "seq_len": 4096, "parallelism": "none (1 GPU)",

@@ -76,6 +76,8 @@ typedef enum {
  * Grouped-query attention: num_heads_q must be a multiple of num_heads_k;
  * query head h reads key/value head h / (num_heads_q / num_heads_k).
  * head_dim must be 32, 64, 128 or 256.  Every pointer must be 16-byte aligned.
+ * Size limit: q and k must each span less than 4 GiB (tile loads use 32-bit
+ * byte offsets); larger inputs return ATTN_ERR_SHAPE.
  */
 attn_status_t attn_fwd_varlen(const void* q, const void* k, const void* v,
                               const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
@@ -101,7 +103,8 @@ attn_status_t attn_fwd_varlen(const void* q, const void* k, const void* v,
  *      multiple of 8 elements (16 bytes of bf16) and of 4 for out.
  * lse (batch, num_heads_q, seqlen_q) fp32 contiguous, or NULL.
  * scale, causal, head_dim, grouped-query heads and the fully-masked-row rule
- * are as for attn_fwd_varlen.
+ * are as for attn_fwd_varlen.  Size limit: one sequence of q, k or v must span
+ * less than 4 GiB (seqlen * seq stride * 2 bytes); else ATTN_ERR_SHAPE.
  */
 attn_status_t attn_fwd_dense(const void* q, const void* k, const void* v,
                              int32_t batch, int32_t seqlen_q, int32_t seqlen_k,

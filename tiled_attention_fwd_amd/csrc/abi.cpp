@@ -39,13 +39,18 @@ attn_status_t check_common(int32_t hq, int32_t hkv, int32_t d, float scale) {
   return ATTN_OK;
 }
 
+// Tile loads address one sequence's rows through 32-bit buffer offsets.
+bool span_fits(int64_t rows, int64_t row_stride_elems) {
+  return rows * row_stride_elems * 2 < (1LL << 32);
+}
+
 attn_status_t launch(AttnArgs& a, int d, bool varlen, int max_q, hipStream_t stream) {
   TilePolicy pol;
   int pid;
-  if (!attnfwd::select_policy(d, max_q, a.causal != 0, tile_override(), &pol, &pid))
+  const int64_t rows = (int64_t)a.nseq * a.hq;
+  if (!attnfwd::select_policy(d, max_q, a.causal != 0, rows, tile_override(), &pol, &pid))
     return ATTN_ERR_UNSUPPORTED;
   a.n_qb = (max_q + pol.bm() - 1) / pol.bm();
-  const int64_t rows = (int64_t)a.nseq * a.hq;
   if (rows * a.n_qb > 0x7fffffffLL) return ATTN_ERR_SHAPE;
   a.xcd_remap = (rows % 8 == 0) ? 1 : 0;
   hipError_t e = attnfwd::launch_attention(a, d, varlen, pid, stream);
@@ -98,6 +103,7 @@ attn_status_t attn_fwd_varlen(const void* q, const void* k, const void* v,
   a.group = num_heads_q / num_heads_k;
   a.c = base2_factor(scale);
   a.causal = causal ? 1 : 0;
+  if (!span_fits(total_q, a.q_ss) || !span_fits(total_k, a.k_ss)) return ATTN_ERR_SHAPE;
   const int max_q = max_seqlen < total_q ? max_seqlen : total_q;
   return launch(a, head_dim, true, max_q, static_cast<hipStream_t>(stream));
 }
@@ -157,6 +163,8 @@ attn_status_t attn_fwd_dense(const void* q, const void* k, const void* v, int32_
   a.sk = seqlen_k;
   a.c = base2_factor(scale);
   a.causal = causal ? 1 : 0;
+  if (!span_fits(seqlen_q, a.q_ss) || !span_fits(seqlen_k, a.k_ss) || !span_fits(seqlen_k, a.v_ss))
+    return ATTN_ERR_SHAPE;
   return launch(a, head_dim, false, seqlen_q, static_cast<hipStream_t>(stream));
 }
 

@@ -40,8 +40,9 @@ struct TilePolicy {
 
 // Picks the policy for a head_dim and the longest query length.  `override_id`
 // (>= 0) forces one of the compiled policies for sweeps.
-bool select_policy(int head_dim, int max_seqlen_q, bool causal, int override_id, TilePolicy* out,
-                   int* policy_id);
+// `rows` is the number of (sequence, head) pairs of the launch.
+bool select_policy(int head_dim, int max_seqlen_q, bool causal, int64_t rows, int override_id,
+                   TilePolicy* out, int* policy_id);
 
 // Enqueues one attention launch.  Returns hipSuccess or the launch error.
 hipError_t launch_attention(const AttnArgs& a, int head_dim, bool varlen, int policy_id,
