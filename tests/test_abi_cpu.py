@@ -124,5 +124,9 @@ def test_gather_scatter_validation(lib):
 def test_tile_override_rejects_uncompiled_policy(lib, monkeypatch):
     monkeypatch.setenv("ATTN_FWD_TILE", "2")
     assert varlen(lib, d=256) == UNSUP
+    for pol in ("11", "14", "15", "16"):
+        monkeypatch.setenv("ATTN_FWD_TILE", pol)
+        assert varlen(lib, d=256) == UNSUP
+        assert varlen(lib, d=32) == UNSUP
     monkeypatch.setenv("ATTN_FWD_TILE", "99")
     assert varlen(lib, d=128) == UNSUP

@@ -195,17 +195,23 @@ def test_future_perturbation_leaves_prefix_bitwise():
     assert np.array_equal(o1[:250], o2[:250]) and np.array_equal(l1[:, :250], l2[:, :250])
 
 
-@pytest.mark.parametrize("policy", [str(i) for i in range(9)])
-def test_every_compiled_tile_policy(policy):
+# Policies the library does not compile for a head_dim (register or LDS budget).
+NOT_COMPILED = {256: {"2", "8", "9", "10", "11", "12", "14", "15", "16"},
+                32: {"11", "14", "15", "16"}}
+
+
+@pytest.mark.parametrize("policy", [str(i) for i in range(17)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_every_compiled_tile_policy(policy, causal):
     os.environ["ATTN_FWD_TILE"] = policy
     try:
         for d in D_ALL:
-            if d == 256 and policy in ("2", "8"):
-                continue  # not compiled for head_dim 256
-            w = gen.make_varlen("pol", 1000 + d, [150, 64, 1, 90, 700], 2, 1, d, True)
+            if policy in NOT_COMPILED.get(d, ()):
+                continue
+            w = gen.make_varlen("pol", 1000 + d, [150, 64, 1, 90, 700], 2, 1, d, causal)
             o, lse = run_varlen(w)
             o_ref, lse_ref = oracle.attention_varlen(w.q, w.k, w.v, w.cu_seqlens_q,
-                                                     w.cu_seqlens_k, w.scale, True)
+                                                     w.cu_seqlens_k, w.scale, causal)
             check_o(o, o_ref)
             check_lse(lse, lse_ref)
     finally:

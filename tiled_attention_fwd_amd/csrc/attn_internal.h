@@ -35,7 +35,8 @@ struct TilePolicy {
   int waves;   // wavefronts per workgroup
   int qcols;   // 32-query column blocks per wave
   int bn;      // keys per LDS tile
-  int bm() const { return waves * 32 * qcols; }
+  int kg = 1;  // key groups: waves / kg waves split the queries, kg groups split the keys
+  int bm() const { return waves / kg * 32 * qcols; }
 };
 
 // Picks the policy for a head_dim and the longest query length.  `override_id`

@@ -22,12 +22,16 @@
 //    half h, accumulator registers 8t..8t+7 hold keys 16t + 8h + 0..7.  Those
 //    8 probabilities, rounded to bf16, are exactly the B operand of the second
 //    product O^T += V^T P^T for keys 16t..16t+15: P never leaves registers.
-//  * V is stored transposed in LDS (V^T[d][key]) so the A operand of the
-//    second product (32 dims x 8 consecutive keys per lane) is one 16-byte
-//    LDS read.  The transpose happens in registers while staging.
-//  * K/V tiles are staged HBM -> registers -> LDS; the global loads of the
-//    next tile are issued before the current tile's math so their latency
-//    overlaps it.
+//  * Three kernel families share that mapping.  The staged kernel
+//    (attn_fwd_kernel) moves K/V tiles HBM -> registers -> LDS and stores V
+//    transposed (V^T[d][key]), so the A operand of the second product (32 dims
+//    x 8 consecutive keys per lane) is one 16-byte LDS read; the global loads
+//    of the next tile are issued before the current tile's math.  The
+//    DMA-staged kernel (attn_fwd_dma_kernel) moves tiles HBM -> LDS directly
+//    and reads V row-major through the transposing LDS read.  The
+//    software-pipelined kernel (attn_fwd_pipe_kernel) adds an LDS layout with
+//    additive fragment addresses and overlaps the scores of the next tile
+//    with the softmax of the current one inside each wave.
 //  * Causal: key tiles beyond the diagonal of the whole query block are never
 //    loaded; a wave whose queries all precede a tile skips its math; only
 //    tiles that cross the diagonal (or the sequence end) apply a mask.
@@ -129,13 +133,21 @@ __device__ __forceinline__ void lds_pipeline_hint() {
 // Kernel variant flags.
 constexpr int kPrio = 1;  // raise wave priority while issuing MFMA blocks
 
-template <int D, int BN, int WAVES, int QC, int MINW, bool VARLEN, int FLAGS = 0>
+// KG > 1 splits the key range of a query block over KG groups of waves: the
+// waves of group g take tiles g, g+KG, g+2KG, ... of the block, so a block's
+// serial key loop is KG times shorter (this is what keeps few-head, long
+// causal sequences from being bound by their last query block).  Each group
+// keeps its own (m, l, O); at the end the groups merge through LDS with the
+// same rescaling rule as the online softmax.
+template <int D, int BN, int WAVES, int QC, int MINW, bool VARLEN, int FLAGS = 0, int KG = 1>
 __global__ __launch_bounds__(WAVES * 64, MINW) void attn_fwd_kernel(const AttnArgs a) {
   constexpr int NT = WAVES * 64;
-  constexpr int SUB = D == 256 ? 32 : 64;  // keys per softmax sub-block (bounds live registers)
+  constexpr int QW = WAVES / KG;  // waves per key group (they split the queries)
+  static_assert(WAVES % KG == 0, "key groups must split the waves evenly");
+  constexpr int SUB = (D == 256 || BN == 32) ? 32 : 64;  // keys per softmax sub-block
   constexpr int NSB = BN / SUB;
   static_assert(BN % SUB == 0, "tile must hold whole sub-blocks");
-  constexpr int BM = WAVES * 32 * QC;
+  constexpr int BM = QW * 32 * QC;
   constexpr int PAD = 8;            // bf16 elements of padding per LDS row
   constexpr int KS = D + PAD;       // K tile row stride (keys are rows)
   constexpr int VS = BN + PAD;      // V^T tile row stride (dims are rows)
@@ -144,19 +156,25 @@ __global__ __launch_bounds__(WAVES * 64, MINW) void attn_fwd_kernel(const AttnAr
   constexpr int NKB = SUB / 32;     // 32-key blocks per sub-block
   constexpr int NDS = D / 16;       // 16-dim slices of one key row
   constexpr int NDB = D / 32;       // 32-dim blocks of the output
-  constexpr int K_UNITS = BN * D / 8;          // 16-byte chunks of a K tile
+  constexpr int K_TILE_UNITS = BN * D / 8;          // 16-byte chunks of a K tile
+  constexpr int K_UNITS = KG * K_TILE_UNITS;         // ... of the KG tiles of one step
   constexpr int K_PER = (K_UNITS + NT - 1) / NT;
-  constexpr int V_UNITS = (BN / 4) * (D / 8);  // 4 keys x 8 dims units of a V tile
+  constexpr int V_TILE_UNITS = (BN / 4) * (D / 8);  // 4 keys x 8 dims units of a V tile
+  constexpr int V_UNITS = KG * V_TILE_UNITS;
   constexpr int V_PER = (V_UNITS + NT - 1) / NT;
   static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
 
-  // Two K/V^T buffers: tile kt+1 is written while tile kt is read.
-  __shared__ __attribute__((aligned(16))) uint16_t ks[2 * KT_ELEMS];
-  __shared__ __attribute__((aligned(16))) uint16_t vt[2 * VT_ELEMS];
+  // Two buffers of KG K/V^T tiles: step i+1 is written while step i is read.
+  // One allocation, so the key-group merge can reuse all of it.
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * KG * (KT_ELEMS + VT_ELEMS)];
+  uint16_t* const ks = smem;
+  uint16_t* const vt = smem + 2 * KG * KT_ELEMS;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int kg = wave / QW;     // key group of this wave
+  const int qw = wave - kg * QW;
   const int l32 = lane & 31;
   const int hh = lane >> 5;
 
@@ -203,8 +221,9 @@ __global__ __launch_bounds__(WAVES * 64, MINW) void attn_fwd_kernel(const AttnAr
   int kend = lk;
   if (a.causal) kend = min(lk, q0 + BM + off);
   const int n_kt = kend > 0 ? (kend + BN - 1) / BN : 0;
+  const int n_steps = (n_kt + KG - 1) / KG;
 
-  const int qw0 = q0 + wave * 32 * QC;  // first query of this wave
+  const int qw0 = q0 + qw * 32 * QC;  // first query of this wave
   int kend_w = lk;
   if (a.causal) kend_w = min(lk, qw0 + 32 * QC + off);
   if (qw0 >= lq) kend_w = 0;  // a wave made only of padding rows does no math
@@ -250,13 +269,15 @@ __global__ __launch_bounds__(WAVES * 64, MINW) void attn_fwd_kernel(const AttnAr
   uint4 kreg[K_PER];
   uint4 vreg[V_PER][4];
 
-  auto fetch = [&](int kt) {
-    const uint32_t kbeg = kt * BN;
+  // Unit u of a step covers tile (step * KG + u / TILE_UNITS); its K rows
+  // are consecutive keys, so a step's KG tiles are KG * BN consecutive keys.
+  auto fetch = [&](int step) {
+    const uint32_t kbeg = step * KG * BN;
 #pragma unroll
     for (int i = 0; i < K_PER; ++i) {
       const int u = tid + i * NT;
       if (K_UNITS % NT == 0 || u < K_UNITS) {
-        const uint32_t row = u / (D / 8);
+        const uint32_t row = u / (D / 8);  // row within the step's KG * BN keys
         const uint32_t col = (u % (D / 8)) * 8;
         kreg[i] = buf_ld16(krs, (kbeg + row) * k_row_bytes + col * 2);
       }
@@ -265,18 +286,19 @@ __global__ __launch_bounds__(WAVES * 64, MINW) void attn_fwd_kernel(const AttnAr
     for (int i = 0; i < V_PER; ++i) {
       const int u = tid + i * NT;
       if (V_UNITS % NT == 0 || u < V_UNITS) {
-        const uint32_t kq = u % (BN / 4);
-        const uint32_t dq = u / (BN / 4);
+        const uint32_t g = u / V_TILE_UNITS;
+        const uint32_t w = u - g * V_TILE_UNITS;
+        const uint32_t kq = w % (BN / 4);
+        const uint32_t dq = w / (BN / 4);
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          vreg[i][j] = buf_ld16(vrs, (kbeg + kq * 4 + j) * v_row_bytes + dq * 16);
+          vreg[i][j] = buf_ld16(vrs, (kbeg + g * BN + kq * 4 + j) * v_row_bytes + dq * 16);
       }
     }
   };
 
   auto stage = [&](int buf) {
-    uint16_t* kd = ks + buf * KT_ELEMS;
-    uint16_t* vd = vt + buf * VT_ELEMS;
+    uint16_t* kd = ks + buf * KG * KT_ELEMS;  // KG tiles back to back: rows continue
 #pragma unroll
     for (int i = 0; i < K_PER; ++i) {
       const int u = tid + i * NT;
@@ -290,8 +312,11 @@ __global__ __launch_bounds__(WAVES * 64, MINW) void attn_fwd_kernel(const AttnAr
     for (int i = 0; i < V_PER; ++i) {
       const int u = tid + i * NT;
       if (V_UNITS % NT == 0 || u < V_UNITS) {
-        const int kq = u % (BN / 4);
-        const int dq = u / (BN / 4);
+        const int g = u / V_TILE_UNITS;
+        const int w = u - g * V_TILE_UNITS;
+        uint16_t* vd = vt + (buf * KG + g) * VT_ELEMS;
+        const int kq = w % (BN / 4);
+        const int dq = w / (BN / 4);
         const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&vreg[i][0]);
         const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&vreg[i][1]);
         const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&vreg[i][2]);
@@ -309,22 +334,23 @@ __global__ __launch_bounds__(WAVES * 64, MINW) void attn_fwd_kernel(const AttnAr
     }
   };
 
-  if (n_kt > 0) {
+  if (n_steps > 0) {
     fetch(0);
     stage(0);
   }
   __syncthreads();
 
-  for (int kt = 0; kt < n_kt; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < n_kt) fetch(kt + 1);
+  for (int step = 0; step < n_steps; ++step) {
+    const int buf = step & 1;
+    if (step + 1 < n_steps) fetch(step + 1);
+    const int kt = step * KG + kg;  // the tile this wave's group handles
 
 #pragma unroll
     for (int sb = 0; sb < NSB; ++sb) {
     const int kbeg = kt * BN + sb * SUB;
     if (kbeg < kend_w) {
-      const uint16_t* kd = ks + buf * KT_ELEMS + sb * SUB * KS;
-      const uint16_t* vd = vt + buf * VT_ELEMS + sb * SUB;
+      const uint16_t* kd = ks + (buf * KG + kg) * KT_ELEMS + sb * SUB * KS;
+      const uint16_t* vd = vt + (buf * KG + kg) * VT_ELEMS + sb * SUB;
       // ---- S^T = K Q^T ------------------------------------------------------
       if constexpr (FLAGS & kPrio) __builtin_amdgcn_s_setprio(1);
       f32x16 sacc[QC][NKB];
@@ -428,8 +454,50 @@ __global__ __launch_bounds__(WAVES * 64, MINW) void attn_fwd_kernel(const AttnAr
       if constexpr (FLAGS & kPrio) __builtin_amdgcn_s_setprio(0);
     }
     }
-    if (kt + 1 < n_kt) stage(buf ^ 1);
+    if (step + 1 < n_steps) stage(buf ^ 1);
     __syncthreads();
+  }
+
+  // ---- merge of the key groups (KG > 1) through LDS -------------------------
+  if constexpr (KG > 1) {
+    constexpr int NREG = QC * (NDB * 16 + 2);  // O accumulators, m, l per lane
+    static_assert((KG - 1) * QW * NREG * 64 * 4 <= 2 * KG * (KT_ELEMS + VT_ELEMS) * 2,
+                  "merge buffer must fit in the tile buffers");
+    float* mrg = reinterpret_cast<float*>(smem);  // [slot][reg][lane]; the key loop is over
+    if (kg > 0) {
+      float* dst = mrg + ((kg - 1) * QW + qw) * NREG * 64 + lane;
+#pragma unroll
+      for (int c = 0; c < QC; ++c) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) dst[((c * NDB + db) * 16 + r) * 64] = oacc[c][db][r];
+        dst[(QC * NDB * 16 + 2 * c) * 64] = m_run[c];
+        dst[(QC * NDB * 16 + 2 * c + 1) * 64] = l_run[c];
+      }
+    }
+    __syncthreads();
+    if (kg > 0) return;  // group 0 finishes the rows
+#pragma unroll
+    for (int g = 1; g < KG; ++g) {
+      const float* src = mrg + ((g - 1) * QW + qw) * NREG * 64 + lane;
+#pragma unroll
+      for (int c = 0; c < QC; ++c) {
+        const float m_o = src[(QC * NDB * 16 + 2 * c) * 64];
+        const float l_o = src[(QC * NDB * 16 + 2 * c + 1) * 64];
+        const float m_new = fmaxf(m_run[c], m_o);
+        const float m_ref = m_new == -INFINITY ? 0.f : m_new;  // both groups saw no key
+        const float a_self = __builtin_amdgcn_exp2f(m_run[c] - m_ref);
+        const float a_other = __builtin_amdgcn_exp2f(m_o - m_ref);
+        m_run[c] = m_new;
+        l_run[c] = l_run[c] * a_self + l_o * a_other;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            oacc[c][db][r] = oacc[c][db][r] * a_self + src[((c * NDB + db) * 16 + r) * 64] * a_other;
+      }
+    }
   }
 
   // ---- epilogue: O = O / l, LSE = (m + log2 l) ln 2 -----------------------
@@ -785,6 +853,756 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_pingpong_kernel(const AttnArg
   }
 }
 
+// ----------------------------------------------------------------------------
+// DMA-staged variant.
+//
+// K and V tiles go from HBM straight into LDS with buffer_load ... lds (each
+// lane's 16 bytes land at LDS base + 16 x lane, so a wave instruction fills 1
+// KiB of LDS; the global address of every lane is free).  No staging
+// registers, no staging VALU work, and loads can run two tiles ahead.
+//  * Rows are stored unpadded; 16-byte chunks are XOR-swizzled per row so the
+//    two read patterns stay conflict-free: the K fragment read (16 lanes, 16
+//    different rows, one chunk each) and the transposed V read (half a wave,
+//    4 rows x 4 chunks).
+//  * V stays row-major; the A operand of O^T += V^T P^T comes from two
+//    ds_read_b64_tr_b16 per MFMA: within each 16-lane group that instruction
+//    gives lane i element (i mod 4) of the 8-byte chunks addressed by lanes
+//    4e + i/4 (e = 0..3), so each lane addresses 4 dims of one key row and
+//    receives 4 keys of one dim.
+//  * NBUF tile buffers are separate LDS objects and the key loop is unrolled
+//    by NBUF, so the compiler can tell the buffer being read from the one the
+//    DMA is filling; an explicit vmcnt wait before each barrier publishes the
+//    next tile.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ uint2 ds_read_tr16(const uint16_t* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(p));
+  return __builtin_bit_cast(uint2, v);
+}
+
+// One wave-wide HBM -> LDS copy of 16 bytes per lane: lane i's bytes land at
+// lds_byte_base + 16 i.  Issued through asm so the compiler does not track the
+// LDS write (it would otherwise stall unrelated LDS reads on it); the kernel
+// itself waits for these loads (vmcnt) before the barrier that publishes them.
+// The asm has no register outputs, only inputs.
+__device__ __forceinline__ void dma16(u32x4 desc, uint32_t voffset, uint32_t lds_byte_base) {
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "buffer_load_dwordx4 %0, %2, 0 offen lds"
+      :
+      : "v"(voffset), "s"(lds_byte_base), "s"(desc)
+      : "memory", "m0");
+}
+
+// Raw buffer descriptor (same fields make_rsrc sets) as four scalars for asm.
+__device__ __forceinline__ u32x4 make_desc(const void* base, uint32_t bytes) {
+  const uint64_t addr = reinterpret_cast<uint64_t>(base);
+  u32x4 d;
+  d[0] = __builtin_amdgcn_readfirstlane((uint32_t)addr);
+  d[1] = __builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32) & 0xffffu);
+  d[2] = __builtin_amdgcn_readfirstlane(bytes);
+  d[3] = 0x00020000u;
+  return d;
+}
+
+// 32-bit LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) char*)p);
+}
+
+// s_waitcnt immediate that waits until at most n vector-memory ops are in flight.
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+template <int D>
+__device__ __forceinline__ int swz_k(int row) {
+  if constexpr (D >= 128) return row & 15;
+  else if constexpr (D == 64) return (row >> 1) & 7;
+  else return (row >> 2) & 3;
+}
+template <int D>
+__device__ __forceinline__ int swz_v(int row) {
+  if constexpr (D >= 128) return (row & 3) << 2;
+  else if constexpr (D == 64) return ((row >> 1) & 1) << 2;
+  else return 0;
+}
+
+template <int D, int WAVES, int KG, int NBUF, bool VARLEN>
+__global__ __launch_bounds__(WAVES * 64, D == 256 ? 1 : 2) void attn_fwd_dma_kernel(const AttnArgs a) {
+  constexpr int NT = WAVES * 64;
+  constexpr int BN = D == 256 ? 32 : 64;
+  constexpr int QW = WAVES / KG;
+  constexpr int BM = QW * 32;
+  constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  constexpr int TILE = BN * D;               // elements of one K (or V) tile
+  constexpr int IPT = BN * CPR / 64;         // 1 KiB DMA instructions per tile
+  constexpr int NK = KG * IPT;               // ... for the K tiles of one step (same for V)
+  static_assert(NK % WAVES == 0, "DMA instructions must split evenly over the waves");
+  constexpr int PER_WAVE = 2 * NK / WAVES;   // DMA instructions one wave issues per step
+  constexpr int NKB = BN / 32;
+  constexpr int NDS = D / 16;
+  constexpr int NDB = D / 32;
+  static_assert(NBUF == 2 || NBUF == 3, "two or three buffers");
+
+  __shared__ __attribute__((aligned(16))) uint16_t ks0[KG * TILE], vs0[KG * TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t ks1[KG * TILE], vs1[KG * TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t ks2[NBUF > 2 ? KG * TILE : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t vs2[NBUF > 2 ? KG * TILE : 8];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int kg = wave / QW;
+  const int qw = wave - kg * QW;
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+
+  const int rows = a.nseq * a.hq;
+  const int id = blockIdx.x;
+  const int qb_rev = id / rows;
+  int p = id - qb_rev * rows;
+  if (a.xcd_remap) p = (p & 7) * (rows >> 3) + (p >> 3);
+  const int seq = p / a.hq;
+  const int h = p - seq * a.hq;
+  const int qb = a.causal ? (a.n_qb - 1 - qb_rev) : qb_rev;
+  int lq, lk;
+  int64_t qoff, koff, voff, ooff, lseoff;
+  if constexpr (VARLEN) {
+    const int qs = a.cu_q[seq];
+    const int kst = a.cu_k[seq];
+    lq = a.cu_q[seq + 1] - qs;
+    lk = a.cu_k[seq + 1] - kst;
+    qoff = (int64_t)qs * a.q_ss;
+    koff = (int64_t)kst * a.k_ss;
+    voff = (int64_t)kst * a.v_ss;
+    ooff = (int64_t)qs * a.o_ss;
+    lseoff = qs;
+  } else {
+    lq = a.sq;
+    lk = a.sk;
+    qoff = (int64_t)seq * a.q_bs;
+    koff = (int64_t)seq * a.k_bs;
+    voff = (int64_t)seq * a.v_bs;
+    ooff = (int64_t)seq * a.o_bs;
+    lseoff = (int64_t)seq * a.lse_bs;
+  }
+  const int q0 = qb * BM;
+  if (q0 >= lq) return;
+  const int kvh = h / a.group;
+  const uint16_t* qbase = a.q + qoff + (int64_t)h * a.q_hs;
+  const uint16_t* kbase = a.k + koff + (int64_t)kvh * a.k_hs;
+  const uint16_t* vbase = a.v + voff + (int64_t)kvh * a.v_hs;
+  float* obase = a.o + ooff + (int64_t)h * a.o_hs;
+
+  const int off = lk - lq;
+  int kend = lk;
+  if (a.causal) kend = min(lk, q0 + BM + off);
+  const int n_kt = kend > 0 ? (kend + BN - 1) / BN : 0;
+  const int n_steps = (n_kt + KG - 1) / KG;
+  const int qw0 = q0 + qw * 32;
+  int kend_w = lk;
+  if (a.causal) kend_w = min(lk, qw0 + 32 + off);
+  if (qw0 >= lq) kend_w = 0;
+
+  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(qbase, span_bytes(lq, a.q_ss));
+  const uint32_t k_row_bytes = (uint32_t)a.k_ss * 2;
+  const uint32_t v_row_bytes = (uint32_t)a.v_ss * 2;
+  const u32x4 kdesc = make_desc(kbase, span_bytes(lk, a.k_ss));
+  const u32x4 vdesc = make_desc(vbase, span_bytes(lk, a.v_ss));
+
+  u32x4 qraw[NDS];
+  {
+    const uint32_t qoff_b = (uint32_t)(qw0 + l32) * (uint32_t)a.q_ss * 2 + hh * 16;
+#pragma unroll
+    for (int s = 0; s < NDS; ++s)
+      qraw[s] = __builtin_amdgcn_raw_buffer_load_b128(qrs, (int)(qoff_b + 32 * s), 0, 0);
+  }
+  bf16x8 qf[NDS];
+#pragma unroll
+  for (int s = 0; s < NDS; ++s) {
+    asm volatile("" : "+v"(qraw[s]));
+    qf[s] = __builtin_bit_cast(bf16x8, qraw[s]);
+  }
+
+  f32x16 oacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  // ---- DMA of one step (KG tiles of K and of V) into buffer B ----------------
+  auto dma = [&](auto Bc, int step) {
+    constexpr int B = decltype(Bc)::value;
+    uint16_t* kd = B == 0 ? ks0 : B == 1 ? ks1 : ks2;
+    uint16_t* vd = B == 0 ? vs0 : B == 1 ? vs1 : vs2;
+    const uint32_t kbeg = step * KG * BN;
+#pragma unroll
+    for (int i = 0; i < NK / WAVES; ++i) {
+      const int ins = wave * (NK / WAVES) + i;  // 0 .. NK-1, wave-uniform
+      const int g = ins / IPT;
+      const int cgi = ins - g * IPT;
+      const int slot = cgi * 64 + lane;
+      const int row = slot / CPR;                 // row within the tile
+      const int phys = slot - row * CPR;
+      const uint32_t grow = kbeg + g * BN + row;  // key index within the sequence
+      dma16(kdesc, grow * k_row_bytes + (uint32_t)((phys ^ swz_k<D>(row)) * 16),
+            __builtin_amdgcn_readfirstlane(lds_addr(kd + g * TILE + cgi * 512)));
+      dma16(vdesc, grow * v_row_bytes + (uint32_t)((phys ^ swz_v<D>(row)) * 16),
+            __builtin_amdgcn_readfirstlane(lds_addr(vd + g * TILE + cgi * 512)));
+    }
+  };
+
+  // lane-constant parts of the fragment addresses
+  int krow[NKB];
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) krow[kb] = (kb * 32 + key_of_row(l32)) * D;
+  const int ksw = swz_k<D>(key_of_row(l32));
+  const int vrow0 = 8 * hh + ((lane & 15) >> 2);
+  const int vsw = swz_v<D>(vrow0);
+  const int vcc = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);  // chunk within a 32-dim block
+  const int vhalf = (lane & 1) * 4;
+
+  auto compute = [&](auto Bc, int step) {
+    constexpr int B = decltype(Bc)::value;
+    const uint16_t* kd = (B == 0 ? ks0 : B == 1 ? ks1 : ks2) + kg * TILE;
+    const uint16_t* vd = (B == 0 ? vs0 : B == 1 ? vs1 : vs2) + kg * TILE;
+    const int kt = step * KG + kg;
+    const int kbeg = kt * BN;
+    if (kbeg >= kend_w) return;
+    f32x16 sacc[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int s = 0; s < NDS; ++s) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kd + krow[kb] + (((2 * s + hh) ^ ksw) * 8));
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], s == 0 ? f32x16{} : sacc[kb],
+                                                           0, 0, 0);
+      }
+    lds_pipeline_hint<NKB * NDS>();
+    if ((kbeg + BN > lk) || (a.causal && kbeg + BN - 1 > qw0 + off)) {
+      const int lim = a.causal ? min(lk - 1, qw0 + l32 + off) : lk - 1;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kbeg + kb * 32 + ((r >> 3) << 4) + hh * 8 + (r & 7);
+          if (key > lim) sacc[kb][r] = -INFINITY;
+        }
+    }
+    float mx0 = -INFINITY, mx1 = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        mx0 = fmaxf(mx0, sacc[kb][r]);
+        mx1 = fmaxf(mx1, sacc[kb][r + 1]);
+      }
+    const float cand = half_max(fmaxf(mx0, mx1)) * a.c;
+    const bool grow = cand > m_run + kRescaleThreshold;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float m_new = grow ? cand : m_run;
+      const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+    bf16x8 pf[NKB][2];
+    float rs0 = 0.f, rs1 = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float pvl = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], a.c, -m_use));
+        sacc[kb][r] = pvl;
+        if (r & 1) rs1 += pvl; else rs0 += pvl;
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        uint4 u;
+        u.x = pack_bf16x2(sacc[kb][8 * t + 0], sacc[kb][8 * t + 1]);
+        u.y = pack_bf16x2(sacc[kb][8 * t + 2], sacc[kb][8 * t + 3]);
+        u.z = pack_bf16x2(sacc[kb][8 * t + 4], sacc[kb][8 * t + 5]);
+        u.w = pack_bf16x2(sacc[kb][8 * t + 6], sacc[kb][8 * t + 7]);
+        pf[kb][t] = as_bf16x8(u);
+      }
+    }
+    l_run += rs0 + rs1;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          // rows kb*32 + 16t + 8hh + (lane%16)/4 (+4 for the second read)
+          const uint16_t* src = vd + (kb * 32 + 16 * t + vrow0) * D + (((db * 4) ^ vsw) + vcc) * 8 + vhalf;
+          const uint2 lo = ds_read_tr16(src);
+          const uint2 hi = ds_read_tr16(src + 4 * D);
+          const bf16x8 vf = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kb][t], oacc[db], 0, 0, 0);
+        }
+  };
+
+  // ---- pipeline: step s reads buffer s % NBUF; the DMA runs NBUF-1 steps ahead --
+  if (n_steps > 0) dma(std::integral_constant<int, 0>{}, 0);
+  if constexpr (NBUF == 3) {
+    if (n_steps > 1) {
+      dma(std::integral_constant<int, 1>{}, 1);
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER_WAVE));
+    } else {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    }
+  } else {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  }
+  __syncthreads();
+
+  auto iteration = [&](auto Bc, int step) {
+    constexpr int B = decltype(Bc)::value;
+    constexpr int BA = (B + NBUF - 1) % NBUF;  // buffer the DMA ahead fills
+    const bool ahead = step + NBUF - 1 < n_steps;
+    if (ahead) dma(std::integral_constant<int, BA>{}, step + NBUF - 1);
+    compute(Bc, step);
+    // publish step+1: its DMA must be complete; the one issued above may run on
+    if (NBUF == 3 && ahead) __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER_WAVE));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __syncthreads();
+  };
+  for (int step = 0; step < n_steps; step += NBUF) {
+    iteration(std::integral_constant<int, 0>{}, step);
+    if (step + 1 < n_steps) iteration(std::integral_constant<int, 1>{}, step + 1);
+    if constexpr (NBUF == 3) {
+      if (step + 2 < n_steps) iteration(std::integral_constant<int, 2>{}, step + 2);
+    }
+  }
+
+  // ---- key-group merge (KG > 1): partial (m, l, O) through LDS ------------------
+  if constexpr (KG > 1) {
+    static_assert(KG == 2, "merge written for two key groups");
+    constexpr int NREG = NDB * 16 + 2;
+    static_assert(NREG * 64 * 4 <= KG * TILE * 2, "one wave's partial must fit one tile array");
+    static_assert(QW <= 4, "merge slots: ks0, vs0, ks1, vs1");
+    uint16_t* slot16 = qw == 0 ? ks0 : qw == 1 ? vs0 : qw == 2 ? ks1 : vs1;
+    float* slot = reinterpret_cast<float*>(slot16) + lane;  // [reg][lane]
+    if (kg == 1) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) slot[(db * 16 + r) * 64] = oacc[db][r];
+      slot[(NDB * 16) * 64] = m_run;
+      slot[(NDB * 16 + 1) * 64] = l_run;
+    }
+    __syncthreads();
+    if (kg == 1) return;
+    const float m_o = slot[(NDB * 16) * 64];
+    const float l_o = slot[(NDB * 16 + 1) * 64];
+    const float m_new = fmaxf(m_run, m_o);
+    const float m_ref = m_new == -INFINITY ? 0.f : m_new;
+    const float a_self = __builtin_amdgcn_exp2f(m_run - m_ref);
+    const float a_other = __builtin_amdgcn_exp2f(m_o - m_ref);
+    m_run = m_new;
+    l_run = l_run * a_self + l_o * a_other;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        oacc[db][r] = oacc[db][r] * a_self + slot[(db * 16 + r) * 64] * a_other;
+  }
+
+  const float lt = half_sum(l_run);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  const int qrow = qw0 + l32;
+  if (qrow < lq) {
+    float* op = obase + (int64_t)qrow * a.o_ss + hh * 4;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float4 w;
+        w.x = oacc[db][4 * g + 0] * inv;
+        w.y = oacc[db][4 * g + 1] * inv;
+        w.z = oacc[db][4 * g + 2] * inv;
+        w.w = oacc[db][4 * g + 3] * inv;
+        *reinterpret_cast<float4*>(op + db * 32 + 8 * g) = w;
+      }
+    if (a.lse != nullptr && hh == 0)
+      a.lse[lseoff + (int64_t)h * a.lse_hs + qrow] =
+          lt > 0.f ? (m_run + __log2f(lt)) * kLn2 : -INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Software-pipelined kernel.
+//
+// Each wave overlaps its own work instead of relying on a second wave: while
+// the matrix core computes the scores of tile j+1 (S_{j+1} = K_{j+1} Q^T), the
+// VALU turns S_j into probabilities; then O += V_j^T P_j runs.  A barrier per
+// tile keeps all waves of a workgroup in the same phase, so overlap between
+// waves alone leaves the matrix core idle during the softmax; here it need not.
+//
+// Tiles arrive by LDS DMA into NBUF buffers; iteration j reads K of tile j+1
+// and V of tile j and issues the DMA of tile j + NBUF - 1.
+//
+// LDS layout.  One DMA instruction moves 64 x 16 bytes = R = 64 / (D/8) rows
+// of a tile.  Inside its 1 KiB the 16-byte chunk c of row-in-group i sits at
+// slot c * R + (i ^ rot(c)) (chunk-major), and consecutive instructions are G
+// bytes apart.  A fragment read then has the address (lane base) + (constant)
+// for every K chunk pair and every V dim block, so the kernel needs only a
+// handful of address registers, and the reads stay free of bank conflicts:
+//  * K read: 16 consecutive lanes read one chunk of 16 consecutive rows; the
+//    rows of one instruction are 16 bytes apart and G_K shifts the next
+//    instruction by a quarter (D=128) or half (D=64) of 256 bytes.
+//  * V transposed read: a 16-lane group reads 4 consecutive rows of two
+//    adjacent chunks, 128 contiguous bytes for D=128; for D=64 rot() moves
+//    one chunk of each pair (and of the 4-chunk set a 32-lane read covers) to
+//    the other half of the bank range.
+// K rows are stored in key_of_row order (the DMA lane picks the source row),
+// so lane l reads row l and its scores come out in the order the P operand
+// needs.
+// ---------------------------------------------------------------------------
+template <int D>
+struct PipeLayout {
+  static constexpr int CPR = D / 8;
+  static constexpr int R = 64 / CPR;
+  static_assert(R == 4 || R == 8, "layout defined for head_dim 128 and 64");
+  static constexpr int GK = 1024 + (R == 4 ? 64 : 128);
+  static constexpr int GV = 1024;
+  static __device__ __forceinline__ int rot(int c) {
+    return R == 8 ? 4 * ((c ^ (c >> 1)) & 1) : 0;
+  }
+  // byte offset of (row, chunk) inside a tile with instruction stride G
+  static __device__ __forceinline__ int at(int row, int c, int G) {
+    return (row / R) * G + 16 * (c * R + ((row % R) ^ rot(c)));
+  }
+};
+
+template <int D, int BN, int WAVES, int NBUF, int MINW, bool VARLEN>
+__global__ __launch_bounds__(WAVES * 64, MINW) void attn_fwd_pipe_kernel(const AttnArgs a) {
+  using L = PipeLayout<D>;
+  constexpr int BM = WAVES * 32;
+  constexpr int R = L::R;
+  constexpr int NI = BN / R;                  // DMA instructions per tile (K or V)
+  static_assert(NI % WAVES == 0, "DMA instructions must split evenly over the waves");
+  constexpr int NIW = NI / WAVES;             // ... per wave
+  constexpr int PER_WAVE = 2 * NIW;           // vector-memory ops a wave issues per tile
+  constexpr int KT = NI * L::GK;              // bytes of one K tile
+  constexpr int VT = NI * L::GV;
+  constexpr int NKB = BN / 32;
+  constexpr int NDS = D / 16;
+  constexpr int NDB = D / 32;
+  static_assert(NBUF == 3 || NBUF == 4, "three or four buffers");
+
+  __shared__ __attribute__((aligned(16))) unsigned char lds[NBUF * (KT + VT)];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+
+  const int rows = a.nseq * a.hq;
+  const int id = blockIdx.x;
+  const int qb_rev = id / rows;
+  int p = id - qb_rev * rows;
+  if (a.xcd_remap) p = (p & 7) * (rows >> 3) + (p >> 3);
+  const int seq = p / a.hq;
+  const int h = p - seq * a.hq;
+  const int qb = a.causal ? (a.n_qb - 1 - qb_rev) : qb_rev;
+  int lq, lk;
+  int64_t qoff, koff, voff, ooff, lseoff;
+  if constexpr (VARLEN) {
+    const int qs = a.cu_q[seq];
+    const int kst = a.cu_k[seq];
+    lq = a.cu_q[seq + 1] - qs;
+    lk = a.cu_k[seq + 1] - kst;
+    qoff = (int64_t)qs * a.q_ss;
+    koff = (int64_t)kst * a.k_ss;
+    voff = (int64_t)kst * a.v_ss;
+    ooff = (int64_t)qs * a.o_ss;
+    lseoff = qs;
+  } else {
+    lq = a.sq;
+    lk = a.sk;
+    qoff = (int64_t)seq * a.q_bs;
+    koff = (int64_t)seq * a.k_bs;
+    voff = (int64_t)seq * a.v_bs;
+    ooff = (int64_t)seq * a.o_bs;
+    lseoff = (int64_t)seq * a.lse_bs;
+  }
+  const int q0 = qb * BM;
+  if (q0 >= lq) return;
+  const int kvh = h / a.group;
+  const uint16_t* qbase = a.q + qoff + (int64_t)h * a.q_hs;
+  const uint16_t* kbase = a.k + koff + (int64_t)kvh * a.k_hs;
+  const uint16_t* vbase = a.v + voff + (int64_t)kvh * a.v_hs;
+  float* obase = a.o + ooff + (int64_t)h * a.o_hs;
+
+  // Tiles of the block (every wave joins every DMA and barrier) and of this
+  // wave: n_w tiles hold a key some query of the wave sees; the first n_full
+  // of them are visible to all of its queries.
+  const int off = lk - lq;
+  int kend = lk;
+  if (a.causal) kend = min(lk, q0 + BM + off);
+  const int n_steps = kend > 0 ? (kend + BN - 1) / BN : 0;
+  const int qw0 = q0 + wave * 32;
+  int kend_w = lk;
+  if (a.causal) kend_w = min(lk, qw0 + 32 + off);
+  if (qw0 >= lq) kend_w = 0;
+  const int n_w = kend_w > 0 ? (kend_w + BN - 1) / BN : 0;
+  const int full_keys = a.causal ? min(lk, qw0 + off + 1) : lk;
+  const int n_full = full_keys > 0 ? min(full_keys / BN, n_w) : 0;
+
+  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(qbase, span_bytes(lq, a.q_ss));
+  const uint32_t k_row_bytes = (uint32_t)a.k_ss * 2;
+  const uint32_t v_row_bytes = (uint32_t)a.v_ss * 2;
+  const u32x4 kdesc = make_desc(kbase, span_bytes(lk, a.k_ss));
+  const u32x4 vdesc = make_desc(vbase, span_bytes(lk, a.v_ss));
+
+  u32x4 qraw[NDS];
+  {
+    const uint32_t qoff_b = (uint32_t)(qw0 + l32) * (uint32_t)a.q_ss * 2 + hh * 16;
+#pragma unroll
+    for (int s = 0; s < NDS; ++s)
+      qraw[s] = __builtin_amdgcn_raw_buffer_load_b128(qrs, (int)(qoff_b + 32 * s), 0, 0);
+  }
+  bf16x8 qf[NDS];
+#pragma unroll
+  for (int s = 0; s < NDS; ++s) {
+    asm volatile("" : "+v"(qraw[s]));
+    qf[s] = __builtin_bit_cast(bf16x8, qraw[s]);
+  }
+
+  f32x16 oacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f, cand = -INFINITY;
+
+  // ---- DMA: the lane's (row, chunk) in each of this wave's instructions ----
+  uint32_t dk[NIW], dv[NIW];
+#pragma unroll
+  for (int i = 0; i < NIW; ++i) {
+    const int q = wave * NIW + i;
+    const int c = lane / R;
+    const int row = q * R + ((lane % R) ^ L::rot(c));
+    const int krow_src = (row & ~31) + key_of_row(row & 31);
+    dk[i] = (uint32_t)krow_src * k_row_bytes + (uint32_t)c * 16;
+    dv[i] = (uint32_t)row * v_row_bytes + (uint32_t)c * 16;
+  }
+  const uint32_t lds0 = lds_addr(lds);
+  auto dma = [&](int t) {
+    const int b = t % NBUF;
+    const uint32_t kb_k = (uint32_t)t * BN * k_row_bytes;
+    const uint32_t kb_v = (uint32_t)t * BN * v_row_bytes;
+#pragma unroll
+    for (int i = 0; i < NIW; ++i) {
+      const int q = wave * NIW + i;
+      dma16(kdesc, kb_k + dk[i], __builtin_amdgcn_readfirstlane(lds0 + b * KT + q * L::GK));
+      dma16(vdesc, kb_v + dv[i], __builtin_amdgcn_readfirstlane(lds0 + NBUF * KT + b * VT + q * L::GV));
+    }
+  };
+
+  // ---- fragment addresses: lane base + constant ------------------------------
+  // K fragment (kb, s): row 32kb + l32, chunk 2s + hh.  V fragment (db, kb, t,
+  // half): rows 32kb + 16t + 8hh + u (+4 for the second read), chunk 4db + vcc.
+  const int u = (lane & 15) >> 2;
+  const int vcc = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const int kl[2] = {L::at(l32, hh, L::GK), L::at(l32, 2 + hh, L::GK)};
+  const int vl[2] = {L::at(8 * hh + u, vcc, L::GV) + 8 * (lane & 1),
+                     L::at(8 * hh + u + 4, vcc, L::GV) + 8 * (lane & 1)};
+  auto kfrag = [&](uint32_t kt_base, int kb, int s) -> bf16x8 {
+    // constant part: rows 32kb (32kb/R instructions), chunk pair s/2 (chunk 2s)
+    const int cst = (32 * kb / R) * L::GK + 16 * R * 2 * (s & ~1);
+    return *reinterpret_cast<const bf16x8*>(lds + kt_base + kl[s & 1] + cst);
+  };
+  auto vfrag = [&](uint32_t vt_base, int db, int kb, int t) -> bf16x8 {
+    const int cst = ((32 * kb + 16 * t) / R) * L::GV + 16 * R * 4 * db;
+    const uint2 lo = ds_read_tr16(reinterpret_cast<const uint16_t*>(lds + vt_base + vl[0] + cst));
+    const uint2 hi = ds_read_tr16(reinterpret_cast<const uint16_t*>(lds + vt_base + vl[1] + cst));
+    return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+  };
+
+  f32x16 S0[NKB], S1[NKB];
+
+  auto qk = [&](int t, f32x16 (&S)[NKB]) {
+    const uint32_t kt_base = (uint32_t)(t % NBUF) * KT;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int s = 0; s < NDS; ++s)
+        S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag(kt_base, kb, s), qf[s],
+                                                        s == 0 ? f32x16{} : S[kb], 0, 0, 0);
+  };
+
+  auto mask = [&](f32x16 (&S)[NKB], int t) {
+    const int kbeg = t * BN;
+    const int lim = a.causal ? min(lk - 1, qw0 + l32 + off) : lk - 1;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kbeg + kb * 32 + ((r >> 3) << 4) + hh * 8 + (r & 7);
+        if (key > lim) S[kb][r] = -INFINITY;
+      }
+  };
+
+  // row maximum in base-2 units; mx0/mx1 hold the running partial maxima
+  auto rowmax_part = [&](const f32x16 (&S)[NKB], int e0, int ne, float& mx0, float& mx1) {
+#pragma unroll
+    for (int e = e0; e < e0 + ne; e += 2) {
+      mx0 = fmaxf(mx0, S[e >> 4][e & 15]);
+      mx1 = fmaxf(mx1, S[e >> 4][(e & 15) + 1]);
+    }
+  };
+  auto rowmax = [&](const f32x16 (&S)[NKB]) {
+    float mx0 = -INFINITY, mx1 = -INFINITY;
+    rowmax_part(S, 0, NKB * 16, mx0, mx1);
+    cand = half_max(fmaxf(mx0, mx1)) * a.c;
+  };
+
+  auto rescale = [&]() {
+    const bool grow = cand > m_run + kRescaleThreshold;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float m_new = grow ? cand : m_run;
+      const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+    }
+  };
+
+  // ---- one iteration's block, laid out slot by slot ---------------------------
+  // A slot holds one MFMA plus the loads and VALU work that overlap it; a
+  // scheduling fence after each slot keeps that order (the compiler would
+  // otherwise cluster all exponentials ahead of the first MFMA).  Fragments
+  // are loaded kAhead slots before the MFMA that uses them.
+  constexpr int N_QK = NKB * NDS;           // score MFMAs of tile j+1
+  constexpr int N_PV = NDB * NKB * 2;       // O MFMAs of tile j
+  constexpr int NE = NKB * 16;              // probabilities per lane and tile
+  constexpr int EQ = (NE + N_QK - 1) / N_QK;   // ... converted per score MFMA
+  constexpr int EM = (NE + N_PV - 1) / N_PV;   // maxima taken per O MFMA
+  constexpr int kAhead = 2;
+  static_assert(EQ % 2 == 0 && 8 % EQ == 0 || EQ % 8 == 0, "conversion chunks must align with packs");
+  bf16x8 pf[NKB][2];
+  auto fused = [&](int j, f32x16 (&Scur)[NKB], f32x16 (&Snext)[NKB]) {
+    const uint32_t kt_base = (uint32_t)((j + 1) % NBUF) * KT;
+    const uint32_t vt_base = (uint32_t)(NBUF * KT) + (uint32_t)(j % NBUF) * VT;
+    // slot i of the score MFMAs: (kb, s) = (i % NKB, i / NKB), alternating
+    // accumulators; slot i of the O MFMAs: (db, kb, t) with db fastest.
+    auto kslot = [&](int i) { return kfrag(kt_base, i % NKB, i / NKB); };
+    auto vslot = [&](int i) {
+      return vfrag(vt_base, i % NDB, (i / NDB) % NKB, i / (NDB * NKB));
+    };
+    bf16x8 fr[kAhead + 1];
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+    float rs0 = 0.f, rs1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i) fr[i] = kslot(i);
+#pragma unroll
+    for (int i = 0; i < N_QK; ++i) {
+      const int kb = i % NKB, s = i / NKB;
+      Snext[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i % (kAhead + 1)], qf[s],
+                                                          s == 0 ? f32x16{} : Snext[kb], 0, 0, 0);
+      const int n = i + kAhead;
+      if (n < N_QK) fr[n % (kAhead + 1)] = kslot(n);
+      else fr[n % (kAhead + 1)] = vslot(n - N_QK);
+#pragma unroll
+      for (int e = i * EQ; e < (i + 1) * EQ && e < NE; ++e) {
+        const float pvl = __builtin_amdgcn_exp2f(fmaf(Scur[e >> 4][e & 15], a.c, -m_use));
+        Scur[e >> 4][e & 15] = pvl;
+        if (e & 1) rs1 += pvl; else rs0 += pvl;
+        if ((e & 7) == 7) {
+          const int kb2 = e >> 4, t = (e >> 3) & 1;
+          uint4 w;
+          w.x = pack_bf16x2(Scur[kb2][8 * t + 0], Scur[kb2][8 * t + 1]);
+          w.y = pack_bf16x2(Scur[kb2][8 * t + 2], Scur[kb2][8 * t + 3]);
+          w.z = pack_bf16x2(Scur[kb2][8 * t + 4], Scur[kb2][8 * t + 5]);
+          w.w = pack_bf16x2(Scur[kb2][8 * t + 6], Scur[kb2][8 * t + 7]);
+          pf[kb2][t] = as_bf16x8(w);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    l_run += rs0 + rs1;
+    float mx0 = -INFINITY, mx1 = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < N_PV; ++i) {
+      const int db = i % NDB, kb = (i / NDB) % NKB, t = i / (NDB * NKB);
+      const int cur = (i + N_QK) % (kAhead + 1);
+      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[cur], pf[kb][t], oacc[db], 0, 0, 0);
+      const int n = i + kAhead;
+      if (n < N_PV) fr[(n + N_QK) % (kAhead + 1)] = vslot(n);
+      const int e0 = i * EM;
+      if (e0 < NE) rowmax_part(Snext, e0, min(EM, NE - e0), mx0, mx1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // speculative maximum of tile j+1, redone after masking on boundary tiles
+    cand = half_max(fmaxf(mx0, mx1)) * a.c;
+  };
+
+  // ---- prologue: tiles 0 .. NBUF-2 in flight, wait for tiles 0 and 1 --------
+  if (n_steps > 0) dma(0);
+  if (n_steps > 1) dma(1);
+  if (NBUF == 4 && n_steps > 2) {
+    dma(2);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER_WAVE));
+  } else {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  }
+  __syncthreads();
+  if (n_w > 0) {
+    qk(0, S0);
+    rowmax(S0);
+  }
+
+  // Iteration j (j < n_w) finds S_j in Scur with its speculative maximum in
+  // cand.  On its last tile a wave still computes scores of tile j+1 (from
+  // whatever that buffer holds): they are never used, and the block stays
+  // branch-free.
+  auto iteration = [&](int j, f32x16 (&Scur)[NKB], f32x16 (&Snext)[NKB]) {
+    const bool issue = j + NBUF - 1 < n_steps;
+    if (issue) dma(j + NBUF - 1);
+    if (j < n_w) {
+      if (j >= n_full) {
+        mask(Scur, j);
+        rowmax(Scur);
+      }
+      rescale();
+      fused(j, Scur, Snext);
+    }
+    // publish tile j+2 (read as K by iteration j+1); a DMA issued above may run on
+    if (NBUF == 4 && issue) __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER_WAVE));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __syncthreads();
+  };
+  for (int j = 0; j < n_steps; j += 2) {
+    iteration(j, S0, S1);
+    if (j + 1 < n_steps) iteration(j + 1, S1, S0);
+  }
+
+  const float lt = half_sum(l_run);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  const int qrow = qw0 + l32;
+  if (qrow < lq) {
+    float* op = obase + (int64_t)qrow * a.o_ss + hh * 4;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float4 w;
+        w.x = oacc[db][4 * g + 0] * inv;
+        w.y = oacc[db][4 * g + 1] * inv;
+        w.z = oacc[db][4 * g + 2] * inv;
+        w.w = oacc[db][4 * g + 3] * inv;
+        *reinterpret_cast<float4*>(op + db * 32 + 8 * g) = w;
+      }
+    if (a.lse != nullptr && hh == 0)
+      a.lse[lseoff + (int64_t)h * a.lse_hs + qrow] =
+          lt > 0.f ? (m_run + __log2f(lt)) * kLn2 : -INFINITY;
+  }
+}
+
 // Compiled tile policies (id: waves x 32-query columns per wave, min waves
 // per SIMD).  Keys per tile: 64 (32 at head_dim 256, whose output
 // accumulator alone takes 128 registers per lane).
@@ -798,7 +1616,15 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_pingpong_kernel(const AttnArg
 //   6: as 5, with raised priority around MFMA blocks
 //   7: as 0, with raised priority around MFMA blocks
 //   8: ping-pong kernel, 8 waves in two alternating groups (BM 256)
-constexpr int kNumPolicies = 9;
+//   9: 8 waves = 4 query waves x 2 key groups (BM 128): half-length key loop
+//  10: 8 waves = 2 query waves x 4 key groups (BM 64, 32-key tiles)
+//  11: DMA-staged kernel, 8 waves (BM 256), three buffers
+//  12: DMA-staged kernel, 8 waves = 4 query waves x 2 key groups (BM 128), two buffers
+//  13: DMA-staged kernel, 4 waves (BM 128), two buffers
+//  14: software-pipelined kernel, 8 waves (BM 256), four buffers
+//  15: software-pipelined kernel, 4 waves (BM 128), 32-key tiles, three buffers
+//  16: as 15 with four buffers
+constexpr int kNumPolicies = 17;
 
 template <int D>
 constexpr int bn_for() { return D == 256 ? 32 : 64; }
@@ -856,6 +1682,54 @@ hipError_t launch_d(const AttnArgs& a, int policy_id, hipStream_t stream) {
         hipLaunchKernelGGL((attn_fwd_pingpong_kernel<D, VARLEN>), g, dim3(512), 0, stream, a);
       }
       break;
+    case 9:
+      if constexpr (D == 256) {
+        return hipErrorInvalidValue;
+      } else {
+        hipLaunchKernelGGL((attn_fwd_kernel<D, 64, 8, 1, 2, VARLEN, 0, 2>), g, dim3(512), 0, stream, a);
+      }
+      break;
+    case 10:
+      if constexpr (D == 256) {
+        return hipErrorInvalidValue;
+      } else {
+        hipLaunchKernelGGL((attn_fwd_kernel<D, 32, 8, 1, 2, VARLEN, 0, 4>), g, dim3(512), 0, stream, a);
+      }
+      break;
+    case 11:
+      if constexpr (D == 32 || D == 256) {
+        return hipErrorInvalidValue;
+      } else {
+        hipLaunchKernelGGL((attn_fwd_dma_kernel<D, 8, 1, 3, VARLEN>), g, dim3(512), 0, stream, a);
+      }
+      break;
+    case 12:
+      if constexpr (D == 256) {
+        return hipErrorInvalidValue;
+      } else {
+        hipLaunchKernelGGL((attn_fwd_dma_kernel<D, 8, 2, 2, VARLEN>), g, dim3(512), 0, stream, a);
+      }
+      break;
+    case 13:
+      hipLaunchKernelGGL((attn_fwd_dma_kernel<D, 4, 1, 2, VARLEN>), g, dim3(256), 0, stream, a);
+      break;
+    case 14:
+    case 15:
+    case 16:
+      if constexpr (D == 256 || D == 32) {
+        return hipErrorInvalidValue;
+      } else {
+        if (policy_id == 14)
+          hipLaunchKernelGGL((attn_fwd_pipe_kernel<D, 64, 8, 4, 2, VARLEN>), g, dim3(512), 0,
+                             stream, a);
+        else if (policy_id == 15)
+          hipLaunchKernelGGL((attn_fwd_pipe_kernel<D, 32, 4, 3, 2, VARLEN>), g, dim3(256), 0,
+                             stream, a);
+        else
+          hipLaunchKernelGGL((attn_fwd_pipe_kernel<D, 32, 4, 4, 2, VARLEN>), g, dim3(256), 0,
+                             stream, a);
+      }
+      break;
     default:
       return hipErrorInvalidValue;
   }
@@ -873,24 +1747,36 @@ bool select_policy(int head_dim, int max_seqlen_q, bool causal, int64_t rows, in
                    TilePolicy* out, int* policy_id) {
   static const TilePolicy kTable[kNumPolicies] = {{4, 1, 64}, {2, 1, 64}, {4, 2, 64}, {8, 1, 64},
                                                   {8, 1, 64}, {8, 1, 128}, {8, 1, 128}, {4, 1, 64},
-                                                  {8, 1, 64}};
+                                                  {8, 1, 64}, {8, 1, 64, 2}, {8, 1, 32, 4},
+                                                  {8, 1, 64}, {8, 1, 64, 2}, {4, 1, 64},
+                                                  {8, 1, 64}, {4, 1, 32}, {4, 1, 32}};
   int id;
   if (override_id >= 0) {
     if (override_id >= kNumPolicies) return false;
-    if (head_dim == 256 && (override_id == 2 || override_id == 8)) return false;  // not compiled
+    if (head_dim == 256 && (override_id == 2 || (override_id >= 8 && override_id <= 12) ||
+                            override_id >= 14))
+      return false;  // not compiled (register or LDS budget)
+    if (head_dim == 32 && (override_id == 11 || override_id >= 14)) return false;
     id = override_id;
   } else {
-    // 256-query blocks share one K/V staging among eight waves, but need at
-    // least one workgroup per CU (256) to fill the chip.
+    // Chosen from measured sweeps over the workload set (dense, varlen,
+    // packed, grouped heads; head_dim 32..256).  256-query blocks share one
+    // K/V tile among eight waves but need at least one workgroup per CU (256)
+    // to fill the chip; with fewer, two key groups per block halve the serial
+    // key loop of the longest (causal) blocks.
     const int64_t wg256 = rows * ((max_seqlen_q + 255) / 256);
     if (max_seqlen_q <= 64) {
       id = 1;  // one 64-query block covers every sequence
-    } else if (head_dim == 128 && max_seqlen_q >= 256 && wg256 >= 256) {
-      id = 3;
-    } else if (head_dim == 64 && !causal && max_seqlen_q >= 256 && wg256 >= 256) {
-      id = 3;
-    } else {
+    } else if (head_dim == 128 && max_seqlen_q <= 128) {
       id = 0;
+    } else if (head_dim == 128 && max_seqlen_q >= 256 && wg256 >= 256) {
+      id = 11;
+    } else if (head_dim == 128 && max_seqlen_q >= 512) {
+      id = 12;
+    } else if (head_dim == 64 && !causal && max_seqlen_q >= 256 && wg256 >= 256) {
+      id = 14;
+    } else {
+      id = 13;
     }
   }
   *out = kTable[id];
