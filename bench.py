@@ -111,13 +111,16 @@ class PaddedPath:
         self.total_len = w.q.shape[1]
         self.out = torch.empty((1, self.total_len, h, d), dtype=torch.float32, device="cuda")
         self.n_valid = n
+        # workspace for split key ranges (None when the shape is not split)
+        self.ws = t.workspace(len(w.lengths_q), w.max_seqlen, h, d, True)
 
     def gather(self):
         self.t.attn_unpad_gather([self.q, self.k, self.v], self.idx, outs=[self.qc, self.kc, self.vc])
 
     def attention(self):
         self.t.attn_fwd_varlen(self.qc, self.kc, self.vc, self.cu, self.cu, self.w.max_seqlen,
-                               scale=float(self.w.scale), causal=True, out=self.o, lse=self.lse)
+                               scale=float(self.w.scale), causal=True, out=self.o, lse=self.lse,
+                               workspace=self.ws)
 
     def scatter(self):
         self.t.attn_pad_scatter(self.o, self.idx, self.total_len, out=self.out)
@@ -183,14 +186,17 @@ def run_configs(torch, t, names, flush):
         elif w.kind == "dense":
             o = torch.empty(w.q.shape, dtype=torch.float32, device="cuda")
             lse = torch.empty((w.q.shape[0], w.hq, w.q.shape[1]), dtype=torch.float32, device="cuda")
-            fn = lambda: t.attn_fwd_dense(q, k, v, scale=float(w.scale), causal=w.causal, out=o, lse=lse)
+            ws = t.workspace(w.q.shape[0], w.q.shape[1], w.hq, w.d, w.causal)
+            fn = lambda: t.attn_fwd_dense(q, k, v, scale=float(w.scale), causal=w.causal, out=o,
+                                          lse=lse, workspace=ws)
         else:
             cq = torch.from_numpy(w.cu_seqlens_q).to("cuda")
             ck = torch.from_numpy(w.cu_seqlens_k).to("cuda")
             o = torch.empty(w.q.shape, dtype=torch.float32, device="cuda")
             lse = torch.empty((w.hq, w.q.shape[0]), dtype=torch.float32, device="cuda")
+            ws = t.workspace(len(w.lengths_q), w.max_seqlen, w.hq, w.d, w.causal)
             fn = lambda: t.attn_fwd_varlen(q, k, v, cq, ck, w.max_seqlen, scale=float(w.scale),
-                                           causal=w.causal, out=o, lse=lse)
+                                           causal=w.causal, out=o, lse=lse, workspace=ws)
         fl, by = attn_flops(w), attn_bytes(w)
         if w.kind == "padded":
             by = by + pp.bytes_gather() + pp.bytes_scatter()

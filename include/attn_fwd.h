@@ -20,7 +20,8 @@
  *
  * Conventions shared by every entry point:
  *  - Every tensor pointer is a DEVICE pointer owned by the caller.  The library
- *    allocates nothing, frees nothing and never synchronises the stream.
+ *    allocates nothing, frees nothing and never synchronises the stream; the
+ *    only scratch memory it uses is a workspace the caller passes (_ws calls).
  *  - bfloat16 tensors are passed as raw 16-bit storage (const void*).
  *  - `stream` is a hipStream_t cast to void*; NULL means the default stream.
  *    Work is enqueued asynchronously on it.
@@ -111,6 +112,58 @@ attn_status_t attn_fwd_dense(const void* q, const void* k, const void* v,
                              int32_t num_heads_q, int32_t num_heads_k, int32_t head_dim,
                              const int64_t* strides, float scale, int32_t causal,
                              float* out, float* lse, void* stream);
+
+/*
+ * attn_fwd_varlen_ws, attn_fwd_dense_ws -- the two calls above with a caller-
+ * owned workspace that lets the library split long key ranges.
+ *
+ * Passage: the same as attn_fwd_varlen / attn_fwd_dense.  The split relies on
+ * the rule of page "Intro to FlashAttention on Ascend CANN", section "the first
+ * pitfall": softmax partials over disjoint key ranges combine exactly once each
+ * carries its running maximum and sum.  Here a part stores O_r normalised by
+ * its own sum and L_r = log2 of that sum in base-2 exponent units, and a merge
+ * launch forms O = sum_r 2^(L_r - L) O_r, L = log2 sum_r 2^(L_r).
+ *
+ * When a launch has few query blocks and their key loops are long (a causal
+ * sequence with few heads), the longest block bounds the run time while most
+ * CUs idle.  With a workspace the key loop of such blocks is cut into parts of
+ * about the per-CU share of all key tiles, each run by its own workgroup.
+ *
+ * workspace: device memory of at least workspace_bytes bytes, 16-byte aligned,
+ *      owned by the caller; contents need no initialisation and are scratch
+ *      after the call.  NULL, or fewer bytes than attn_fwd_workspace_bytes
+ *      reports for the shape, runs the call without splitting (same results up
+ *      to rounding order).  Two calls that share one workspace must not overlap
+ *      in time (same stream, or synchronised).
+ * workspace_bytes: size of workspace; negative returns ATTN_ERR_SHAPE.
+ * All other arguments, results and errors are those of the call without _ws.
+ * Results differ from the unsplit call only in floating-point rounding order.
+ */
+attn_status_t attn_fwd_varlen_ws(const void* q, const void* k, const void* v,
+                                 const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                 int32_t num_seqs, int32_t total_q, int32_t total_k,
+                                 int32_t num_heads_q, int32_t num_heads_k, int32_t head_dim,
+                                 int32_t max_seqlen, float scale, int32_t causal,
+                                 float* out, float* lse, void* workspace,
+                                 int64_t workspace_bytes, void* stream);
+
+attn_status_t attn_fwd_dense_ws(const void* q, const void* k, const void* v,
+                                int32_t batch, int32_t seqlen_q, int32_t seqlen_k,
+                                int32_t num_heads_q, int32_t num_heads_k, int32_t head_dim,
+                                const int64_t* strides, float scale, int32_t causal,
+                                float* out, float* lse, void* workspace,
+                                int64_t workspace_bytes, void* stream);
+
+/*
+ * attn_fwd_workspace_bytes -- workspace size that enables splitting for a shape.
+ *
+ * num_seqs (batch for dense), max_seqlen (seqlen_q for dense), num_heads_q,
+ * head_dim and causal as in the calls above.  Returns the byte count the _ws
+ * calls need to split key ranges for this shape, or 0 when the library would
+ * not split it (or the arguments are invalid).  Pure host computation.
+ */
+int64_t attn_fwd_workspace_bytes(int32_t num_seqs, int32_t max_seqlen, int32_t num_heads_q,
+                                 int32_t head_dim, int32_t causal);
 
 /*
  * attn_unpad_gather -- copy the rows named by `indices` into a compact tensor.

@@ -130,3 +130,37 @@ def test_tile_override_rejects_uncompiled_policy(lib, monkeypatch):
         assert varlen(lib, d=32) == UNSUP
     monkeypatch.setenv("ATTN_FWD_TILE", "99")
     assert varlen(lib, d=128) == UNSUP
+
+
+def test_workspace_plan_splits_only_low_parallelism_launches(lib, monkeypatch):
+    monkeypatch.delenv("ATTN_FWD_TILE", raising=False)
+    monkeypatch.delenv("ATTN_FWD_SPLIT_TILES", raising=False)
+    ws = lib.attn_fwd_workspace_bytes
+    # enough query blocks to occupy every CU: no split, no workspace
+    assert ws(1, 2048, 16, 128, 1) == 0
+    assert ws(1, 4096, 32, 128, 1) == 0
+    assert ws(1, 8192, 64, 128, 1) == 0
+    # few heads, long causal sequence: the key loop is split
+    assert ws(1, 8192, 2, 128, 1) > 0
+    assert ws(1, 16384, 1, 128, 1) > 0
+    # invalid arguments report 0
+    assert ws(0, 2048, 16, 128, 1) == 0
+    assert ws(1, 2048, 16, 96, 1) == 0
+    # forcing parts of 4 tiles sizes a workspace for any DMA-staged launch:
+    # rows x blocks x parts x block x (head_dim + 1) floats
+    monkeypatch.setenv("ATTN_FWD_TILE", "12")
+    monkeypatch.setenv("ATTN_FWD_SPLIT_TILES", "4")
+    parts = -(-(2048 // 64) // 4)
+    assert ws(1, 2048, 16, 128, 1) == 16 * (2048 // 128) * parts * 128 * 129 * 4
+
+
+def test_workspace_argument_checks(lib):
+    P = ctypes.c_void_p(16)
+    cu = ctypes.c_void_p(16)
+    # negative size and misaligned workspace are rejected before any launch
+    assert lib.attn_fwd_varlen_ws(P, P, P, cu, cu, 1, 8, 8, 2, 2, 64, 8, 0.125, 1, P, None,
+                                  P, -1, None) == SHAPE
+    assert lib.attn_fwd_varlen_ws(P, P, P, cu, cu, 1, 8, 8, 2, 2, 64, 8, 0.125, 1, P, None,
+                                  ctypes.c_void_p(24), 64, None) == ALIGN
+    assert lib.attn_fwd_dense_ws(P, P, P, 1, 8, 8, 2, 2, 64, None, 0.125, 1, P, None,
+                                 P, -5, None) == SHAPE

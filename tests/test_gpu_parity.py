@@ -260,15 +260,104 @@ def test_scatter_search_sizes(n_valid, n_rows):
     assert np.array_equal(host(out), oracle.pad_scatter(host(src), idx, n_rows))
 
 
+# ----------------------------------------------------------------------------- split key ranges
+SPLIT_POLICIES = ["11", "12", "13"]
+
+
+def _forced_split(policy, tiles):
+    os.environ["ATTN_FWD_TILE"] = policy
+    os.environ["ATTN_FWD_SPLIT_TILES"] = str(tiles)
+
+
+def _clear_forced():
+    os.environ.pop("ATTN_FWD_TILE", None)
+    os.environ.pop("ATTN_FWD_SPLIT_TILES", None)
+
+
+@pytest.mark.parametrize("policy", SPLIT_POLICIES)
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_split_key_ranges_varlen(policy, causal, d):
+    """Key loops cut into parts of 1-3 tiles (several parts per block, uneven
+    last parts, empty sequences, GQA) and merged, against the oracle."""
+    if policy in NOT_COMPILED.get(d, ()):
+        pytest.skip("policy not compiled for this head_dim")
+    t = api()
+    w = gen.make_varlen("split", 1500 + d, [150, 64, 1, 0, 90, 700, 333], 4, 2, d, causal)
+    for tiles in (1, 3):
+        _forced_split(policy, tiles)
+        try:
+            ws = t.workspace(len(w.lengths_q), w.max_seqlen, 4, d, causal)
+            assert ws is not None
+            o, lse = t.attn_fwd_varlen(dev_bf16(w.q), dev_bf16(w.k), dev_bf16(w.v),
+                                       dev_i32(w.cu_seqlens_q), dev_i32(w.cu_seqlens_k),
+                                       w.max_seqlen, scale=float(w.scale), causal=causal,
+                                       workspace=ws)
+        finally:
+            _clear_forced()
+        o_ref, lse_ref = oracle.attention_varlen(w.q, w.k, w.v, w.cu_seqlens_q, w.cu_seqlens_k,
+                                                 w.scale, causal)
+        print(policy, d, causal, tiles, check_o(host(o), o_ref), check_lse(host(lse), lse_ref))
+
+
+@pytest.mark.parametrize("policy", SPLIT_POLICIES)
+def test_split_key_ranges_dense_lq_ne_lk(policy):
+    """Dense, bottom-right causal with Lk > Lq and Lk < Lq, strided output."""
+    t = api()
+    for sq, sk in ((300, 520), (520, 300)):
+        w = gen.make_dense(f"sd{sq}", 1600 + sq, 2, sq, sk, 4, 1, 128, True)
+        _forced_split(policy, 2)
+        try:
+            ws = t.workspace(2, sq, 4, 128, True)
+            o, lse = t.attn_fwd_dense(dev_bf16(w.q), dev_bf16(w.k), dev_bf16(w.v),
+                                      scale=float(w.scale), causal=True, workspace=ws)
+        finally:
+            _clear_forced()
+        o_ref, lse_ref = oracle.attention_dense(w.q, w.k, w.v, w.scale, True)
+        print(policy, sq, sk, check_o(host(o), o_ref), check_lse(host(lse), lse_ref))
+
+
+def test_split_workspace_too_small_runs_unsplit():
+    import torch
+    t = api()
+    w = gen.make_varlen("small", 1700, [700, 300], 2, 2, 128, True)
+    _forced_split("12", 2)
+    try:
+        n = t.attn_fwd_workspace_bytes(2, w.max_seqlen, 2, 128, True)
+        assert n > 0
+        small = torch.empty(n - 16, dtype=torch.uint8, device="cuda")
+        o, lse = t.attn_fwd_varlen(dev_bf16(w.q), dev_bf16(w.k), dev_bf16(w.v),
+                                   dev_i32(w.cu_seqlens_q), dev_i32(w.cu_seqlens_k),
+                                   w.max_seqlen, scale=float(w.scale), causal=True,
+                                   workspace=small)
+    finally:
+        _clear_forced()
+    o_ref, lse_ref = oracle.attention_varlen(w.q, w.k, w.v, w.cu_seqlens_q, w.cu_seqlens_k,
+                                             w.scale, True)
+    check_o(host(o), o_ref)
+    check_lse(host(lse), lse_ref)
+
+
 # ----------------------------------------------------------------------------- the padded path end to end
-@pytest.mark.parametrize("name", ["padded_32x128_random", "padded_32x128_exact", "padded_1x2048"])
-def test_padded_path_full_size(name):
+@pytest.mark.parametrize("name,use_ws", [("padded_32x128_random", False),
+                                         ("padded_32x128_exact", False),
+                                         ("padded_1x2048", False), ("padded_1x2048", True)])
+def test_padded_path_full_size(name, use_ws):
     t = api()
     w = gen.build_workload(name)
     idx = dev_i32(w.indices)
     qc, kc, vc = t.attn_unpad_gather([dev_bf16(w.q), dev_bf16(w.k), dev_bf16(w.v)], idx)
-    o, lse = t.attn_fwd_varlen(qc, kc, vc, dev_i32(w.cu_seqlens_q), dev_i32(w.cu_seqlens_k),
-                               w.max_seqlen, scale=float(w.scale), causal=True)
+    ws = None
+    if use_ws:  # split path at full size: parts of at most 8 key tiles
+        os.environ["ATTN_FWD_SPLIT_TILES"] = "8"
+    try:
+        if use_ws:
+            ws = t.workspace(len(w.lengths_q), w.max_seqlen, w.hq, w.d, True)
+            assert ws is not None
+        o, lse = t.attn_fwd_varlen(qc, kc, vc, dev_i32(w.cu_seqlens_q), dev_i32(w.cu_seqlens_k),
+                                   w.max_seqlen, scale=float(w.scale), causal=True, workspace=ws)
+    finally:
+        os.environ.pop("ATTN_FWD_SPLIT_TILES", None)
     padded = t.attn_pad_scatter(o, idx, w.q.shape[1], out_shape=(1,) + w.q.shape[1:])
     # the oracle: gather, attention, scatter
     hd = w.q.shape[2:]

@@ -16,7 +16,7 @@ from typing import List, Optional, Sequence, Tuple
 from . import _lib
 
 __all__ = ["attn_fwd_varlen", "attn_fwd_dense", "attn_unpad_gather", "attn_pad_scatter",
-           "abi_version", "AttnError"]
+           "attn_fwd_workspace_bytes", "workspace", "abi_version", "AttnError"]
 
 AttnError = _lib.AttnError
 
@@ -50,11 +50,39 @@ def abi_version() -> int:
     return int(_lib.load().attn_abi_version())
 
 
+def attn_fwd_workspace_bytes(num_seqs: int, max_seqlen: int, num_heads_q: int, head_dim: int,
+                             causal: bool) -> int:
+    """Bytes of workspace that let a launch of this shape split long key ranges (0: none)."""
+    return int(_lib.load().attn_fwd_workspace_bytes(int(num_seqs), int(max_seqlen),
+                                                     int(num_heads_q), int(head_dim),
+                                                     int(bool(causal))))
+
+
+def workspace(num_seqs: int, max_seqlen: int, num_heads_q: int, head_dim: int, causal: bool,
+              device="cuda"):
+    """A device buffer of attn_fwd_workspace_bytes for the shape, or None when none is needed."""
+    n = attn_fwd_workspace_bytes(num_seqs, max_seqlen, num_heads_q, head_dim, causal)
+    if n <= 0:
+        return None
+    return _torch().empty(n, dtype=_torch().uint8, device=device)
+
+
+def _ws_args(ws):
+    if ws is None:
+        return None, 0
+    if not ws.is_cuda or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    return _ptr(ws), int(ws.numel() * ws.element_size())
+
+
 def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen: int,
                     scale: Optional[float] = None, causal: bool = False,
-                    out=None, lse=None, return_lse: bool = True, stream=None):
+                    out=None, lse=None, return_lse: bool = True, stream=None,
+                    workspace=None):
     """Packed variable-length attention.  q (Tq, Hq, D), k/v (Tk, Hkv, D) bf16.
 
+    ``workspace`` (optional, see ``workspace()``) lets the library split the
+    key loop of long query blocks over several workgroups.
     Returns (out (Tq, Hq, D) fp32, lse (Hq, Tq) fp32 or None).
     """
     torch = _torch()
@@ -78,16 +106,20 @@ def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen: int,
         out = torch.empty((tq, hq, d), dtype=torch.float32, device=q.device)
     if lse is None and return_lse:
         lse = torch.empty((hq, tq), dtype=torch.float32, device=q.device)
-    st = lib.attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
-                             cu_seqlens_q.numel() - 1, tq, tk, hq, hkv, d, int(max_seqlen),
-                             float(scale), int(bool(causal)), _ptr(out), _ptr(lse),
-                             _stream_ptr(q.device, stream))
-    _lib.check("attn_fwd_varlen", st)
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+            cu_seqlens_q.numel() - 1, tq, tk, hq, hkv, d, int(max_seqlen),
+            float(scale), int(bool(causal)), _ptr(out), _ptr(lse))
+    if workspace is None:
+        st = lib.attn_fwd_varlen(*args, _stream_ptr(q.device, stream))
+        _lib.check("attn_fwd_varlen", st)
+    else:
+        st = lib.attn_fwd_varlen_ws(*args, *_ws_args(workspace), _stream_ptr(q.device, stream))
+        _lib.check("attn_fwd_varlen_ws", st)
     return out, lse
 
 
 def attn_fwd_dense(q, k, v, scale: Optional[float] = None, causal: bool = False,
-                   out=None, lse=None, return_lse: bool = True, stream=None):
+                   out=None, lse=None, return_lse: bool = True, stream=None, workspace=None):
     """Dense batched attention.  q (B, Sq, Hq, D), k/v (B, Sk, Hkv, D) bf16.
 
     Non-contiguous q/k/v/out are accepted when the head_dim stride is 1 (their
@@ -113,11 +145,15 @@ def attn_fwd_dense(q, k, v, scale: Optional[float] = None, causal: bool = False,
         lse = torch.empty((b, hq, sq), dtype=torch.float32, device=q.device)
     strides = (ctypes.c_int64 * 12)(*(list(q.stride()[:3]) + list(k.stride()[:3]) +
                                       list(v.stride()[:3]) + list(out.stride()[:3])))
-    st = lib.attn_fwd_dense(_ptr(q), _ptr(k), _ptr(v), b, sq, sk, hq, hkv, d,
-                            ctypes.cast(strides, ctypes.c_void_p), float(scale),
-                            int(bool(causal)), _ptr(out), _ptr(lse),
-                            _stream_ptr(q.device, stream))
-    _lib.check("attn_fwd_dense", st)
+    args = (_ptr(q), _ptr(k), _ptr(v), b, sq, sk, hq, hkv, d,
+            ctypes.cast(strides, ctypes.c_void_p), float(scale), int(bool(causal)),
+            _ptr(out), _ptr(lse))
+    if workspace is None:
+        st = lib.attn_fwd_dense(*args, _stream_ptr(q.device, stream))
+        _lib.check("attn_fwd_dense", st)
+    else:
+        st = lib.attn_fwd_dense_ws(*args, *_ws_args(workspace), _stream_ptr(q.device, stream))
+        _lib.check("attn_fwd_dense_ws", st)
     return out, lse
 
 

@@ -25,6 +25,14 @@ SIGNATURES = {
     "attn_fwd_dense": (c_int32, [c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32,
                                  c_int32, c_int32, c_int32, c_void_p, c_float, c_int32,
                                  c_void_p, c_void_p, c_void_p]),
+    "attn_fwd_varlen_ws": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                     c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,
+                                     c_int32, c_float, c_int32, c_void_p, c_void_p, c_void_p,
+                                     c_int64, c_void_p]),
+    "attn_fwd_dense_ws": (c_int32, [c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32,
+                                    c_int32, c_int32, c_int32, c_void_p, c_float, c_int32,
+                                    c_void_p, c_void_p, c_void_p, c_int64, c_void_p]),
+    "attn_fwd_workspace_bytes": (c_int64, [c_int32, c_int32, c_int32, c_int32, c_int32]),
     "attn_unpad_gather": (c_int32, [c_void_p, c_void_p, c_int32, c_void_p, c_int32, c_int32,
                                     c_int64, c_void_p]),
     "attn_pad_scatter": (c_int32, [c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int64,

@@ -8,6 +8,8 @@
 #include <math.h>
 #include <stdlib.h>
 
+#include <algorithm>
+
 using attnfwd::AttnArgs;
 using attnfwd::TilePolicy;
 
@@ -28,6 +30,68 @@ int tile_override() {
   return (int)v;
 }
 
+// ATTN_FWD_SPLIT_TILES=<n> forces the key-range split of the DMA-staged
+// policies to parts of at most n tiles (used by parity tests of the split path).
+int split_override() {
+  const char* s = getenv("ATTN_FWD_SPLIT_TILES");
+  if (s == nullptr || *s == '\0') return -1;
+  char* end = nullptr;
+  long v = strtol(s, &end, 10);
+  if (end == s || v < 1 || v > 1000000) return -1;
+  return (int)v;
+}
+
+// Key-range split of long query blocks (DMA-staged policies 11-13 only).  A
+// causal launch with few blocks is bound by its longest block: the last query
+// block walks the whole key range while most CUs sit idle.  The plan cuts a
+// block's key loop into parts of about the per-CU share of all tiles, so no
+// workgroup runs much longer than that share; a merge launch combines parts.
+struct SplitPlan {
+  int n_split = 1;
+  int split_tiles = 0;
+  int bn = 64;
+  int bm = 0;
+};
+
+SplitPlan plan_split(const TilePolicy& pol, int pid, int64_t rows, int n_qb, int max_q,
+                     bool causal) {
+  SplitPlan sp;
+  sp.bm = pol.bm();
+  sp.bn = pol.bn;
+  if (pid < 11 || pid > 13) return sp;
+  const int64_t bm = pol.bm(), bn = pol.bn;
+  const int64_t max_tiles = (max_q + bn - 1) / bn;
+  int64_t total = 0;  // key tiles summed over the blocks of one (sequence, head)
+  for (int64_t qb = 0; qb < n_qb; ++qb) {
+    const int64_t keys = causal ? std::min<int64_t>(max_q, (qb + 1) * bm) : max_q;
+    total += (keys + bn - 1) / bn;
+  }
+  total *= rows;
+  const int64_t slots = (pid == 13) ? 512 : 256;  // resident workgroups on 256 CUs
+  int64_t st = split_override();
+  if (st < 1) {
+    // Measured: splitting pays only while the blocks alone leave CUs idle
+    // (1x8192 causal d=128 with 2 heads: 112 -> 83 us; 1x16384 with 1 head:
+    // 213 -> 137 us); with at least one block per slot the extra workgroups,
+    // partial stores and merge cost more than the shorter critical path saves
+    // (1x2048 with 16 heads: 41 -> 50 us).
+    if (rows * n_qb >= slots) return sp;
+    const int64_t share = (total + slots - 1) / slots;
+    if (max_tiles * 4 <= share * 5) return sp;  // longest block within 25% of the share
+    st = std::max<int64_t>(share, 2 * pol.kg);
+  }
+  const int64_t parts = (max_tiles + st - 1) / st;
+  if (parts <= 1) return sp;
+  sp.n_split = (int)std::min<int64_t>(parts, 8);
+  sp.split_tiles = (int)st;
+  return sp;
+}
+
+int64_t split_workspace_bytes(const SplitPlan& sp, int64_t rows, int n_qb, int head_dim) {
+  if (sp.n_split <= 1) return 0;
+  return rows * n_qb * sp.n_split * sp.bm * (int64_t)(head_dim + 1) * 4;
+}
+
 // scale * log2(e), the factor that turns scores into base-2 exponents.
 float base2_factor(float scale) { return (float)((double)scale * 1.4426950408889634074); }
 
@@ -44,31 +108,52 @@ bool span_fits(int64_t rows, int64_t row_stride_elems) {
   return rows * row_stride_elems * 2 < (1LL << 32);
 }
 
-attn_status_t launch(AttnArgs& a, int d, bool varlen, int max_q, hipStream_t stream) {
+attn_status_t launch(AttnArgs& a, int d, bool varlen, int max_q, void* ws, int64_t ws_bytes,
+                     hipStream_t stream) {
   TilePolicy pol;
   int pid;
   const int64_t rows = (int64_t)a.nseq * a.hq;
   if (!attnfwd::select_policy(d, max_q, a.causal != 0, rows, tile_override(), &pol, &pid))
     return ATTN_ERR_UNSUPPORTED;
   a.n_qb = (max_q + pol.bm() - 1) / pol.bm();
-  if (rows * a.n_qb > 0x7fffffffLL) return ATTN_ERR_SHAPE;
   a.xcd_remap = (rows % 8 == 0) ? 1 : 0;
+  a.n_split = 1;
+  const SplitPlan sp = plan_split(pol, pid, rows, a.n_qb, max_q, a.causal != 0);
+  const int64_t need = split_workspace_bytes(sp, rows, a.n_qb, d);
+  if (need > 0 && ws != nullptr && ws_bytes >= need) {
+    a.n_split = sp.n_split;
+    a.split_tiles = sp.split_tiles;
+    a.split_bn = sp.bn;
+    a.part_o = static_cast<float*>(ws);
+    a.part_lse = a.part_o + rows * a.n_qb * sp.n_split * sp.bm * d;
+  }
+  if (rows * a.n_qb * a.n_split > 0x7fffffffLL) return ATTN_ERR_SHAPE;
   hipError_t e = attnfwd::launch_attention(a, d, varlen, pid, stream);
+  if (e == hipSuccess && a.n_split > 1) e = attnfwd::launch_merge(a, d, varlen, sp.bm, stream);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+attn_status_t check_workspace(const void* ws, int64_t ws_bytes) {
+  if (ws_bytes < 0) return ATTN_ERR_SHAPE;
+  if (ws != nullptr && !aligned16(ws)) return ATTN_ERR_ALIGN;
+  return ATTN_OK;
 }
 
 }  // namespace
 
 extern "C" {
 
-attn_status_t attn_fwd_varlen(const void* q, const void* k, const void* v,
-                              const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
-                              int32_t num_seqs, int32_t total_q, int32_t total_k,
-                              int32_t num_heads_q, int32_t num_heads_k, int32_t head_dim,
-                              int32_t max_seqlen, float scale, int32_t causal, float* out,
-                              float* lse, void* stream) {
+attn_status_t attn_fwd_varlen_ws(const void* q, const void* k, const void* v,
+                                 const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                 int32_t num_seqs, int32_t total_q, int32_t total_k,
+                                 int32_t num_heads_q, int32_t num_heads_k, int32_t head_dim,
+                                 int32_t max_seqlen, float scale, int32_t causal, float* out,
+                                 float* lse, void* workspace, int64_t workspace_bytes,
+                                 void* stream) {
   if (num_seqs < 0 || total_q < 0 || total_k < 0 || max_seqlen < 0) return ATTN_ERR_SHAPE;
   attn_status_t st = check_common(num_heads_q, num_heads_k, head_dim, scale);
+  if (st != ATTN_OK) return st;
+  st = check_workspace(workspace, workspace_bytes);
   if (st != ATTN_OK) return st;
   if (num_seqs == 0 || total_q == 0 || num_heads_q == 0) return ATTN_OK;
   if (max_seqlen == 0) return ATTN_ERR_SHAPE;  // some sequence has queries
@@ -105,15 +190,30 @@ attn_status_t attn_fwd_varlen(const void* q, const void* k, const void* v,
   a.causal = causal ? 1 : 0;
   if (!span_fits(total_q, a.q_ss) || !span_fits(total_k, a.k_ss)) return ATTN_ERR_SHAPE;
   const int max_q = max_seqlen < total_q ? max_seqlen : total_q;
-  return launch(a, head_dim, true, max_q, static_cast<hipStream_t>(stream));
+  return launch(a, head_dim, true, max_q, workspace, workspace_bytes,
+                static_cast<hipStream_t>(stream));
 }
 
-attn_status_t attn_fwd_dense(const void* q, const void* k, const void* v, int32_t batch,
-                             int32_t seqlen_q, int32_t seqlen_k, int32_t num_heads_q,
-                             int32_t num_heads_k, int32_t head_dim, const int64_t* strides,
-                             float scale, int32_t causal, float* out, float* lse, void* stream) {
+attn_status_t attn_fwd_varlen(const void* q, const void* k, const void* v,
+                              const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                              int32_t num_seqs, int32_t total_q, int32_t total_k,
+                              int32_t num_heads_q, int32_t num_heads_k, int32_t head_dim,
+                              int32_t max_seqlen, float scale, int32_t causal, float* out,
+                              float* lse, void* stream) {
+  return attn_fwd_varlen_ws(q, k, v, cu_seqlens_q, cu_seqlens_k, num_seqs, total_q, total_k,
+                            num_heads_q, num_heads_k, head_dim, max_seqlen, scale, causal, out,
+                            lse, nullptr, 0, stream);
+}
+
+attn_status_t attn_fwd_dense_ws(const void* q, const void* k, const void* v, int32_t batch,
+                                int32_t seqlen_q, int32_t seqlen_k, int32_t num_heads_q,
+                                int32_t num_heads_k, int32_t head_dim, const int64_t* strides,
+                                float scale, int32_t causal, float* out, float* lse,
+                                void* workspace, int64_t workspace_bytes, void* stream) {
   if (batch < 0 || seqlen_q < 0 || seqlen_k < 0) return ATTN_ERR_SHAPE;
   attn_status_t st = check_common(num_heads_q, num_heads_k, head_dim, scale);
+  if (st != ATTN_OK) return st;
+  st = check_workspace(workspace, workspace_bytes);
   if (st != ATTN_OK) return st;
   if (batch == 0 || seqlen_q == 0 || num_heads_q == 0) return ATTN_OK;
   if (q == nullptr || out == nullptr) return ATTN_ERR_NULL;
@@ -165,7 +265,29 @@ attn_status_t attn_fwd_dense(const void* q, const void* k, const void* v, int32_
   a.causal = causal ? 1 : 0;
   if (!span_fits(seqlen_q, a.q_ss) || !span_fits(seqlen_k, a.k_ss) || !span_fits(seqlen_k, a.v_ss))
     return ATTN_ERR_SHAPE;
-  return launch(a, head_dim, false, seqlen_q, static_cast<hipStream_t>(stream));
+  return launch(a, head_dim, false, seqlen_q, workspace, workspace_bytes,
+                static_cast<hipStream_t>(stream));
+}
+
+attn_status_t attn_fwd_dense(const void* q, const void* k, const void* v, int32_t batch,
+                             int32_t seqlen_q, int32_t seqlen_k, int32_t num_heads_q,
+                             int32_t num_heads_k, int32_t head_dim, const int64_t* strides,
+                             float scale, int32_t causal, float* out, float* lse, void* stream) {
+  return attn_fwd_dense_ws(q, k, v, batch, seqlen_q, seqlen_k, num_heads_q, num_heads_k, head_dim,
+                           strides, scale, causal, out, lse, nullptr, 0, stream);
+}
+
+int64_t attn_fwd_workspace_bytes(int32_t num_seqs, int32_t max_seqlen, int32_t num_heads_q,
+                                 int32_t head_dim, int32_t causal) {
+  if (num_seqs <= 0 || max_seqlen <= 0 || num_heads_q <= 0 || !head_dim_ok(head_dim)) return 0;
+  TilePolicy pol;
+  int pid;
+  const int64_t rows = (int64_t)num_seqs * num_heads_q;
+  if (!attnfwd::select_policy(head_dim, max_seqlen, causal != 0, rows, tile_override(), &pol, &pid))
+    return 0;
+  const int n_qb = (max_seqlen + pol.bm() - 1) / pol.bm();
+  const SplitPlan sp = plan_split(pol, pid, rows, n_qb, max_seqlen, causal != 0);
+  return split_workspace_bytes(sp, rows, n_qb, head_dim);
 }
 
 attn_status_t attn_unpad_gather(const void* const* src, void* const* dst, int32_t n_tensors,

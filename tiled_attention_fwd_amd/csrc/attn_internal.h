@@ -28,7 +28,24 @@ struct AttnArgs {
   float c;           // scale * log2(e): scores enter exp2 in base-2 units
   int32_t causal;
   int32_t xcd_remap; // 1: spread (sequence, head) rows so each XCD gets a contiguous slice
+  // Split key ranges (DMA-staged kernel only).  n_split == 1: off.  Otherwise
+  // a query block whose key loop has more than split_tiles tiles of split_bn
+  // keys is cut into up to n_split even parts; each part writes its
+  // normalised partial output and base-2 LSE to part_o / part_lse, and
+  // merge_split combines them.
+  int32_t n_split;
+  int32_t split_tiles;
+  int32_t split_bn;
+  float* part_o;    // [rows][n_qb][n_split][bm][head_dim]
+  float* part_lse;  // [rows][n_qb][n_split][bm]
 };
+
+// Number of parts a query block with n_kt key tiles is cut into.
+__host__ __device__ inline int split_parts(int n_kt, int n_split, int split_tiles) {
+  if (n_split <= 1 || n_kt <= split_tiles) return 1;
+  const int want = (n_kt + split_tiles - 1) / split_tiles;
+  return want < n_split ? want : n_split;
+}
 
 // Tile policies: the query block BM = waves * 32 * qcols, key block BN.
 struct TilePolicy {
@@ -48,6 +65,10 @@ bool select_policy(int head_dim, int max_seqlen_q, bool causal, int64_t rows, in
 // Enqueues one attention launch.  Returns hipSuccess or the launch error.
 hipError_t launch_attention(const AttnArgs& a, int head_dim, bool varlen, int policy_id,
                             hipStream_t stream);
+
+// Combines the partial outputs of split query blocks (after launch_attention
+// with n_split > 1).  bm is the query block of the policy used.
+hipError_t launch_merge(const AttnArgs& a, int head_dim, bool varlen, int bm, hipStream_t stream);
 
 // Row gather of up to three tensors sharing one index list.
 hipError_t launch_gather(const void* const* src, void* const* dst, int n_tensors,

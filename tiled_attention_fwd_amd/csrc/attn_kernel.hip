@@ -960,8 +960,11 @@ __global__ __launch_bounds__(WAVES * 64, D == 256 ? 1 : 2) void attn_fwd_dma_ker
 
   const int rows = a.nseq * a.hq;
   const int id = blockIdx.x;
-  const int qb_rev = id / rows;
-  int p = id - qb_rev * rows;
+  const int per_qb = rows * a.n_split;
+  const int qb_rev = id / per_qb;
+  const int rem = id - qb_rev * per_qb;
+  const int part = rem / rows;
+  int p = rem - part * rows;
   if (a.xcd_remap) p = (p & 7) * (rows >> 3) + (p >> 3);
   const int seq = p / a.hq;
   const int h = p - seq * a.hq;
@@ -998,7 +1001,14 @@ __global__ __launch_bounds__(WAVES * 64, D == 256 ? 1 : 2) void attn_fwd_dma_ker
   const int off = lk - lq;
   int kend = lk;
   if (a.causal) kend = min(lk, q0 + BM + off);
-  const int n_kt = kend > 0 ? (kend + BN - 1) / BN : 0;
+  const int n_kt_all = kend > 0 ? (kend + BN - 1) / BN : 0;
+  // key tiles [t_begin, t_end) of this part of the block
+  const int n_parts = split_parts(n_kt_all, a.n_split, a.split_tiles);
+  if (part >= n_parts) return;
+  const int per_part = (n_kt_all + n_parts - 1) / n_parts;
+  const int t_begin = part * per_part;
+  const int t_end = min(n_kt_all, t_begin + per_part);
+  const int n_kt = max(t_end - t_begin, 0);
   const int n_steps = (n_kt + KG - 1) / KG;
   const int qw0 = q0 + qw * 32;
   int kend_w = lk;
@@ -1035,7 +1045,7 @@ __global__ __launch_bounds__(WAVES * 64, D == 256 ? 1 : 2) void attn_fwd_dma_ker
     constexpr int B = decltype(Bc)::value;
     uint16_t* kd = B == 0 ? ks0 : B == 1 ? ks1 : ks2;
     uint16_t* vd = B == 0 ? vs0 : B == 1 ? vs1 : vs2;
-    const uint32_t kbeg = step * KG * BN;
+    const uint32_t kbeg = (t_begin + step * KG) * BN;
 #pragma unroll
     for (int i = 0; i < NK / WAVES; ++i) {
       const int ins = wave * (NK / WAVES) + i;  // 0 .. NK-1, wave-uniform
@@ -1066,9 +1076,9 @@ __global__ __launch_bounds__(WAVES * 64, D == 256 ? 1 : 2) void attn_fwd_dma_ker
     constexpr int B = decltype(Bc)::value;
     const uint16_t* kd = (B == 0 ? ks0 : B == 1 ? ks1 : ks2) + kg * TILE;
     const uint16_t* vd = (B == 0 ? vs0 : B == 1 ? vs1 : vs2) + kg * TILE;
-    const int kt = step * KG + kg;
+    const int kt = t_begin + step * KG + kg;
     const int kbeg = kt * BN;
-    if (kbeg >= kend_w) return;
+    if (kt >= t_end || kbeg >= kend_w) return;
     f32x16 sacc[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
@@ -1213,6 +1223,27 @@ __global__ __launch_bounds__(WAVES * 64, D == 256 ? 1 : 2) void attn_fwd_dma_ker
   const float lt = half_sum(l_run);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   const int qrow = qw0 + l32;
+  if (n_parts > 1) {
+    // partial result of this part: O / l and the base-2 LSE, merged later
+    if (qrow < lq) {
+      const int64_t slot = (((int64_t)(seq * a.hq + h) * a.n_qb + qb) * a.n_split + part) * BM +
+                           (qrow - q0);
+      float* op = a.part_o + slot * D + hh * 4;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          float4 w;
+          w.x = oacc[db][4 * g + 0] * inv;
+          w.y = oacc[db][4 * g + 1] * inv;
+          w.z = oacc[db][4 * g + 2] * inv;
+          w.w = oacc[db][4 * g + 3] * inv;
+          *reinterpret_cast<float4*>(op + db * 32 + 8 * g) = w;
+        }
+      if (hh == 0) a.part_lse[slot] = lt > 0.f ? m_run + __log2f(lt) : -INFINITY;
+    }
+    return;
+  }
   if (qrow < lq) {
     float* op = obase + (int64_t)qrow * a.o_ss + hh * 4;
 #pragma unroll
@@ -1229,6 +1260,85 @@ __global__ __launch_bounds__(WAVES * 64, D == 256 ? 1 : 2) void attn_fwd_dma_ker
     if (a.lse != nullptr && hh == 0)
       a.lse[lseoff + (int64_t)h * a.lse_hs + qrow] =
           lt > 0.f ? (m_run + __log2f(lt)) * kLn2 : -INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Merge of split query blocks.  Part r of a block holds O_r (normalised by its
+// own row sum) and L_r = log2 of that row sum in base-2 exponent units; the
+// whole block is O = sum_r 2^(L_r - L) O_r with L = log2 sum_r 2^(L_r), the
+// log-sum-exp rule that combines softmax partials over disjoint key ranges
+// ("Intro to FlashAttention on Ascend CANN", the running maximum and sum of
+// the online softmax applied to whole parts).
+// ---------------------------------------------------------------------------
+// One thread per 4 output values; a workgroup covers kMergeRows rows of a
+// block, so each thread waits on one round of loads only.
+constexpr int kMergeRows = 8;
+
+template <int D, bool VARLEN>
+__global__ __launch_bounds__(kMergeRows * D / 4) void merge_split_kernel(const AttnArgs a, int bm) {
+  const int rows = a.nseq * a.hq;
+  const int chunks = bm / kMergeRows;
+  const int blk = blockIdx.x / chunks;
+  const int chunk = blockIdx.x - blk * chunks;
+  const int qb = blk / rows;
+  const int pr = blk - qb * rows;
+  const int seq = pr / a.hq;
+  const int h = pr - seq * a.hq;
+  int lq, lk;
+  int64_t ooff, lseoff;
+  if constexpr (VARLEN) {
+    const int qs = a.cu_q[seq];
+    lq = a.cu_q[seq + 1] - qs;
+    lk = a.cu_k[seq + 1] - a.cu_k[seq];
+    ooff = (int64_t)qs * a.o_ss;
+    lseoff = qs;
+  } else {
+    lq = a.sq;
+    lk = a.sk;
+    ooff = (int64_t)seq * a.o_bs;
+    lseoff = (int64_t)seq * a.lse_bs;
+  }
+  const int q0 = qb * bm;
+  if (q0 >= lq) return;
+  const int off = lk - lq;
+  int kend = lk;
+  if (a.causal) kend = min(lk, q0 + bm + off);
+  const int n_kt = kend > 0 ? (kend + a.split_bn - 1) / a.split_bn : 0;
+  const int np = split_parts(n_kt, a.n_split, a.split_tiles);
+  if (np <= 1) return;  // the attention kernel wrote this block itself
+  const int64_t base = ((int64_t)pr * a.n_qb + qb) * a.n_split * bm;
+  constexpr int C4 = D / 4;
+  {
+    const int row = chunk * kMergeRows + (int)threadIdx.x / C4;
+    const int c = (int)threadIdx.x % C4;
+    if (q0 + row >= lq) return;
+    float mx = -INFINITY;
+    for (int r = 0; r < np; ++r) mx = fmaxf(mx, a.part_lse[base + (int64_t)r * bm + row]);
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    float wsum = 0.f;
+    if (mx != -INFINITY) {
+      for (int r = 0; r < np; ++r) {
+        const int64_t slot = base + (int64_t)r * bm + row;
+        const float w = __builtin_amdgcn_exp2f(a.part_lse[slot] - mx);
+        const float4 o = *reinterpret_cast<const float4*>(a.part_o + slot * D + 4 * c);
+        acc.x = fmaf(w, o.x, acc.x);
+        acc.y = fmaf(w, o.y, acc.y);
+        acc.z = fmaf(w, o.z, acc.z);
+        acc.w = fmaf(w, o.w, acc.w);
+        wsum += w;
+      }
+      const float inv = 1.f / wsum;
+      acc.x *= inv;
+      acc.y *= inv;
+      acc.z *= inv;
+      acc.w *= inv;
+    }
+    float* op = a.o + ooff + (int64_t)(q0 + row) * a.o_ss + (int64_t)h * a.o_hs + 4 * c;
+    *reinterpret_cast<float4*>(op) = acc;
+    if (c == 0 && a.lse != nullptr)
+      a.lse[lseoff + (int64_t)h * a.lse_hs + q0 + row] =
+          mx == -INFINITY ? -INFINITY : (mx + __log2f(wsum)) * kLn2;
   }
 }
 
@@ -1634,7 +1744,7 @@ constexpr int minw_for() { return D == 256 ? 1 : 2; }
 template <int D, bool VARLEN>
 hipError_t launch_d(const AttnArgs& a, int policy_id, hipStream_t stream) {
   const int64_t rows = (int64_t)a.nseq * a.hq;
-  const int64_t grid = rows * a.n_qb;
+  const int64_t grid = rows * a.n_qb * a.n_split;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   const dim3 g((unsigned)grid);
@@ -1783,6 +1893,30 @@ bool select_policy(int head_dim, int max_seqlen_q, bool causal, int64_t rows, in
   if (head_dim == 256) out->bn /= 2;
   *policy_id = id;
   return true;
+}
+
+template <int D>
+hipError_t merge_d(const AttnArgs& a, bool varlen, int bm, hipStream_t stream) {
+  if (bm % kMergeRows != 0) return hipErrorInvalidValue;
+  const int64_t grid = (int64_t)a.nseq * a.hq * a.n_qb * (bm / kMergeRows);
+  if (grid <= 0) return hipSuccess;
+  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  const dim3 block(kMergeRows * D / 4);
+  if (varlen)
+    hipLaunchKernelGGL((merge_split_kernel<D, true>), dim3((unsigned)grid), block, 0, stream, a, bm);
+  else
+    hipLaunchKernelGGL((merge_split_kernel<D, false>), dim3((unsigned)grid), block, 0, stream, a, bm);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge(const AttnArgs& a, int head_dim, bool varlen, int bm, hipStream_t stream) {
+  switch (head_dim) {
+    case 32: return merge_d<32>(a, varlen, bm, stream);
+    case 64: return merge_d<64>(a, varlen, bm, stream);
+    case 128: return merge_d<128>(a, varlen, bm, stream);
+    case 256: return merge_d<256>(a, varlen, bm, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_attention(const AttnArgs& a, int head_dim, bool varlen, int policy_id,
