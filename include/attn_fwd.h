@@ -203,6 +203,40 @@ attn_status_t attn_pad_scatter(const void* src, void* dst, const int32_t* indice
                                int32_t n_valid, int32_t n_rows_total, int64_t row_bytes,
                                void* stream);
 
+/*
+ * attn_fwd_padded -- unpad gather, varlen attention and pad scatter in one call
+ * that never materialises the compact tensors.
+ *
+ * Passage: page "Lesson 5: IAW model FA2 vs FA3 measured", section 1 (the
+ * padded path: gather rows by indices, varlen attention on the compact rows,
+ * scatter back by indices) and section 6 (the launches and the movement that
+ * path costs); the attention is the one of attn_fwd_varlen.
+ *
+ * q    (n_rows, num_heads_q, head_dim) bf16, the PADDED tensor (B * total_len
+ *      rows, row-major, contiguous); k, v (n_rows, num_heads_k, head_dim) bf16.
+ * indices: device int32, n_valid entries, strictly increasing, in [0, n_rows):
+ *      compact row r is padded row indices[r].
+ * cu_seqlens: device int32, num_seqs+1 offsets over the compact rows (queries
+ *      and keys alike); last = n_valid.
+ * Precondition: the rows of one sequence are consecutive in the padded tensor,
+ *      indices[cu_seqlens[s] + i] == indices[cu_seqlens[s]] + i (true of right-
+ *      padded slots and of packed rows).  Violating it gives wrong values for
+ *      that sequence but no out-of-range access.
+ * out  (n_rows, num_heads_q, head_dim) fp32: indexed rows get the attention
+ *      output, every other row is written with +0.0 bytes.
+ * lse  (num_heads_q, n_valid) fp32 over the COMPACT rows, or NULL.
+ * max_seqlen, scale, causal, grouped-query heads, alignment and size limits
+ *      are those of attn_fwd_varlen (sizes measured on the padded tensors).
+ * Two launches: a zero fill of the padding rows, then the attention reading
+ * and writing the padded rows in place.  Results equal those of
+ * attn_unpad_gather + attn_fwd_varlen + attn_pad_scatter bit for bit.
+ */
+attn_status_t attn_fwd_padded(const void* q, const void* k, const void* v,
+                              const int32_t* indices, const int32_t* cu_seqlens, int32_t num_seqs,
+                              int32_t n_valid, int32_t n_rows, int32_t num_heads_q,
+                              int32_t num_heads_k, int32_t head_dim, int32_t max_seqlen,
+                              float scale, int32_t causal, float* out, float* lse, void* stream);
+
 /* Human-readable text of a status code (static storage, never NULL). */
 const char* attn_status_str(attn_status_t s);
 

@@ -164,3 +164,19 @@ def test_workspace_argument_checks(lib):
                                   ctypes.c_void_p(24), 64, None) == ALIGN
     assert lib.attn_fwd_dense_ws(P, P, P, 1, 8, 8, 2, 2, 64, None, 0.125, 1, P, None,
                                  P, -5, None) == SHAPE
+
+
+def test_fused_padded_argument_checks(lib):
+    P = ctypes.c_void_p(16)
+    f = lib.attn_fwd_padded
+    # q, k, v, indices, cu, nseq, n_valid, n_rows, hq, hkv, d, max_seqlen, scale, causal, out, lse
+    assert f(P, P, P, P, P, 1, 9, 8, 2, 2, 64, 8, 0.125, 1, P, None, None) == SHAPE   # n_valid > n_rows
+    assert f(P, P, P, P, P, 1, 8, 8, 2, 2, 64, 8, 0.125, 1, None, None, None) == NULL  # out
+    assert f(None, P, P, P, P, 1, 8, 8, 2, 2, 64, 8, 0.125, 1, P, None, None) == NULL  # q
+    assert f(P, P, P, None, P, 1, 8, 8, 2, 2, 64, 8, 0.125, 1, P, None, None) == NULL  # indices
+    assert f(P, P, P, P, P, 1, 8, 8, 2, 2, 96, 8, 0.125, 1, P, None, None) == UNSUP   # head_dim
+    assert f(P, P, P, P, P, 1, 8, 8, 3, 2, 64, 8, 0.125, 1, P, None, None) == SHAPE   # hq % hkv
+    assert f(P, P, P, P, P, 1, 8, 8, 2, 2, 64, 0, 0.125, 1, P, None, None) == SHAPE   # max_seqlen
+    assert f(P, P, P, P, P, 1, 8, 8, 2, 2, 64, 8, 0.125, 1, ctypes.c_void_p(24), None, None) == ALIGN
+    assert f(P, P, P, P, P, 1, 8, 0, 2, 2, 64, 8, 0.125, 1, P, None, None) == SHAPE   # n_valid > 0 rows
+    assert f(None, None, None, None, None, 0, 0, 0, 2, 2, 64, 0, 0.125, 1, None, None, None) == OK

@@ -372,6 +372,81 @@ def test_padded_path_full_size(name, use_ws):
     print(check_o(ph, p_ref), check_lse(host(lse), lse_ref))
 
 
+# ----------------------------------------------------------------------------- fused padded path
+@pytest.mark.parametrize("name", ["padded_32x128_random", "padded_32x128_exact", "padded_1x2048"])
+def test_fused_padded_equals_three_call_path_bitwise(name):
+    """attn_fwd_padded reads and writes the padded rows in place; with the
+    same tile policy it computes exactly what gather + varlen + scatter do."""
+    t = api()
+    w = gen.build_workload(name)
+    idx = dev_i32(w.indices)
+    cu = dev_i32(w.cu_seqlens_q)
+    q, k, v = dev_bf16(w.q), dev_bf16(w.k), dev_bf16(w.v)
+    qc, kc, vc = t.attn_unpad_gather([q, k, v], idx)
+    o3, lse3 = t.attn_fwd_varlen(qc, kc, vc, cu, cu, w.max_seqlen, scale=float(w.scale),
+                                 causal=True)
+    p3 = host(t.attn_pad_scatter(o3, idx, w.q.shape[1], out_shape=(1,) + w.q.shape[1:]))
+    pf, lsef = t.attn_fwd_padded(q, k, v, idx, cu, w.max_seqlen, scale=float(w.scale),
+                                 causal=True)
+    pf = host(pf)
+    assert pf.shape == p3.shape
+    assert np.array_equal(pf.view(np.uint32), p3.view(np.uint32))
+    assert np.array_equal(host(lsef).view(np.uint32), host(lse3).view(np.uint32))
+    pad_rows = np.ones(w.q.shape[1], bool)
+    pad_rows[w.indices] = False
+    assert np.all(pf[0, pad_rows].view(np.uint32) == 0)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_fused_padded_gqa_nan_padding_vs_oracle(d):
+    """Grouped heads, NaN in every padding row of q/k/v, slots of mixed
+    lengths with an empty one; compared with the oracle's gather, attention
+    and scatter."""
+    t = api()
+    r = np.random.Generator(np.random.PCG64(1800 + d))
+    total, hq, hkv = 1536, 4, 2
+    slots = [256, 512, 128, 384, 256]
+    lens = [200, 512, 0, 1, 97]
+    mask = np.zeros(total, bool)
+    st = 0
+    for sl, L in zip(slots, lens):
+        mask[st:st + L] = True
+        st += sl
+    idx = np.flatnonzero(mask).astype(np.int32)
+    nz = [L for L in lens if L > 0]
+    cu = gen.cu_seqlens_from_lengths(nz)
+    nan = gen.bf16_bits_from_f32(np.array([np.nan], np.float32))[0]
+    q = gen.normal_bf16(r, (1, total, hq, d))
+    k = gen.normal_bf16(r, (1, total, hkv, d))
+    v = gen.normal_bf16(r, (1, total, hkv, d))
+    for x in (q, k, v):
+        x[0, ~mask] = nan
+    for causal in (True, False):
+        out, lse = t.attn_fwd_padded(dev_bf16(q), dev_bf16(k), dev_bf16(v), dev_i32(idx),
+                                     dev_i32(cu), max(nz), causal=causal)
+        out = host(out)
+        assert not np.isnan(out).any()
+        assert np.all(out[0, ~mask].view(np.uint32) == 0)
+        gq = oracle.unpad_gather(q, idx, (hq, d))
+        gk = oracle.unpad_gather(k, idx, (hkv, d))
+        gv = oracle.unpad_gather(v, idx, (hkv, d))
+        scale = np.float32(1.0 / math.sqrt(d))
+        o_ref, lse_ref = oracle.attention_varlen(gq, gk, gv, cu, cu, scale, causal)
+        p_ref = oracle.pad_scatter(o_ref, idx, total).reshape(out.shape)
+        print(d, causal, check_o(out, p_ref), check_lse(host(lse), lse_ref))
+
+
+def test_fused_padded_all_padding_is_zero_fill():
+    import torch
+    t = api()
+    q = torch.full((1, 256, 2, 64), float("nan"), dtype=torch.bfloat16, device="cuda")
+    idx = torch.empty(0, dtype=torch.int32, device="cuda")
+    cu = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = torch.full((1, 256, 2, 64), 5.0, dtype=torch.float32, device="cuda")
+    t.attn_fwd_padded(q, q, q, idx, cu, 0, causal=True, out=out, return_lse=False)
+    assert np.all(host(out).view(np.uint32) == 0)
+
+
 def test_padded_path_nan_padding_does_not_leak():
     t = api()
     w = gen.make_padded("nan", 1300, 1024, [128] * 8, 4, 64, True, random_max=128,

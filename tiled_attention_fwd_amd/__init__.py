@@ -15,7 +15,8 @@ from typing import List, Optional, Sequence, Tuple
 
 from . import _lib
 
-__all__ = ["attn_fwd_varlen", "attn_fwd_dense", "attn_unpad_gather", "attn_pad_scatter",
+__all__ = ["attn_fwd_varlen", "attn_fwd_dense", "attn_fwd_padded", "attn_unpad_gather",
+           "attn_pad_scatter",
            "attn_fwd_workspace_bytes", "workspace", "abi_version", "AttnError"]
 
 AttnError = _lib.AttnError
@@ -154,6 +155,40 @@ def attn_fwd_dense(q, k, v, scale: Optional[float] = None, causal: bool = False,
     else:
         st = lib.attn_fwd_dense_ws(*args, *_ws_args(workspace), _stream_ptr(q.device, stream))
         _lib.check("attn_fwd_dense_ws", st)
+    return out, lse
+
+
+def attn_fwd_padded(q, k, v, indices, cu_seqlens, max_seqlen: int,
+                    scale: Optional[float] = None, causal: bool = False,
+                    out=None, lse=None, return_lse: bool = True, stream=None):
+    """The padded path in one call: q (..., Hq, D), k/v (..., Hkv, D) padded bf16
+    (leading dims flattened to rows), int32 ``indices`` of the valid rows and
+    ``cu_seqlens`` over them.  Returns (out shaped like q, fp32, padding rows
+    +0.0; lse (Hq, n_valid) fp32 or None)."""
+    torch = _torch()
+    lib = _lib.load()
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _check_bf16(n, t)
+    if k.shape != v.shape or q.shape[:-2] != k.shape[:-2] or q.shape[-1] != k.shape[-1]:
+        raise ValueError("q (..., Hq, D) and k, v (..., Hkv, D) must share leading dims and D")
+    for n, t in (("indices", indices), ("cu_seqlens", cu_seqlens)):
+        if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{n} must be a contiguous int32 GPU tensor")
+    hq, d = q.shape[-2], q.shape[-1]
+    hkv = k.shape[-2]
+    n_rows = int(math.prod(q.shape[:-2]))
+    n_valid = indices.numel()
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty((hq, n_valid), dtype=torch.float32, device=q.device)
+    st = lib.attn_fwd_padded(_ptr(q), _ptr(k), _ptr(v), _ptr(indices), _ptr(cu_seqlens),
+                             cu_seqlens.numel() - 1, n_valid, n_rows, hq, hkv, d,
+                             int(max_seqlen), float(scale), int(bool(causal)), _ptr(out),
+                             _ptr(lse), _stream_ptr(q.device, stream))
+    _lib.check("attn_fwd_padded", st)
     return out, lse
 
 

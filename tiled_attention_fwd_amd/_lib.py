@@ -33,6 +33,9 @@ SIGNATURES = {
                                     c_int32, c_int32, c_int32, c_void_p, c_float, c_int32,
                                     c_void_p, c_void_p, c_void_p, c_int64, c_void_p]),
     "attn_fwd_workspace_bytes": (c_int64, [c_int32, c_int32, c_int32, c_int32, c_int32]),
+    "attn_fwd_padded": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32,
+                                  c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,
+                                  c_float, c_int32, c_void_p, c_void_p, c_void_p]),
     "attn_unpad_gather": (c_int32, [c_void_p, c_void_p, c_int32, c_void_p, c_int32, c_int32,
                                     c_int64, c_void_p]),
     "attn_pad_scatter": (c_int32, [c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int64,

@@ -290,6 +290,66 @@ int64_t attn_fwd_workspace_bytes(int32_t num_seqs, int32_t max_seqlen, int32_t n
   return split_workspace_bytes(sp, rows, n_qb, head_dim);
 }
 
+attn_status_t attn_fwd_padded(const void* q, const void* k, const void* v,
+                              const int32_t* indices, const int32_t* cu_seqlens, int32_t num_seqs,
+                              int32_t n_valid, int32_t n_rows, int32_t num_heads_q,
+                              int32_t num_heads_k, int32_t head_dim, int32_t max_seqlen,
+                              float scale, int32_t causal, float* out, float* lse, void* stream) {
+  if (num_seqs < 0 || n_valid < 0 || n_rows < 0 || max_seqlen < 0) return ATTN_ERR_SHAPE;
+  if (n_valid > n_rows) return ATTN_ERR_SHAPE;
+  attn_status_t st = check_common(num_heads_q, num_heads_k, head_dim, scale);
+  if (st != ATTN_OK) return st;
+  if (n_rows == 0 || num_heads_q == 0) return ATTN_OK;
+  if (out == nullptr) return ATTN_ERR_NULL;
+  if (!aligned16(out)) return ATTN_ERR_ALIGN;
+  const bool work = n_valid > 0 && num_seqs > 0;
+  if (work) {
+    if (max_seqlen == 0) return ATTN_ERR_SHAPE;
+    if (q == nullptr || k == nullptr || v == nullptr || indices == nullptr || cu_seqlens == nullptr)
+      return ATTN_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return ATTN_ERR_ALIGN;
+    if (!aligned4(indices) || !aligned4(cu_seqlens) || (lse && !aligned4(lse)))
+      return ATTN_ERR_ALIGN;
+  } else if (n_valid > 0 && (indices == nullptr || !aligned4(indices))) {
+    return indices == nullptr ? ATTN_ERR_NULL : ATTN_ERR_ALIGN;
+  }
+  const int64_t out_row_bytes = (int64_t)num_heads_q * head_dim * 4;
+  if ((int64_t)n_rows * (out_row_bytes / 16) >= (1LL << 31)) return ATTN_ERR_SHAPE;
+  AttnArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = out;
+  a.lse = lse;
+  a.cu_q = cu_seqlens;
+  a.cu_k = cu_seqlens;
+  a.row_of = indices;
+  a.q_ss = (int64_t)num_heads_q * head_dim;
+  a.q_hs = head_dim;
+  a.k_ss = (int64_t)num_heads_k * head_dim;
+  a.k_hs = head_dim;
+  a.v_ss = a.k_ss;
+  a.v_hs = head_dim;
+  a.o_ss = a.q_ss;
+  a.o_hs = head_dim;
+  a.lse_hs = n_valid;
+  a.nseq = num_seqs;
+  a.hq = num_heads_q;
+  a.hkv = num_heads_k;
+  a.group = num_heads_k > 0 ? num_heads_q / num_heads_k : 1;
+  a.c = base2_factor(scale);
+  a.causal = causal ? 1 : 0;
+  if (!span_fits(n_rows, a.q_ss) || !span_fits(n_rows, a.k_ss)) return ATTN_ERR_SHAPE;
+  // padding rows: +0.0, one pass; the attention writes every indexed row
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (attnfwd::launch_scatter(nullptr, out, indices, n_valid, n_rows, out_row_bytes, s) !=
+      hipSuccess)
+    return ATTN_ERR_HIP;
+  if (!work) return ATTN_OK;
+  const int max_q = max_seqlen < n_valid ? max_seqlen : n_valid;
+  return launch(a, head_dim, true, max_q, nullptr, 0, s);
+}
+
 attn_status_t attn_unpad_gather(const void* const* src, void* const* dst, int32_t n_tensors,
                                 const int32_t* indices, int32_t n_valid, int32_t n_rows_src,
                                 int64_t row_bytes, void* stream) {

@@ -17,6 +17,11 @@ struct AttnArgs {
   float* lse;  // may be null
   const int32_t* cu_q;  // varlen only
   const int32_t* cu_k;  // varlen only
+  // Padded layout (varlen only, may be null): compact row r lives at row
+  // row_of[r] of q/k/v/o, and the rows of one sequence are consecutive there,
+  // so a sequence starts at row row_of[cu[s]].  The LSE stays indexed by
+  // compact row.
+  const int32_t* row_of;
   int64_t q_bs, q_ss, q_hs;
   int64_t k_bs, k_ss, k_hs;
   int64_t v_bs, v_ss, v_hs;
@@ -39,6 +44,26 @@ struct AttnArgs {
   float* part_o;    // [rows][n_qb][n_split][bm][head_dim]
   float* part_lse;  // [rows][n_qb][n_split][bm]
 };
+
+// First q/k/v/o row of varlen sequence `seq` and its lengths.  qs / ks are
+// the compact offsets (cu_q[seq], cu_k[seq]); q_row / k_row the storage rows.
+struct SeqRows {
+  int qs, ks, lq, lk, q_row, k_row;
+};
+__device__ __forceinline__ SeqRows seq_rows(const AttnArgs& a, int seq) {
+  SeqRows r;
+  r.qs = a.cu_q[seq];
+  r.ks = a.cu_k[seq];
+  r.lq = a.cu_q[seq + 1] - r.qs;
+  r.lk = a.cu_k[seq + 1] - r.ks;
+  r.q_row = r.qs;
+  r.k_row = r.ks;
+  if (a.row_of != nullptr) {
+    if (r.lq > 0) r.q_row = a.row_of[r.qs];
+    if (r.lk > 0) r.k_row = a.row_of[r.ks];
+  }
+  return r;
+}
 
 // Number of parts a query block with n_kt key tiles is cut into.
 __host__ __device__ inline int split_parts(int n_kt, int n_split, int split_tiles) {
@@ -75,7 +100,8 @@ hipError_t launch_gather(const void* const* src, void* const* dst, int n_tensors
                          const int32_t* indices, int n_valid, int n_rows_src, int64_t row_bytes,
                          hipStream_t stream);
 
-// Row scatter with zero fill of the rows no index names.
+// Row scatter with zero fill of the rows no index names.  src == nullptr:
+// only the zero fill (indexed rows are left untouched).
 hipError_t launch_scatter(const void* src, void* dst, const int32_t* indices, int n_valid,
                           int n_rows_total, int64_t row_bytes, hipStream_t stream);
 

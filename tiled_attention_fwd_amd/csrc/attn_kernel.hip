@@ -191,15 +191,14 @@ __global__ __launch_bounds__(WAVES * 64, MINW) void attn_fwd_kernel(const AttnAr
   int lq, lk;
   int64_t qoff, koff, voff, ooff, lseoff;
   if constexpr (VARLEN) {
-    const int qs = a.cu_q[seq];
-    const int kst = a.cu_k[seq];
-    lq = a.cu_q[seq + 1] - qs;
-    lk = a.cu_k[seq + 1] - kst;
-    qoff = (int64_t)qs * a.q_ss;
-    koff = (int64_t)kst * a.k_ss;
-    voff = (int64_t)kst * a.v_ss;
-    ooff = (int64_t)qs * a.o_ss;
-    lseoff = qs;
+    const SeqRows sr = seq_rows(a, seq);
+    lq = sr.lq;
+    lk = sr.lk;
+    qoff = (int64_t)sr.q_row * a.q_ss;
+    koff = (int64_t)sr.k_row * a.k_ss;
+    voff = (int64_t)sr.k_row * a.v_ss;
+    ooff = (int64_t)sr.q_row * a.o_ss;
+    lseoff = sr.qs;
   } else {
     lq = a.sq;
     lk = a.sk;
@@ -580,15 +579,14 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_pingpong_kernel(const AttnArg
   int lq, lk;
   int64_t qoff, koff, voff, ooff, lseoff;
   if constexpr (VARLEN) {
-    const int qs = a.cu_q[seq];
-    const int kst = a.cu_k[seq];
-    lq = a.cu_q[seq + 1] - qs;
-    lk = a.cu_k[seq + 1] - kst;
-    qoff = (int64_t)qs * a.q_ss;
-    koff = (int64_t)kst * a.k_ss;
-    voff = (int64_t)kst * a.v_ss;
-    ooff = (int64_t)qs * a.o_ss;
-    lseoff = qs;
+    const SeqRows sr = seq_rows(a, seq);
+    lq = sr.lq;
+    lk = sr.lk;
+    qoff = (int64_t)sr.q_row * a.q_ss;
+    koff = (int64_t)sr.k_row * a.k_ss;
+    voff = (int64_t)sr.k_row * a.v_ss;
+    ooff = (int64_t)sr.q_row * a.o_ss;
+    lseoff = sr.qs;
   } else {
     lq = a.sq;
     lk = a.sk;
@@ -972,15 +970,14 @@ __global__ __launch_bounds__(WAVES * 64, D == 256 ? 1 : 2) void attn_fwd_dma_ker
   int lq, lk;
   int64_t qoff, koff, voff, ooff, lseoff;
   if constexpr (VARLEN) {
-    const int qs = a.cu_q[seq];
-    const int kst = a.cu_k[seq];
-    lq = a.cu_q[seq + 1] - qs;
-    lk = a.cu_k[seq + 1] - kst;
-    qoff = (int64_t)qs * a.q_ss;
-    koff = (int64_t)kst * a.k_ss;
-    voff = (int64_t)kst * a.v_ss;
-    ooff = (int64_t)qs * a.o_ss;
-    lseoff = qs;
+    const SeqRows sr = seq_rows(a, seq);
+    lq = sr.lq;
+    lk = sr.lk;
+    qoff = (int64_t)sr.q_row * a.q_ss;
+    koff = (int64_t)sr.k_row * a.k_ss;
+    voff = (int64_t)sr.k_row * a.v_ss;
+    ooff = (int64_t)sr.q_row * a.o_ss;
+    lseoff = sr.qs;
   } else {
     lq = a.sq;
     lk = a.sk;
@@ -1288,11 +1285,11 @@ __global__ __launch_bounds__(kMergeRows * D / 4) void merge_split_kernel(const A
   int lq, lk;
   int64_t ooff, lseoff;
   if constexpr (VARLEN) {
-    const int qs = a.cu_q[seq];
-    lq = a.cu_q[seq + 1] - qs;
-    lk = a.cu_k[seq + 1] - a.cu_k[seq];
-    ooff = (int64_t)qs * a.o_ss;
-    lseoff = qs;
+    const SeqRows sr = seq_rows(a, seq);
+    lq = sr.lq;
+    lk = sr.lk;
+    ooff = (int64_t)sr.q_row * a.o_ss;
+    lseoff = sr.qs;
   } else {
     lq = a.sq;
     lk = a.sk;
@@ -1422,15 +1419,14 @@ __global__ __launch_bounds__(WAVES * 64, MINW) void attn_fwd_pipe_kernel(const A
   int lq, lk;
   int64_t qoff, koff, voff, ooff, lseoff;
   if constexpr (VARLEN) {
-    const int qs = a.cu_q[seq];
-    const int kst = a.cu_k[seq];
-    lq = a.cu_q[seq + 1] - qs;
-    lk = a.cu_k[seq + 1] - kst;
-    qoff = (int64_t)qs * a.q_ss;
-    koff = (int64_t)kst * a.k_ss;
-    voff = (int64_t)kst * a.v_ss;
-    ooff = (int64_t)qs * a.o_ss;
-    lseoff = qs;
+    const SeqRows sr = seq_rows(a, seq);
+    lq = sr.lq;
+    lk = sr.lk;
+    qoff = (int64_t)sr.q_row * a.q_ss;
+    koff = (int64_t)sr.k_row * a.k_ss;
+    voff = (int64_t)sr.k_row * a.v_ss;
+    ooff = (int64_t)sr.q_row * a.o_ss;
+    lseoff = sr.qs;
   } else {
     lq = a.sq;
     lk = a.sk;

@@ -112,6 +112,7 @@ __global__ __launch_bounds__(kThreads) void scatter_rows_kernel(
     const int row = g / cpr;
     const int col = g - row * cpr;
     const int sp = srcpos[row];
+    if (sp >= 0 && src == nullptr) continue;  // fill only: indexed rows stay as they are
     const uint4 v = sp >= 0 ? src[(int64_t)sp * cpr + col] : make_uint4(0, 0, 0, 0);
     dst[(int64_t)(r0 + row) * cpr + col] = v;
   }
