@@ -196,11 +196,11 @@ def test_future_perturbation_leaves_prefix_bitwise():
 
 
 # Policies the library does not compile for a head_dim (register or LDS budget).
-NOT_COMPILED = {256: {"2", "8", "9", "10", "11", "12", "14", "15", "16"},
+NOT_COMPILED = {256: {"2", "8", "9", "10", "11", "12", "14", "15", "16", "17"},
                 32: {"11", "14", "15", "16"}}
 
 
-@pytest.mark.parametrize("policy", [str(i) for i in range(17)])
+@pytest.mark.parametrize("policy", [str(i) for i in range(18)])
 @pytest.mark.parametrize("causal", [True, False])
 def test_every_compiled_tile_policy(policy, causal):
     os.environ["ATTN_FWD_TILE"] = policy
@@ -261,7 +261,7 @@ def test_scatter_search_sizes(n_valid, n_rows):
 
 
 # ----------------------------------------------------------------------------- split key ranges
-SPLIT_POLICIES = ["11", "12", "13"]
+SPLIT_POLICIES = ["11", "12", "13", "17"]
 
 
 def _forced_split(policy, tiles):

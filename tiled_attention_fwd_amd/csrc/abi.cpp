@@ -58,7 +58,7 @@ SplitPlan plan_split(const TilePolicy& pol, int pid, int64_t rows, int n_qb, int
   SplitPlan sp;
   sp.bm = pol.bm();
   sp.bn = pol.bn;
-  if (pid < 11 || pid > 13) return sp;
+  if (!(pid >= 11 && pid <= 13) && pid != 17) return sp;
   const int64_t bm = pol.bm(), bn = pol.bn;
   const int64_t max_tiles = (max_q + bn - 1) / bn;
   int64_t total = 0;  // key tiles summed over the blocks of one (sequence, head)

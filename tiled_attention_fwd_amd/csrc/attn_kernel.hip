@@ -926,10 +926,11 @@ __device__ __forceinline__ int swz_v(int row) {
   else return 0;
 }
 
-template <int D, int WAVES, int KG, int NBUF, bool VARLEN>
+template <int D, int WAVES, int KG, int NBUF, bool VARLEN, int SUB = 1>
 __global__ __launch_bounds__(WAVES * 64, D == 256 ? 1 : 2) void attn_fwd_dma_kernel(const AttnArgs a) {
   constexpr int NT = WAVES * 64;
-  constexpr int BN = D == 256 ? 32 : 64;
+  constexpr int BN0 = D == 256 ? 32 : 64;    // keys per compute sub-tile
+  constexpr int BN = SUB * BN0;              // keys per DMA tile (one barrier each)
   constexpr int QW = WAVES / KG;
   constexpr int BM = QW * 32;
   constexpr int CPR = D / 8;                 // 16-byte chunks per row
@@ -938,7 +939,7 @@ __global__ __launch_bounds__(WAVES * 64, D == 256 ? 1 : 2) void attn_fwd_dma_ker
   constexpr int NK = KG * IPT;               // ... for the K tiles of one step (same for V)
   static_assert(NK % WAVES == 0, "DMA instructions must split evenly over the waves");
   constexpr int PER_WAVE = 2 * NK / WAVES;   // DMA instructions one wave issues per step
-  constexpr int NKB = BN / 32;
+  constexpr int NKB = BN0 / 32;
   constexpr int NDS = D / 16;
   constexpr int NDB = D / 32;
   static_assert(NBUF == 2 || NBUF == 3, "two or three buffers");
@@ -1069,13 +1070,9 @@ __global__ __launch_bounds__(WAVES * 64, D == 256 ? 1 : 2) void attn_fwd_dma_ker
   const int vcc = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);  // chunk within a 32-dim block
   const int vhalf = (lane & 1) * 4;
 
-  auto compute = [&](auto Bc, int step) {
-    constexpr int B = decltype(Bc)::value;
-    const uint16_t* kd = (B == 0 ? ks0 : B == 1 ? ks1 : ks2) + kg * TILE;
-    const uint16_t* vd = (B == 0 ? vs0 : B == 1 ? vs1 : vs2) + kg * TILE;
-    const int kt = t_begin + step * KG + kg;
-    const int kbeg = kt * BN;
-    if (kt >= t_end || kbeg >= kend_w) return;
+  // one sub-tile of BN0 keys starting at key kbeg, rows kd / vd of the tile
+  auto sub_tile = [&](const uint16_t* kd, const uint16_t* vd, int kbeg) __attribute__((always_inline)) {
+    if (kbeg >= kend_w) return;
     f32x16 sacc[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
@@ -1086,7 +1083,7 @@ __global__ __launch_bounds__(WAVES * 64, D == 256 ? 1 : 2) void attn_fwd_dma_ker
                                                            0, 0, 0);
       }
     lds_pipeline_hint<NKB * NDS>();
-    if ((kbeg + BN > lk) || (a.causal && kbeg + BN - 1 > qw0 + off)) {
+    if ((kbeg + BN0 > lk) || (a.causal && kbeg + BN0 - 1 > qw0 + off)) {
       const int lim = a.causal ? min(lk - 1, qw0 + l32 + off) : lk - 1;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
@@ -1149,6 +1146,16 @@ __global__ __launch_bounds__(WAVES * 64, D == 256 ? 1 : 2) void attn_fwd_dma_ker
           const bf16x8 vf = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
           oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kb][t], oacc[db], 0, 0, 0);
         }
+  };
+
+  auto compute = [&](auto Bc, int step) {
+    constexpr int B = decltype(Bc)::value;
+    const uint16_t* kd = (B == 0 ? ks0 : B == 1 ? ks1 : ks2) + kg * TILE;
+    const uint16_t* vd = (B == 0 ? vs0 : B == 1 ? vs1 : vs2) + kg * TILE;
+    const int kt = t_begin + step * KG + kg;
+    if (kt >= t_end) return;
+#pragma unroll
+    for (int sb = 0; sb < SUB; ++sb) sub_tile(kd + sb * BN0 * D, vd + sb * BN0 * D, kt * BN + sb * BN0);
   };
 
   // ---- pipeline: step s reads buffer s % NBUF; the DMA runs NBUF-1 steps ahead --
@@ -1730,7 +1737,9 @@ __global__ __launch_bounds__(WAVES * 64, MINW) void attn_fwd_pipe_kernel(const A
 //  14: software-pipelined kernel, 8 waves (BM 256), four buffers
 //  15: software-pipelined kernel, 4 waves (BM 128), 32-key tiles, three buffers
 //  16: as 15 with four buffers
-constexpr int kNumPolicies = 17;
+//  17: DMA-staged kernel, 8 waves (BM 256), 128-key DMA tiles computed as two
+//      64-key sub-tiles (one barrier per 128 keys), two buffers
+constexpr int kNumPolicies = 18;
 
 template <int D>
 constexpr int bn_for() { return D == 256 ? 32 : 64; }
@@ -1836,6 +1845,13 @@ hipError_t launch_d(const AttnArgs& a, int policy_id, hipStream_t stream) {
                              stream, a);
       }
       break;
+    case 17:
+      if constexpr (D == 256) {
+        return hipErrorInvalidValue;
+      } else {
+        hipLaunchKernelGGL((attn_fwd_dma_kernel<D, 8, 1, 2, VARLEN, 2>), g, dim3(512), 0, stream, a);
+      }
+      break;
     default:
       return hipErrorInvalidValue;
   }
@@ -1855,14 +1871,16 @@ bool select_policy(int head_dim, int max_seqlen_q, bool causal, int64_t rows, in
                                                   {8, 1, 64}, {8, 1, 128}, {8, 1, 128}, {4, 1, 64},
                                                   {8, 1, 64}, {8, 1, 64, 2}, {8, 1, 32, 4},
                                                   {8, 1, 64}, {8, 1, 64, 2}, {4, 1, 64},
-                                                  {8, 1, 64}, {4, 1, 32}, {4, 1, 32}};
+                                                  {8, 1, 64}, {4, 1, 32}, {4, 1, 32},
+                                                  {8, 1, 128}};
   int id;
   if (override_id >= 0) {
     if (override_id >= kNumPolicies) return false;
     if (head_dim == 256 && (override_id == 2 || (override_id >= 8 && override_id <= 12) ||
                             override_id >= 14))
       return false;  // not compiled (register or LDS budget)
-    if (head_dim == 32 && (override_id == 11 || override_id >= 14)) return false;
+    if (head_dim == 32 && (override_id == 11 || (override_id >= 14 && override_id <= 16)))
+      return false;
     id = override_id;
   } else {
     // Chosen from measured sweeps over the workload set (dense, varlen,
