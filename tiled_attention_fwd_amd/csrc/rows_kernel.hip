@@ -18,6 +18,15 @@ namespace attnfwd {
 namespace {
 
 constexpr int kThreads = 256;
+
+// The padded output of the scatter is written once and read by nothing that
+// follows on the path: streaming (nontemporal) stores keep it from displacing
+// useful lines.  (The gather's output is read right away by the attention, so
+// it stays on normal stores: streaming it measured slower end to end.)
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store_stream(uint4* p, uint4 v) {
+  __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4*>(p));
+}
 constexpr int kUnroll = 4;  // 16-byte chunks per thread per pass
 
 struct GatherArgs {
@@ -53,7 +62,7 @@ __global__ __launch_bounds__(kThreads) void gather_rows_kernel(const GatherArgs 
   }
 #pragma unroll
   for (int i = 0; i < kUnroll; ++i)
-    if (out_at[i] >= 0) dst[out_at[i]] = val[i];
+    if (out_at[i] >= 0) dst[out_at[i]] = val[i];  // read next by the attention: keep cached
 }
 
 // Scatter: each workgroup owns kRows consecutive destination rows.  Because
@@ -114,7 +123,7 @@ __global__ __launch_bounds__(kThreads) void scatter_rows_kernel(
     const int sp = srcpos[row];
     if (sp >= 0 && src == nullptr) continue;  // fill only: indexed rows stay as they are
     const uint4 v = sp >= 0 ? src[(int64_t)sp * cpr + col] : make_uint4(0, 0, 0, 0);
-    dst[(int64_t)(r0 + row) * cpr + col] = v;
+    store_stream(&dst[(int64_t)(r0 + row) * cpr + col], v);
   }
 }
 
