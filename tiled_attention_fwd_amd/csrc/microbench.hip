@@ -1,7 +1,9 @@
 // Microbenchmarks that ground the roofline figures used for the attention
 // kernel on gfx950: MFMA bf16 32x32x16 rate, v_exp_f32 and v_fma_f32 issue
-// rates, LDS 16-byte read bandwidth, and a plain 16-byte copy kernel (its
-// known byte count calibrates the HBM traffic counters).
+// rates, LDS 16-byte read bandwidth, a plain 16-byte copy kernel (its known
+// byte count calibrates the HBM traffic counters), and the MFMA rate with
+// independent VALU, exp and LDS work mixed in at 2 waves per SIMD (the
+// ceiling for the attention loop's instruction mix).
 //
 // Prints one JSON object.  Every kernel only touches buffers it allocates, with
 // indices bounded by the launch shape.
@@ -102,6 +104,45 @@ __global__ __launch_bounds__(256) void copy_kernel(const uint4* __restrict__ src
   for (; i < n; i += stride) dst[i] = src[i];
 }
 
+// Per MFMA: NV independent v_fma_f32, NX v_exp_f32, NL 16-byte LDS reads
+// (each feeding a later MFMA's A operand).  Two accumulators alternate.
+constexpr int kMixIters = 256;
+template <int NV, int NX, int NL>
+__global__ void mix_kernel(float* out, float seed) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  const int lane = threadIdx.x & 63;
+  for (int i = threadIdx.x; i < 8192; i += blockDim.x) reinterpret_cast<float*>(lds)[i] = seed * i;
+  __syncthreads();
+  bf16x8 a, b;
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (__bf16)(seed * (threadIdx.x + i));
+    b[i] = (__bf16)(seed * i);
+  }
+  f32x16 acc0 = {}, acc1 = {};
+  float v[16];
+  for (int i = 0; i < 16; ++i) v[i] = seed * (i + lane);
+  for (int it = 0; it < kMixIters; ++it) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      if (k & 1) acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc1, 0, 0, 0);
+      else acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc0, 0, 0, 0);
+#pragma unroll
+      for (int j = 0; j < NV; ++j) v[(k * 3 + j) & 15] = fmaf(v[(k * 3 + j) & 15], seed, 0.5f);
+#pragma unroll
+      for (int j = 0; j < NX; ++j) v[(k * 5 + j + 7) & 15] = __builtin_amdgcn_exp2f(v[(k * 5 + j + 7) & 15]);
+#pragma unroll
+      for (int j = 0; j < NL; ++j) {
+        // offsets stay below 32 KiB of the 100 KiB dynamic LDS
+        const uint4 u = *reinterpret_cast<const uint4*>(lds + ((lane * 16 + (k * NL + j) * 1024 + it * 64) & 32767));
+        a = __builtin_bit_cast(bf16x8, u);
+      }
+    }
+  }
+  float s = 0.f;
+  for (int r = 0; r < 16; ++r) s += acc0[r] + acc1[r] + v[r];
+  out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
 template <typename F>
 float time_ms(F launch, int reps) {
   hipEvent_t a, b;
@@ -150,6 +191,20 @@ int main(int argc, char** argv) {
   const double lds_bytes = (double)cus * 2 * 256 * kIters * 8 * 16;
   const double lds_tbs = lds_bytes / (ms * 1e-3) / 1e12;
 
+  // MFMA rate with mixed-in work: 512 threads and 100 KiB of LDS per workgroup,
+  // one workgroup per CU = 2 waves per SIMD
+  const size_t mix_lds = 100 * 1024;
+  auto mix = [&](auto kern) {
+    CHECK(hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, mix_lds));
+    const double ms_ = time_ms([&] { hipLaunchKernelGGL(kern, dim3(cus), dim3(512), mix_lds, 0, out, 1e-3f); }, 5);
+    return (double)cus * 8 * kMixIters * 16 * 32768.0 / (ms_ * 1e-3) / 1e12;
+  };
+  const double mix_pure = mix(mix_kernel<0, 0, 0>);
+  const double mix_v4 = mix(mix_kernel<4, 0, 0>);
+  const double mix_x1 = mix(mix_kernel<0, 1, 0>);
+  const double mix_l1 = mix(mix_kernel<0, 0, 1>);
+  const double mix_all = mix(mix_kernel<4, 1, 1>);
+
   uint4 *src, *dst;
   const long n = copy_bytes / 16;
   CHECK(hipMalloc(&src, n * 16));
@@ -161,9 +216,11 @@ int main(int argc, char** argv) {
   printf("{\"device\": \"%s\", \"cus\": %d, \"clock_mhz\": %d, "
          "\"mfma_bf16_32x32x16_tflops\": %.1f, \"exp2_plus_sub_tops\": %.3f, "
          "\"exp2_tops\": %.3f, \"fma_tops\": %.3f, \"lds_read_tbs\": %.2f, "
-         "\"copy_gbs\": %.1f, \"copy_bytes_each_way\": %ld}\n",
+         "\"copy_gbs\": %.1f, \"copy_bytes_each_way\": %ld, "
+         "\"mfma_mix_2w_tflops\": {\"mfma_only\": %.1f, \"plus_4_fma\": %.1f, "
+         "\"plus_1_exp\": %.1f, \"plus_1_lds16\": %.1f, \"plus_4_fma_1_exp_1_lds16\": %.1f}}\n",
          prop.name, cus, prop.clockRate / 1000, mfma_tflops, exp_sub_rate, exp_rate, fma_rate,
-         lds_tbs, copy_gbs, n * 16);
+         lds_tbs, copy_gbs, n * 16, mix_pure, mix_v4, mix_x1, mix_l1, mix_all);
   CHECK(hipFree(src));
   CHECK(hipFree(dst));
   CHECK(hipFree(out));
