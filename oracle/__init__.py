@@ -14,8 +14,13 @@ the same result as the standard softmax.  The causal mask (same page, the
 paragraph on fusing the causal mask) lets each query see only keys at or before
 its own position.
 
+The gradients (backward.py) follow the page's statement that the backward pass
+recomputes the forward (same page, the second pitfall) and are the exact
+chain-rule derivative of the definition above.
+
 Every function in this package is pinned by CPU tests against closed forms,
-invariants and a brute-force per-query loop; none is "parity unpinned".
+invariants, a brute-force per-query loop and, for the gradients, central finite
+differences of the forward; none is "parity unpinned".
 """
 
 from .attention import (  # noqa: F401
@@ -28,3 +33,8 @@ from .attention import (  # noqa: F401
     attention_query,
 )
 from .layout import unpad_gather, pad_scatter  # noqa: F401
+from .backward import (  # noqa: F401
+    attention_backward_one,
+    attention_backward_varlen,
+    attention_backward_dense,
+)
