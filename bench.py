@@ -35,7 +35,8 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ["tiled_attention_fwd_amd/csrc/attn_kernel.hip",
+KERNEL_SOURCES = ["tiled_attention_fwd_amd/csrc/attn_device.h",
+                  "tiled_attention_fwd_amd/csrc/attn_kernel.hip",
                   "tiled_attention_fwd_amd/csrc/rows_kernel.hip"]
 
 
