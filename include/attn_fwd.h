@@ -4,7 +4,8 @@
  * The library computes O = softmax(scale * Q K^T) V per (sequence, query head)
  * without materialising the score matrix, for dense batched inputs and for
  * variable-length packed inputs, plus the row gather/scatter that moves packed
- * rows between the padded and the compact layouts.
+ * rows between the padded and the compact layouts, and the gradients of the
+ * attention (backward by recomputation).
  *
  * Sources of the operations (web pages, cited by title and section):
  *  - "Intro to FlashAttention on Ascend CANN" (ai6s.net): the standard
@@ -236,6 +237,66 @@ attn_status_t attn_fwd_padded(const void* q, const void* k, const void* v,
                               int32_t n_valid, int32_t n_rows, int32_t num_heads_q,
                               int32_t num_heads_k, int32_t head_dim, int32_t max_seqlen,
                               float scale, int32_t causal, float* out, float* lse, void* stream);
+
+/*
+ * attn_bwd_varlen -- gradients of attn_fwd_varlen with respect to q, k and v.
+ *
+ * Passage: page "Intro to FlashAttention on Ascend CANN", section on the
+ * second pitfall (backward propagation): the backward pass recomputes the
+ * attention probabilities tile by tile from q, k and the forward's
+ * log-sum-exp instead of storing them.  The gradients are the exact
+ * derivatives of the forward's definition: with P = exp(scale q.k - lse)
+ * over the visible keys (0 elsewhere) and dO the gradient of `out`,
+ *   dv = P^T dO,  dS = P * (dO v^T - rowsum(dO * out)),
+ *   dq = scale dS k,  dk = scale dS^T q,
+ * and a grouped key/value head receives the sum over its query heads.
+ *
+ * q, k, v, cu_seqlens_q, cu_seqlens_k, num_seqs, total_q, total_k, the head
+ *      counts, scale and causal: exactly as passed to attn_fwd_varlen.
+ * out  (total_q, num_heads_q, head_dim) fp32 and lse (num_heads_q, total_q)
+ *      fp32: the forward's outputs for these inputs (lse is required here).
+ * dout (total_q, num_heads_q, head_dim) bf16: the gradient of out.
+ * max_seqlen_q / max_seqlen_k: upper bounds on every query / key length.
+ * dq (total_q, num_heads_q, head_dim), dk and dv (total_k, num_heads_k,
+ *      head_dim): fp32 outputs, every element written once (keys that no
+ *      query sees get 0, as do queries that see no key).
+ * workspace: device memory of at least attn_bwd_workspace_bytes(total_q,
+ *      num_heads_q) bytes, 16-byte aligned, owned by the caller; it holds
+ *      rowsum(dO * out) between the launches and may be reused afterwards.
+ * head_dim must be 64 or 128 (else ATTN_ERR_UNSUPPORTED).  Every pointer
+ * must be non-NULL and 16-byte aligned (lse and cu_seqlens 4-byte aligned).
+ * Three launches on `stream`, no atomics: rowsum(dO * out), then dq, then
+ * dk and dv.  Results are deterministic.
+ */
+attn_status_t attn_bwd_varlen(const void* q, const void* k, const void* v, const float* out,
+                              const void* dout, const float* lse, const int32_t* cu_seqlens_q,
+                              const int32_t* cu_seqlens_k, int32_t num_seqs, int32_t total_q,
+                              int32_t total_k, int32_t num_heads_q, int32_t num_heads_k,
+                              int32_t head_dim, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                              float scale, int32_t causal, float* dq, float* dk, float* dv,
+                              void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * attn_bwd_dense -- gradients of attn_fwd_dense (contiguous layouts only).
+ *
+ * Passage and formulas: those of attn_bwd_varlen.  q, dout (batch, seqlen_q,
+ * num_heads_q, head_dim) bf16; k, v (batch, seqlen_k, num_heads_k, head_dim)
+ * bf16; out (batch, seqlen_q, num_heads_q, head_dim) fp32 and lse (batch,
+ * num_heads_q, seqlen_q) fp32 from attn_fwd_dense; dq, dk, dv fp32 shaped
+ * like q, k, v.  Workspace: attn_bwd_workspace_bytes(batch * seqlen_q,
+ * num_heads_q) bytes.  Other rules as for attn_bwd_varlen.
+ */
+attn_status_t attn_bwd_dense(const void* q, const void* k, const void* v, const float* out,
+                             const void* dout, const float* lse, int32_t batch, int32_t seqlen_q,
+                             int32_t seqlen_k, int32_t num_heads_q, int32_t num_heads_k,
+                             int32_t head_dim, float scale, int32_t causal, float* dq, float* dk,
+                             float* dv, void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * attn_bwd_workspace_bytes -- workspace the backward calls need: 4 bytes per
+ * (query row, query head).  Returns 0 for non-positive arguments.  Host only.
+ */
+int64_t attn_bwd_workspace_bytes(int64_t total_q, int32_t num_heads_q);
 
 /* Human-readable text of a status code (static storage, never NULL). */
 const char* attn_status_str(attn_status_t s);

@@ -67,6 +67,12 @@ def normal_bf16(rng: np.random.Generator, shape) -> np.ndarray:
     return bf16_bits_from_f32(rng.standard_normal(size=shape, dtype=np.float32))
 
 
+def upstream_grad_bf16(seed: int, shape) -> np.ndarray:
+    """Seeded N(0,1) bf16 bits standing in for the gradient of the attention
+    output (its own stream, so the forward inputs do not change)."""
+    return normal_bf16(np.random.Generator(np.random.PCG64(seed + 7_000_000)), shape)
+
+
 def cu_seqlens_from_lengths(lengths) -> np.ndarray:
     """Packing offsets [0, L0, L0+L1, ...] as int32."""
     lens = np.asarray(lengths, dtype=np.int64)

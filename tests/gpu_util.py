@@ -11,6 +11,13 @@ O_MEAN_ABS = 2e-3
 LSE_MAX_ABS = 1e-3
 
 
+# Gradient bar (bf16 inputs, bf16 P and dS operands, fp32 accumulation):
+# relative to the gradient's scale G = max(1, max |ref|),
+# max |g - ref| <= 2e-2 G and mean |g - ref| <= 2e-3 G.
+GRAD_MAX_REL = 2e-2
+GRAD_MEAN_REL = 2e-3
+
+
 def dev_bf16(bits: np.ndarray):
     import torch
     t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
@@ -51,3 +58,16 @@ def check_lse(l_gpu: np.ndarray, l_ref: np.ndarray, what: str = "LSE") -> float:
     e = float(np.abs(l_gpu[fin].astype(np.float64) - l_ref[fin]).max())
     assert e <= LSE_MAX_ABS, f"{what}: max abs err {e:.3e} > {LSE_MAX_ABS}"
     return e
+
+
+def check_grad(g_gpu: np.ndarray, g_ref: np.ndarray, what: str) -> dict:
+    assert g_gpu.shape == g_ref.shape, (g_gpu.shape, g_ref.shape)
+    assert np.isfinite(g_gpu).all(), f"{what}: non-finite value in GPU gradient"
+    if g_ref.size == 0:
+        return {"max": 0.0, "mean": 0.0, "scale": 0.0}
+    scale = max(1.0, float(np.abs(g_ref).max()))
+    err = np.abs(g_gpu.astype(np.float64) - g_ref)
+    mx, mean = float(err.max()), float(err.mean())
+    assert mx <= GRAD_MAX_REL * scale, f"{what}: max abs err {mx:.3e} > {GRAD_MAX_REL} * {scale:.3g}"
+    assert mean <= GRAD_MEAN_REL * scale, f"{what}: mean abs err {mean:.3e} > {GRAD_MEAN_REL} * {scale:.3g}"
+    return {"max": mx, "mean": mean, "scale": scale}

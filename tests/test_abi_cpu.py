@@ -180,3 +180,32 @@ def test_fused_padded_argument_checks(lib):
     assert f(P, P, P, P, P, 1, 8, 8, 2, 2, 64, 8, 0.125, 1, ctypes.c_void_p(24), None, None) == ALIGN
     assert f(P, P, P, P, P, 1, 8, 0, 2, 2, 64, 8, 0.125, 1, P, None, None) == SHAPE   # n_valid > 0 rows
     assert f(None, None, None, None, None, 0, 0, 0, 2, 2, 64, 0, 0.125, 1, None, None, None) == OK
+
+
+def test_backward_argument_checks(lib):
+    P = ctypes.c_void_p(16)
+    f = lib.attn_bwd_varlen
+    # q, k, v, out, dout, lse, cu_q, cu_k, nseq, tq, tk, hq, hkv, d, mq, mk, scale, causal,
+    # dq, dk, dv, ws, ws_bytes, stream
+    ok = lambda **kw: dict(dict(d=64, ws=P, wsb=1 << 20, dq=P, hq=2, hkv=2, scale=0.125, mq=8), **kw)
+
+    def call(**kw):
+        a = ok(**kw)
+        return f(P, P, P, P, P, P, P, P, 1, 8, 8, a["hq"], a["hkv"], a["d"], a["mq"], 8,
+                 a["scale"], 1, a["dq"], P, P, a["ws"], a["wsb"], None)
+    assert call(d=32) == UNSUP and call(d=256) == UNSUP and call(d=96) == UNSUP
+    assert call(scale=0.0) == UNSUP
+    assert call(hq=3) == SHAPE                       # hq % hkv
+    assert call(wsb=8 * 2 * 4 - 4) == SHAPE          # workspace below 4 * tq * hq bytes
+    assert call(wsb=-1) == SHAPE
+    assert call(ws=None) == NULL
+    assert call(dq=None) == NULL
+    assert call(dq=ctypes.c_void_p(24)) == ALIGN
+    assert call(mq=0) == SHAPE                       # queries but no max length
+    assert lib.attn_bwd_workspace_bytes(8, 2) == 64
+    assert lib.attn_bwd_workspace_bytes(0, 2) == 0
+    g = lib.attn_bwd_dense
+    assert g(P, P, P, P, P, P, 1, 8, 8, 2, 2, 32, 0.125, 1, P, P, P, P, 1 << 20, None) == UNSUP
+    assert g(P, P, P, P, P, P, 1, 8, 8, 2, 2, 64, 0.125, 1, P, P, P, P, 63, None) == SHAPE
+    assert g(None, None, None, None, None, None, 0, 8, 8, 2, 2, 64, 0.125, 1, None, None, None,
+             None, 0, None) == OK

@@ -1,6 +1,6 @@
 """MI355X (gfx950) FlashAttention forward: thin PyTorch binding over libattnfwd.so.
 
-The four calls carry the names of the C ABI (include/attn_fwd.h).  This module
+The calls carry the names of the C ABI (include/attn_fwd.h).  This module
 only marshals arguments: it checks tensor placement and layout, allocates the
 outputs with torch.empty, and passes raw device pointers plus the current HIP
 stream to the library.  Every step of the computation runs in the library's
@@ -16,7 +16,7 @@ from typing import List, Optional, Sequence, Tuple
 from . import _lib
 
 __all__ = ["attn_fwd_varlen", "attn_fwd_dense", "attn_fwd_padded", "attn_unpad_gather",
-           "attn_pad_scatter",
+           "attn_pad_scatter", "attn_bwd_varlen", "attn_bwd_dense", "attn_bwd_workspace_bytes",
            "attn_fwd_workspace_bytes", "workspace", "abi_version", "AttnError"]
 
 AttnError = _lib.AttnError
@@ -253,3 +253,89 @@ def attn_pad_scatter(src, indices, n_rows_total: int, out_shape: Optional[Tuple[
                               row_bytes, _stream_ptr(src.device, stream))
     _lib.check("attn_pad_scatter", st)
     return out
+
+
+def attn_bwd_workspace_bytes(total_q: int, num_heads_q: int) -> int:
+    """Bytes of workspace the backward calls need (4 per query row and head)."""
+    return int(_lib.load().attn_bwd_workspace_bytes(int(total_q), int(num_heads_q)))
+
+
+def _bwd_outputs(q, k, v, dq, dk, dv, ws, total_q, hq):
+    torch = _torch()
+    if dq is None:
+        dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    if dk is None:
+        dk = torch.empty(k.shape, dtype=torch.float32, device=q.device)
+    if dv is None:
+        dv = torch.empty(v.shape, dtype=torch.float32, device=q.device)
+    for n, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if t.dtype != torch.float32 or not t.is_contiguous() or t.shape != ref.shape:
+            raise ValueError(f"{n} must be a contiguous fp32 tensor shaped like its input")
+    if ws is None:
+        ws = torch.empty(max(attn_bwd_workspace_bytes(total_q, hq), 16), dtype=torch.uint8,
+                         device=q.device)
+    return dq, dk, dv, ws
+
+
+def _check_fp32(name, t, shape):
+    torch = _torch()
+    if not t.is_cuda or t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be a contiguous fp32 GPU tensor of shape {tuple(shape)}")
+
+
+def attn_bwd_varlen(q, k, v, out, lse, dout, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int,
+                    max_seqlen_k: Optional[int] = None, scale: Optional[float] = None,
+                    causal: bool = False, dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Gradients of attn_fwd_varlen.  out / lse are that call's results for the
+    same inputs; dout (Tq, Hq, D) bf16 is the gradient of out.
+    Returns (dq, dk, dv) fp32 shaped like q, k, v."""
+    torch = _torch()
+    lib = _lib.load()
+    for n, t in (("q", q), ("k", k), ("v", v), ("dout", dout)):
+        _check_bf16(n, t)
+    if q.dim() != 3 or k.dim() != 3 or k.shape != v.shape or dout.shape != q.shape:
+        raise ValueError("q, dout must be (Tq, Hq, D) and k, v (Tk, Hkv, D)")
+    tq, hq, d = q.shape
+    tk, hkv, _ = k.shape
+    _check_fp32("out", out, q.shape)
+    _check_fp32("lse", lse, (hq, tq))
+    for n, t in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{n} must be a contiguous int32 GPU tensor")
+    if cu_seqlens_q.numel() != cu_seqlens_k.numel():
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+    if max_seqlen_k is None:
+        max_seqlen_k = max_seqlen_q
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq, dk, dv, ws = _bwd_outputs(q, k, v, dq, dk, dv, workspace, tq, hq)
+    st = lib.attn_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse),
+                             _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), cu_seqlens_q.numel() - 1,
+                             tq, tk, hq, hkv, d, int(max_seqlen_q), int(max_seqlen_k),
+                             float(scale), int(bool(causal)), _ptr(dq), _ptr(dk), _ptr(dv),
+                             *_ws_args(ws), _stream_ptr(q.device, stream))
+    _lib.check("attn_bwd_varlen", st)
+    return dq, dk, dv
+
+
+def attn_bwd_dense(q, k, v, out, lse, dout, scale: Optional[float] = None, causal: bool = False,
+                   dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Gradients of attn_fwd_dense for contiguous q, k, v (B, S, H, D) bf16.
+    Returns (dq, dk, dv) fp32 shaped like q, k, v."""
+    lib = _lib.load()
+    for n, t in (("q", q), ("k", k), ("v", v), ("dout", dout)):
+        _check_bf16(n, t)
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape or dout.shape != q.shape:
+        raise ValueError("q, dout must be (B, Sq, Hq, D) and k, v (B, Sk, Hkv, D)")
+    b, sq, hq, d = q.shape
+    _, sk, hkv, _ = k.shape
+    _check_fp32("out", out, q.shape)
+    _check_fp32("lse", lse, (b, hq, sq))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq, dk, dv, ws = _bwd_outputs(q, k, v, dq, dk, dv, workspace, b * sq, hq)
+    st = lib.attn_bwd_dense(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), b, sq,
+                            sk, hq, hkv, d, float(scale), int(bool(causal)), _ptr(dq), _ptr(dk),
+                            _ptr(dv), *_ws_args(ws), _stream_ptr(q.device, stream))
+    _lib.check("attn_bwd_dense", st)
+    return dq, dk, dv

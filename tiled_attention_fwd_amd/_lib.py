@@ -40,6 +40,15 @@ SIGNATURES = {
                                     c_int64, c_void_p]),
     "attn_pad_scatter": (c_int32, [c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int64,
                                    c_void_p]),
+    "attn_bwd_varlen": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                  c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32,
+                                  c_int32, c_int32, c_int32, c_int32, c_float, c_int32,
+                                  c_void_p, c_void_p, c_void_p, c_void_p, c_int64, c_void_p]),
+    "attn_bwd_dense": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                 c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_float,
+                                 c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_int64,
+                                 c_void_p]),
+    "attn_bwd_workspace_bytes": (c_int64, [c_int64, c_int32]),
     "attn_status_str": (ctypes.c_char_p, [c_int32]),
     "attn_abi_version": (c_int32, []),
 }

@@ -139,6 +139,31 @@ attn_status_t check_workspace(const void* ws, int64_t ws_bytes) {
   return ATTN_OK;
 }
 
+// Shared checks and launch of the two backward entry points.  `a` carries the
+// layout; rows_q is the number of query rows (packed or batch * seqlen_q).
+attn_status_t launch_bwd(AttnArgs& a, int d, bool varlen, int max_q, int max_k, int64_t rows_q,
+                         const void* dout, float* dq, float* dk, float* dv, void* ws,
+                         int64_t ws_bytes, hipStream_t stream) {
+  if (ws_bytes < rows_q * a.hq * 4) return ATTN_ERR_SHAPE;
+  a.part_lse = static_cast<float*>(ws);
+  a.n_qb = (max_q + 127) / 128;
+  const int n_kb = (max_k + 127) / 128;
+  const hipError_t e = attnfwd::launch_attention_bwd(a, d, varlen, static_cast<const uint16_t*>(dout),
+                                                     dq, dk, dv, rows_q * a.hq, n_kb, stream);
+  return e == hipSuccess ? ATTN_OK : (e == hipErrorInvalidConfiguration ? ATTN_ERR_SHAPE : ATTN_ERR_HIP);
+}
+
+attn_status_t check_bwd_ptrs(const void* q, const void* k, const void* v, const float* out,
+                             const void* dout, const float* lse, float* dq, float* dk, float* dv,
+                             void* ws) {
+  if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv || !ws) return ATTN_ERR_NULL;
+  const void* p16[] = {q, k, v, out, dout, dq, dk, dv, ws};
+  for (const void* p : p16)
+    if (!aligned16(p)) return ATTN_ERR_ALIGN;
+  if (!aligned4(lse)) return ATTN_ERR_ALIGN;
+  return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -348,6 +373,107 @@ attn_status_t attn_fwd_padded(const void* q, const void* k, const void* v,
   if (!work) return ATTN_OK;
   const int max_q = max_seqlen < n_valid ? max_seqlen : n_valid;
   return launch(a, head_dim, true, max_q, nullptr, 0, s);
+}
+
+int64_t attn_bwd_workspace_bytes(int64_t total_q, int32_t num_heads_q) {
+  if (total_q <= 0 || num_heads_q <= 0) return 0;
+  return total_q * num_heads_q * 4;
+}
+
+attn_status_t attn_bwd_varlen(const void* q, const void* k, const void* v, const float* out,
+                              const void* dout, const float* lse, const int32_t* cu_seqlens_q,
+                              const int32_t* cu_seqlens_k, int32_t num_seqs, int32_t total_q,
+                              int32_t total_k, int32_t num_heads_q, int32_t num_heads_k,
+                              int32_t head_dim, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                              float scale, int32_t causal, float* dq, float* dk, float* dv,
+                              void* workspace, int64_t workspace_bytes, void* stream) {
+  if (num_seqs < 0 || total_q < 0 || total_k < 0 || max_seqlen_q < 0 || max_seqlen_k < 0)
+    return ATTN_ERR_SHAPE;
+  attn_status_t st = check_common(num_heads_q, num_heads_k, head_dim, scale);
+  if (st != ATTN_OK) return st;
+  if (head_dim != 64 && head_dim != 128) return ATTN_ERR_UNSUPPORTED;
+  if (workspace_bytes < 0) return ATTN_ERR_SHAPE;
+  if (num_seqs == 0 || num_heads_q == 0 || (total_q == 0 && total_k == 0)) return ATTN_OK;
+  if ((total_q > 0 && max_seqlen_q == 0) || (total_k > 0 && max_seqlen_k == 0)) return ATTN_ERR_SHAPE;
+  if (cu_seqlens_q == nullptr || cu_seqlens_k == nullptr) return ATTN_ERR_NULL;
+  if (!aligned4(cu_seqlens_q) || !aligned4(cu_seqlens_k)) return ATTN_ERR_ALIGN;
+  st = check_bwd_ptrs(q, k, v, out, dout, lse, dq, dk, dv, workspace);
+  if (st != ATTN_OK) return st;
+  AttnArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = const_cast<float*>(out);
+  a.lse = const_cast<float*>(lse);
+  a.cu_q = cu_seqlens_q;
+  a.cu_k = cu_seqlens_k;
+  a.q_ss = (int64_t)num_heads_q * head_dim;
+  a.q_hs = head_dim;
+  a.k_ss = (int64_t)num_heads_k * head_dim;
+  a.k_hs = head_dim;
+  a.v_ss = a.k_ss;
+  a.v_hs = head_dim;
+  a.o_ss = a.q_ss;
+  a.o_hs = head_dim;
+  a.lse_hs = total_q;
+  a.nseq = num_seqs;
+  a.hq = num_heads_q;
+  a.hkv = num_heads_k;
+  a.group = num_heads_q / num_heads_k;
+  a.c = base2_factor(scale);
+  a.causal = causal ? 1 : 0;
+  if (!span_fits(total_q, a.q_ss) || !span_fits(total_k, a.k_ss)) return ATTN_ERR_SHAPE;
+  const int max_q = max_seqlen_q < total_q ? max_seqlen_q : total_q;
+  const int max_k = max_seqlen_k < total_k ? max_seqlen_k : total_k;
+  return launch_bwd(a, head_dim, true, max_q, max_k, total_q, dout, dq, dk, dv, workspace,
+                    workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+attn_status_t attn_bwd_dense(const void* q, const void* k, const void* v, const float* out,
+                             const void* dout, const float* lse, int32_t batch, int32_t seqlen_q,
+                             int32_t seqlen_k, int32_t num_heads_q, int32_t num_heads_k,
+                             int32_t head_dim, float scale, int32_t causal, float* dq, float* dk,
+                             float* dv, void* workspace, int64_t workspace_bytes, void* stream) {
+  if (batch < 0 || seqlen_q < 0 || seqlen_k < 0) return ATTN_ERR_SHAPE;
+  attn_status_t st = check_common(num_heads_q, num_heads_k, head_dim, scale);
+  if (st != ATTN_OK) return st;
+  if (head_dim != 64 && head_dim != 128) return ATTN_ERR_UNSUPPORTED;
+  if (workspace_bytes < 0) return ATTN_ERR_SHAPE;
+  if (batch == 0 || num_heads_q == 0 || (seqlen_q == 0 && seqlen_k == 0)) return ATTN_OK;
+  st = check_bwd_ptrs(q, k, v, out, dout, lse, dq, dk, dv, workspace);
+  if (st != ATTN_OK) return st;
+  AttnArgs a{};
+  const int64_t d = head_dim;
+  a.q_hs = d;
+  a.q_ss = num_heads_q * d;
+  a.q_bs = a.q_ss * seqlen_q;
+  a.k_hs = d;
+  a.k_ss = num_heads_k * d;
+  a.k_bs = a.k_ss * seqlen_k;
+  a.v_hs = d;
+  a.v_ss = a.k_ss;
+  a.v_bs = a.k_bs;
+  a.o_hs = d;
+  a.o_ss = a.q_ss;
+  a.o_bs = a.q_bs;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = const_cast<float*>(out);
+  a.lse = const_cast<float*>(lse);
+  a.lse_hs = seqlen_q;
+  a.lse_bs = (int64_t)num_heads_q * seqlen_q;
+  a.nseq = batch;
+  a.hq = num_heads_q;
+  a.hkv = num_heads_k;
+  a.group = num_heads_q / num_heads_k;
+  a.sq = seqlen_q;
+  a.sk = seqlen_k;
+  a.c = base2_factor(scale);
+  a.causal = causal ? 1 : 0;
+  if (!span_fits(seqlen_q, a.q_ss) || !span_fits(seqlen_k, a.k_ss)) return ATTN_ERR_SHAPE;
+  return launch_bwd(a, head_dim, false, seqlen_q, seqlen_k, (int64_t)batch * seqlen_q, dout, dq,
+                    dk, dv, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
 attn_status_t attn_unpad_gather(const void* const* src, void* const* dst, int32_t n_tensors,

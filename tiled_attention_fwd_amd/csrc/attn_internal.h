@@ -95,6 +95,15 @@ hipError_t launch_attention(const AttnArgs& a, int head_dim, bool varlen, int po
 // with n_split > 1).  bm is the query block of the policy used.
 hipError_t launch_merge(const AttnArgs& a, int head_dim, bool varlen, int bm, hipStream_t stream);
 
+// Enqueues the attention backward: D = rowsum(dO * O) into a.part_lse (laid
+// out like the LSE), then dQ, then dK / dV.  a.o is the forward output, a.lse
+// its natural-log LSE; dout has the layout of q; dq / dk / dv are fp32 with
+// the shapes of q / k / v.  n_pairs = query rows * heads, n_kb = key blocks
+// of 128 per (sequence, key head).  head_dim 64 or 128.
+hipError_t launch_attention_bwd(const AttnArgs& a, int head_dim, bool varlen, const uint16_t* dout,
+                                float* dq, float* dk, float* dv, int64_t n_pairs, int n_kb,
+                                hipStream_t stream);
+
 // Row gather of up to three tensors sharing one index list.
 hipError_t launch_gather(const void* const* src, void* const* dst, int n_tensors,
                          const int32_t* indices, int n_valid, int n_rows_src, int64_t row_bytes,
