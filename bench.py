@@ -234,6 +234,55 @@ def run_configs(torch, t, names, flush):
     return rows
 
 
+def run_backward(torch, t, names, flush):
+    """Backward (attn_bwd_*) per workload: the forward runs once for out/lse,
+    then the three backward launches are timed as one call.  FLOPs follow the
+    usual convention of 2.5x the forward (five products of the visible
+    pairs); the kernels execute seven (S and dP are recomputed in both the dQ
+    and the dK/dV pass, which keeps the passes free of atomics)."""
+    import numpy as np
+    from synth import gen
+    rows = []
+    for name in names:
+        w = gen.build_workload(name)
+        if w.d not in (64, 128) or w.kind == "padded":
+            continue
+        dev = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to("cuda").view(torch.bfloat16)
+        q, k, v = dev(w.q), dev(w.k), dev(w.v)
+        do = dev(gen.upstream_grad_bf16(w.seed, w.q.shape))
+        dq = torch.empty(w.q.shape, dtype=torch.float32, device="cuda")
+        dk = torch.empty(w.k.shape, dtype=torch.float32, device="cuda")
+        dv = torch.empty(w.v.shape, dtype=torch.float32, device="cuda")
+        if w.kind == "dense":
+            o, lse = t.attn_fwd_dense(q, k, v, scale=float(w.scale), causal=w.causal)
+            ws = torch.empty(t.attn_bwd_workspace_bytes(w.q.shape[0] * w.q.shape[1], w.hq),
+                             dtype=torch.uint8, device="cuda")
+            fn = lambda: t.attn_bwd_dense(q, k, v, o, lse, do, scale=float(w.scale),
+                                          causal=w.causal, dq=dq, dk=dk, dv=dv, workspace=ws)
+        else:
+            cq = torch.from_numpy(w.cu_seqlens_q).to("cuda")
+            ck = torch.from_numpy(w.cu_seqlens_k).to("cuda")
+            o, lse = t.attn_fwd_varlen(q, k, v, cq, ck, w.max_seqlen, scale=float(w.scale),
+                                       causal=w.causal)
+            ws = torch.empty(t.attn_bwd_workspace_bytes(w.q.shape[0], w.hq), dtype=torch.uint8,
+                             device="cuda")
+            fn = lambda: t.attn_bwd_varlen(q, k, v, o, lse, do, cq, ck, w.max_seqlen, w.max_seqlen,
+                                           scale=float(w.scale), causal=w.causal, dq=dq, dk=dk,
+                                           dv=dv, workspace=ws)
+        fl = 2.5 * attn_flops(w)
+        probe = time_calls(torch, fn, 3, 2)
+        iters = int(min(30, max(5, 0.25e6 / max(1.0, statistics.median(probe)))))
+        cold = time_calls(torch, fn, iters, 1, flush=flush)
+        med = statistics.median(cold)
+        tf = fl / (med * 1e-6) / 1e12
+        rows.append({"workload": name, "us_median_cold": round(med, 1), "gflop": round(fl / 1e9, 2),
+                     "tflops": round(tf, 1), "pct_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 1),
+                     "executed_tflops": round(tf * 7 / 5, 1)})
+        del q, k, v, o, lse, do, dq, dk, dv, ws
+        torch.cuda.empty_cache()
+    return rows
+
+
 # ------------------------------------------------------------------------- CPU baseline
 def cpu_baseline(step_workloads, budget_s=20.0):
     """The fp64 oracle on the host, for the same padded-path step."""
@@ -274,6 +323,8 @@ def main():
     ap.add_argument("--configs", default="all",
                     help="comma list of extra workloads to time per call, 'all' or 'none'")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--bwd-configs", default="varlen_1x8192,hdim_sweep_d128,hdim_sweep_d64",
+                    help="comma list of workloads whose backward is timed, or 'none'")
     ap.add_argument("--only-configs", action="store_true",
                     help="time only the per-workload rows (no step, no JSON contract line)")
     args = ap.parse_args()
@@ -295,9 +346,13 @@ def main():
 
     if args.only_configs:
         flush_buf = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
-        cfg_names = list(gen.WORKLOADS) if args.configs == "all" else args.configs.split(",")
+        cfg_names = [] if args.configs == "none" else (
+            list(gen.WORKLOADS) if args.configs == "all" else args.configs.split(","))
         for row in run_configs(torch, t, cfg_names, lambda: flush_buf.zero_()):
             print(json.dumps(row), flush=True)
+        if args.bwd_configs != "none":
+            for row in run_backward(torch, t, args.bwd_configs.split(","), lambda: flush_buf.zero_()):
+                print(json.dumps({"backward": row}), flush=True)
         return
 
     names = ["padded_32x128_random", "padded_1x2048"]
@@ -436,6 +491,12 @@ def main():
         print(f"[bench] timing {len(cfg_names)} workloads", file=sys.stderr, flush=True)
         cfg_rows = run_configs(torch, t, cfg_names, flush)
         del flush_buf
+    bwd_rows = []
+    if args.bwd_configs != "none":
+        flush_buf = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        print("[bench] timing the backward", file=sys.stderr, flush=True)
+        bwd_rows = run_backward(torch, t, args.bwd_configs.split(","), lambda: flush_buf.zero_())
+        del flush_buf
 
     cpu = None
     if not args.no_cpu:
@@ -461,6 +522,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "configs": cfg_rows,
+        "backward": bwd_rows,
         "kernel_source_hash": source_hash(),
     }
     print(json.dumps(line), flush=True)
