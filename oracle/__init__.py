@@ -14,6 +14,10 @@ the same result as the standard softmax.  The causal mask (same page, the
 paragraph on fusing the causal mask) lets each query see only keys at or before
 its own position.
 
+Attention over a paged KV cache (paged.py) reads each sequence's keys and
+values through its page table (page "why FA is 2x on A100 but 1.5x on Ascend
+910", section 5, PagedAttention) and then applies the same definition.
+
 The gradients (backward.py) follow the page's statement that the backward pass
 recomputes the forward (same page, the second pitfall) and are the exact
 chain-rule derivative of the definition above.
@@ -33,6 +37,7 @@ from .attention import (  # noqa: F401
     attention_query,
 )
 from .layout import unpad_gather, pad_scatter  # noqa: F401
+from .paged import gather_pages, attention_paged  # noqa: F401
 from .backward import (  # noqa: F401
     attention_backward_one,
     attention_backward_varlen,

@@ -193,6 +193,75 @@ def make_padded(name: str, seed: int, total_len: int, slots, h: int, d: int, cau
                     lengths_q=nz, lengths_k=list(nz))
 
 
+@dataclasses.dataclass
+class PagedWorkload:
+    """New queries against a paged KV cache.
+
+    q (Tq, Hq, D) packed by cu_seqlens_q; k_cache / v_cache (num_pages,
+    page_size, Hkv, D); sequence s's key j lives in page block_table[s, j //
+    page_size] at row j % page_size, for j < seqlens_k[s].  Pages are handed
+    out in a random order, unused table entries are -1, and every cache row no
+    sequence uses holds ``fill`` (random values, or NaN to prove it is never
+    read into a result)."""
+
+    name: str
+    causal: bool
+    hq: int
+    hkv: int
+    d: int
+    scale: np.float32
+    page_size: int
+    q: np.ndarray
+    k_cache: np.ndarray
+    v_cache: np.ndarray
+    block_table: np.ndarray
+    seqlens_k: np.ndarray
+    cu_seqlens_q: np.ndarray
+    lengths_q: List[int]
+    seed: int
+
+    @property
+    def max_seqlen_q(self) -> int:
+        return max(self.lengths_q + [0])
+
+    @property
+    def max_seqlen_k(self) -> int:
+        return int(self.seqlens_k.max()) if self.seqlens_k.size else 0
+
+
+def make_paged(name: str, seed: int, lengths_q, lengths_k, hq: int, hkv: int, d: int,
+               page_size: int, causal: bool, spare_pages: int = 3,
+               fill: Optional[float] = None) -> PagedWorkload:
+    rng = np.random.Generator(np.random.PCG64(seed))
+    lengths_q = [int(x) for x in lengths_q]
+    lengths_k = [int(x) for x in lengths_k]
+    need = [(L + page_size - 1) // page_size for L in lengths_k]
+    n_pages = sum(need) + spare_pages
+    max_pages = max(need + [1])
+    perm = rng.permutation(n_pages)
+    table = np.full((len(lengths_k), max_pages), -1, dtype=np.int32)
+    at = 0
+    for s, n in enumerate(need):
+        table[s, :n] = perm[at:at + n]
+        at += n
+    q = normal_bf16(rng, (sum(lengths_q), hq, d))
+    k_cache = normal_bf16(rng, (n_pages, page_size, hkv, d))
+    v_cache = normal_bf16(rng, (n_pages, page_size, hkv, d))
+    if fill is not None:
+        used = np.zeros((n_pages, page_size), dtype=bool)
+        for s, L in enumerate(lengths_k):
+            j = np.arange(L)
+            used[table[s, j // page_size], j % page_size] = True
+        bits = bf16_bits_from_f32(np.array([fill], dtype=np.float32))[0]
+        k_cache[~used] = bits
+        v_cache[~used] = bits
+    return PagedWorkload(name=name, causal=causal, hq=hq, hkv=hkv, d=d, scale=default_scale(d),
+                         page_size=page_size, q=q, k_cache=k_cache, v_cache=v_cache,
+                         block_table=table, seqlens_k=np.asarray(lengths_k, dtype=np.int32),
+                         cu_seqlens_q=cu_seqlens_from_lengths(lengths_q), lengths_q=lengths_q,
+                         seed=seed)
+
+
 def pack_lengths_uniform(rng: np.random.Generator, total: int, max_len: int) -> List[int]:
     """Draw L ~ U{1..max_len} until the sum reaches ``total``; trim the last to hit it exactly."""
     lens: List[int] = []
