@@ -4,8 +4,8 @@
  * The library computes O = softmax(scale * Q K^T) V per (sequence, query head)
  * without materialising the score matrix, for dense batched inputs and for
  * variable-length packed inputs, plus the row gather/scatter that moves packed
- * rows between the padded and the compact layouts, and the gradients of the
- * attention (backward by recomputation).
+ * rows between the padded and the compact layouts, attention over a paged KV
+ * cache, and the gradients of the attention (backward by recomputation).
  *
  * Sources of the operations (web pages, cited by title and section):
  *  - "Intro to FlashAttention on Ascend CANN" (ai6s.net): the standard
@@ -237,6 +237,60 @@ attn_status_t attn_fwd_padded(const void* q, const void* k, const void* v,
                               int32_t n_valid, int32_t n_rows, int32_t num_heads_q,
                               int32_t num_heads_k, int32_t head_dim, int32_t max_seqlen,
                               float scale, int32_t causal, float* out, float* lse, void* stream);
+
+/*
+ * attn_fwd_paged -- attention of new queries over a paged KV cache (decode,
+ * speculative decode, chunked prefill).
+ *
+ * Passage: page "why FA is 2x on A100 but 1.5x on Ascend 910", section 5
+ * (manage the inference KV cache with PagedAttention; inference is bound by
+ * moving K and V), with the attention of page "Intro to FlashAttention on
+ * Ascend CANN" (online softmax over key tiles; partial results over disjoint
+ * key ranges merge exactly through their log-sum-exps, "the first pitfall").
+ *
+ * q        (total_q, num_heads_q, head_dim) bf16: the new queries, packed;
+ *          sequence s owns rows [cu_seqlens_q[s], cu_seqlens_q[s+1]).
+ * k_cache, v_cache (num_pages, page_size, num_heads_k, head_dim) bf16: the
+ *          page pool.  Key j of sequence s is row j % page_size of page
+ *          block_table[s * max_pages_per_seq + j / page_size], j < seqlens_k[s].
+ *          A dense (batch, max_len, H, D) cache is the case page_size = max_len,
+ *          block_table[s] = s.
+ * seqlens_k (num_seqs) int32: keys of each sequence (the new tokens included).
+ * block_table (num_seqs, max_pages_per_seq) int32.  Page numbers outside
+ *          [0, num_pages) read as zero keys (never out of bounds); entries past
+ *          a sequence's last page are not read.
+ * causal: nonzero => query i of Lq sees keys j <= i + (Lk - Lq) (bottom-right:
+ *          the new tokens are the last Lq keys).
+ * out (total_q, num_heads_q, head_dim) fp32; lse (num_heads_q, total_q) fp32
+ *          natural log, or NULL.  A query that sees no key gets 0 and -inf.
+ * max_seqlen_q / max_seqlen_k: upper bounds on query / key counts (host);
+ *          max_seqlen_k <= max_pages_per_seq * page_size.
+ * workspace: optional (may be NULL), 16-byte aligned, at least
+ *          attn_fwd_paged_workspace_bytes(...) bytes: lets long key ranges be
+ *          split over several workgroups (one more launch merges them).  Too
+ *          small or NULL: no split.
+ * head_dim 64 or 128; page_size a positive multiple of 16; one page of one
+ * tensor (page_size * num_heads_k * head_dim * 2 bytes) under 4 GiB.
+ * GQA: the query heads of one KV head are processed together, so each K/V
+ * byte is read once per (sequence, KV head).  One or two launches on `stream`.
+ */
+attn_status_t attn_fwd_paged(const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* cu_seqlens_q, const int32_t* seqlens_k,
+                             const int32_t* block_table, int32_t num_seqs, int32_t total_q,
+                             int32_t num_pages, int32_t page_size, int32_t max_pages_per_seq,
+                             int32_t num_heads_q, int32_t num_heads_k, int32_t head_dim,
+                             int32_t max_seqlen_q, int32_t max_seqlen_k, float scale,
+                             int32_t causal, float* out, float* lse, void* workspace,
+                             int64_t workspace_bytes, void* stream);
+
+/*
+ * attn_fwd_paged_workspace_bytes -- workspace that lets attn_fwd_paged split
+ * key ranges for this shape; 0 when it would not split (or for invalid
+ * arguments).  Pure host computation.
+ */
+int64_t attn_fwd_paged_workspace_bytes(int32_t num_seqs, int32_t max_seqlen_q,
+                                       int32_t max_seqlen_k, int32_t num_heads_q,
+                                       int32_t num_heads_k, int32_t head_dim);
 
 /*
  * attn_bwd_varlen -- gradients of attn_fwd_varlen with respect to q, k and v.

@@ -17,6 +17,7 @@ from . import _lib
 
 __all__ = ["attn_fwd_varlen", "attn_fwd_dense", "attn_fwd_padded", "attn_unpad_gather",
            "attn_pad_scatter", "attn_bwd_varlen", "attn_bwd_dense", "attn_bwd_workspace_bytes",
+           "attn_fwd_paged", "attn_fwd_paged_workspace_bytes", "paged_workspace",
            "attn_fwd_workspace_bytes", "workspace", "abi_version", "AttnError"]
 
 AttnError = _lib.AttnError
@@ -339,3 +340,62 @@ def attn_bwd_dense(q, k, v, out, lse, dout, scale: Optional[float] = None, causa
                             _ptr(dv), *_ws_args(ws), _stream_ptr(q.device, stream))
     _lib.check("attn_bwd_dense", st)
     return dq, dk, dv
+
+
+def attn_fwd_paged_workspace_bytes(num_seqs: int, max_seqlen_q: int, max_seqlen_k: int,
+                                   num_heads_q: int, num_heads_k: int, head_dim: int) -> int:
+    """Bytes of workspace that let attn_fwd_paged split long key ranges (0: none)."""
+    return int(_lib.load().attn_fwd_paged_workspace_bytes(int(num_seqs), int(max_seqlen_q),
+                                                           int(max_seqlen_k), int(num_heads_q),
+                                                           int(num_heads_k), int(head_dim)))
+
+
+def paged_workspace(num_seqs: int, max_seqlen_q: int, max_seqlen_k: int, num_heads_q: int,
+                    num_heads_k: int, head_dim: int, device="cuda"):
+    """A device buffer of attn_fwd_paged_workspace_bytes, or None when none is needed."""
+    n = attn_fwd_paged_workspace_bytes(num_seqs, max_seqlen_q, max_seqlen_k, num_heads_q,
+                                       num_heads_k, head_dim)
+    if n <= 0:
+        return None
+    return _torch().empty(n, dtype=_torch().uint8, device=device)
+
+
+def attn_fwd_paged(q, k_cache, v_cache, cu_seqlens_q, seqlens_k, block_table,
+                   max_seqlen_q: int, max_seqlen_k: int, scale: Optional[float] = None,
+                   causal: bool = True, out=None, lse=None, return_lse: bool = True,
+                   workspace=None, stream=None):
+    """New queries q (Tq, Hq, D) bf16 over a paged cache k_cache / v_cache
+    (num_pages, page_size, Hkv, D) bf16 with block_table (num_seqs, max_pages)
+    and seqlens_k (num_seqs) int32.  Returns (out (Tq, Hq, D) fp32, lse (Hq, Tq)
+    fp32 or None)."""
+    torch = _torch()
+    lib = _lib.load()
+    for n, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _check_bf16(n, t)
+    if q.dim() != 3 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
+        raise ValueError("q must be (Tq, Hq, D) and the caches (num_pages, page_size, Hkv, D)")
+    for n, t in (("cu_seqlens_q", cu_seqlens_q), ("seqlens_k", seqlens_k),
+                 ("block_table", block_table)):
+        if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{n} must be a contiguous int32 GPU tensor")
+    tq, hq, d = q.shape
+    num_pages, page_size, hkv, dk = k_cache.shape
+    if dk != d:
+        raise ValueError("head_dim of q and the caches differ")
+    nseq = cu_seqlens_q.numel() - 1
+    if seqlens_k.numel() != nseq or block_table.dim() != 2 or block_table.shape[0] != nseq:
+        raise ValueError("seqlens_k must be (num_seqs,) and block_table (num_seqs, max_pages)")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((tq, hq, d), dtype=torch.float32, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty((hq, tq), dtype=torch.float32, device=q.device)
+    ws_ptr, ws_bytes = _ws_args(workspace)
+    st = lib.attn_fwd_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cu_seqlens_q),
+                            _ptr(seqlens_k), _ptr(block_table), nseq, tq, num_pages, page_size,
+                            block_table.shape[1], hq, hkv, d, int(max_seqlen_q),
+                            int(max_seqlen_k), float(scale), int(bool(causal)), _ptr(out),
+                            _ptr(lse), ws_ptr, ws_bytes, _stream_ptr(q.device, stream))
+    _lib.check("attn_fwd_paged", st)
+    return out, lse

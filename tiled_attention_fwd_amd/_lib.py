@@ -49,6 +49,12 @@ SIGNATURES = {
                                  c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_int64,
                                  c_void_p]),
     "attn_bwd_workspace_bytes": (c_int64, [c_int64, c_int32]),
+    "attn_fwd_paged": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                 c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,
+                                 c_int32, c_int32, c_int32, c_float, c_int32, c_void_p, c_void_p,
+                                 c_void_p, c_int64, c_void_p]),
+    "attn_fwd_paged_workspace_bytes": (c_int64, [c_int32, c_int32, c_int32, c_int32, c_int32,
+                                                 c_int32]),
     "attn_status_str": (ctypes.c_char_p, [c_int32]),
     "attn_abi_version": (c_int32, []),
 }

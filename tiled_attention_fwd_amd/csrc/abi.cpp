@@ -4,6 +4,7 @@
 
 #include "../../include/attn_fwd.h"
 #include "attn_internal.h"
+#include "decode_internal.h"
 
 #include <math.h>
 #include <stdlib.h>
@@ -162,6 +163,63 @@ attn_status_t check_bwd_ptrs(const void* q, const void* k, const void* v, const 
     if (!aligned16(p)) return ATTN_ERR_ALIGN;
   if (!aligned4(lse)) return ATTN_ERR_ALIGN;
   return ATTN_OK;
+}
+
+
+// ---- paged KV cache (decode_kernel.hip)
+
+// ATTN_PAGED_CHUNK_TILES=<n> forces key-range parts of n 32-key tiles (tests).
+int paged_chunk_override() {
+  const char* s = getenv("ATTN_PAGED_CHUNK_TILES");
+  if (s == nullptr || *s == '\0') return -1;
+  char* end = nullptr;
+  long v = strtol(s, &end, 10);
+  if (end == s || v < 1 || v > 1000000) return -1;
+  return (int)v;
+}
+
+// ATTN_PAGED_VARIANT=<0|1|2> picks the d=128 wave/stage layout (sweeps).
+int paged_variant() {
+  const char* s = getenv("ATTN_PAGED_VARIANT");
+  if (s == nullptr || *s < '0' || *s > '2' || s[1] != '\0') return 0;
+  return *s - '0';
+}
+
+struct PagedPlan {
+  int n_rb = 0;
+  int n_split = 1;
+  int chunk_tiles = 0;
+};
+
+// Row blocks of 32 (query, head-of-group) pairs, and the key-range split: the
+// launch has nseq * hkv * n_rb workgroups before splitting; parts are added
+// until about 1024 workgroups (4 per CU) exist, keeping at least 8 tiles
+// (2 per wave) in a part.
+PagedPlan plan_paged(int nseq, int max_q, int max_k, int group, int hkv) {
+  PagedPlan p;
+  p.n_rb = (int)(((int64_t)max_q * group + 31) / 32);
+  const int n_kt = (max_k + 31) / 32;
+  const int64_t base = (int64_t)nseq * hkv * p.n_rb;
+  if (n_kt <= 0 || base <= 0) return p;
+  int parts;
+  const int forced = paged_chunk_override();
+  if (forced > 0) {
+    parts = (n_kt + forced - 1) / forced;
+  } else {
+    const int64_t want = (1024 + base - 1) / base;
+    parts = (int)std::min<int64_t>(want, (n_kt + 7) / 8);
+    parts = std::min(parts, 64);
+  }
+  if (parts <= 1) return p;
+  p.chunk_tiles = (n_kt + parts - 1) / parts;
+  p.n_split = (n_kt + p.chunk_tiles - 1) / p.chunk_tiles;
+  if (p.n_split <= 1) p.n_split = 1;
+  return p;
+}
+
+int64_t paged_workspace_bytes(const PagedPlan& p, int nseq, int hkv, int d) {
+  if (p.n_split <= 1) return 0;
+  return (int64_t)nseq * hkv * p.n_rb * p.n_split * 32 * (int64_t)(d + 1) * 4;
 }
 
 }  // namespace
@@ -474,6 +532,85 @@ attn_status_t attn_bwd_dense(const void* q, const void* k, const void* v, const 
   if (!span_fits(seqlen_q, a.q_ss) || !span_fits(seqlen_k, a.k_ss)) return ATTN_ERR_SHAPE;
   return launch_bwd(a, head_dim, false, seqlen_q, seqlen_k, (int64_t)batch * seqlen_q, dout, dq,
                     dk, dv, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+int64_t attn_fwd_paged_workspace_bytes(int32_t num_seqs, int32_t max_seqlen_q,
+                                       int32_t max_seqlen_k, int32_t num_heads_q,
+                                       int32_t num_heads_k, int32_t head_dim) {
+  if (num_seqs <= 0 || max_seqlen_q <= 0 || max_seqlen_k <= 0 || num_heads_q <= 0 ||
+      num_heads_k <= 0 || num_heads_q % num_heads_k != 0 || (head_dim != 64 && head_dim != 128))
+    return 0;
+  const PagedPlan p = plan_paged(num_seqs, max_seqlen_q, max_seqlen_k, num_heads_q / num_heads_k,
+                                 num_heads_k);
+  return paged_workspace_bytes(p, num_seqs, num_heads_k, head_dim);
+}
+
+attn_status_t attn_fwd_paged(const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* cu_seqlens_q, const int32_t* seqlens_k,
+                             const int32_t* block_table, int32_t num_seqs, int32_t total_q,
+                             int32_t num_pages, int32_t page_size, int32_t max_pages_per_seq,
+                             int32_t num_heads_q, int32_t num_heads_k, int32_t head_dim,
+                             int32_t max_seqlen_q, int32_t max_seqlen_k, float scale,
+                             int32_t causal, float* out, float* lse, void* workspace,
+                             int64_t workspace_bytes, void* stream) {
+  if (num_seqs < 0 || total_q < 0 || num_pages < 0 || max_pages_per_seq < 0 ||
+      max_seqlen_q < 0 || max_seqlen_k < 0)
+    return ATTN_ERR_SHAPE;
+  attn_status_t st = check_common(num_heads_q, num_heads_k, head_dim, scale);
+  if (st != ATTN_OK) return st;
+  if (head_dim != 64 && head_dim != 128) return ATTN_ERR_UNSUPPORTED;
+  if (page_size < 16 || page_size % 16 != 0) return ATTN_ERR_UNSUPPORTED;
+  st = check_workspace(workspace, workspace_bytes);
+  if (st != ATTN_OK) return st;
+  if (num_seqs == 0 || total_q == 0 || num_heads_q == 0) return ATTN_OK;
+  if (max_seqlen_q == 0) return ATTN_ERR_SHAPE;
+  if ((int64_t)max_seqlen_k > (int64_t)max_pages_per_seq * page_size) return ATTN_ERR_SHAPE;
+  if (q == nullptr || out == nullptr || cu_seqlens_q == nullptr || seqlens_k == nullptr)
+    return ATTN_ERR_NULL;
+  if (max_seqlen_k > 0 && (k_cache == nullptr || v_cache == nullptr || block_table == nullptr))
+    return ATTN_ERR_NULL;
+  if (!aligned16(q) || !aligned16(out) ||
+      (max_seqlen_k > 0 && (!aligned16(k_cache) || !aligned16(v_cache))))
+    return ATTN_ERR_ALIGN;
+  if (!aligned4(cu_seqlens_q) || !aligned4(seqlens_k) || (block_table && !aligned4(block_table)) ||
+      (lse && !aligned4(lse)))
+    return ATTN_ERR_ALIGN;
+  const int64_t page_bytes = (int64_t)page_size * num_heads_k * head_dim * 2;
+  if (page_bytes >= (1LL << 32)) return ATTN_ERR_SHAPE;
+  attnfwd::DecodeArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k_cache = static_cast<const uint16_t*>(k_cache);
+  a.v_cache = static_cast<const uint16_t*>(v_cache);
+  a.block_table = block_table;
+  a.seqlens_k = seqlens_k;
+  a.cu_q = cu_seqlens_q;
+  a.o = out;
+  a.lse = lse;
+  a.nseq = num_seqs;
+  a.tq = total_q;
+  a.hq = num_heads_q;
+  a.hkv = num_heads_k;
+  a.group = num_heads_q / num_heads_k;
+  a.num_pages = num_pages;
+  a.page_size = page_size;
+  a.max_pages = max_pages_per_seq;
+  a.c = base2_factor(scale);
+  a.causal = causal ? 1 : 0;
+  const int max_q = max_seqlen_q < total_q ? max_seqlen_q : total_q;
+  const PagedPlan p = plan_paged(num_seqs, max_q, max_seqlen_k, a.group, num_heads_k);
+  a.n_rb = p.n_rb;
+  a.n_split = 1;
+  a.chunk_tiles = 0;
+  const int64_t need = paged_workspace_bytes(p, num_seqs, num_heads_k, head_dim);
+  if (need > 0 && workspace != nullptr && workspace_bytes >= need) {
+    a.n_split = p.n_split;
+    a.chunk_tiles = p.chunk_tiles;
+    a.part_o = static_cast<float*>(workspace);
+    a.part_lse = a.part_o + (int64_t)num_seqs * num_heads_k * p.n_rb * p.n_split * 32 * head_dim;
+  }
+  const hipError_t e =
+      attnfwd::launch_decode(a, head_dim, paged_variant(), static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : (e == hipErrorInvalidConfiguration ? ATTN_ERR_SHAPE : ATTN_ERR_HIP);
 }
 
 attn_status_t attn_unpad_gather(const void* const* src, void* const* dst, int32_t n_tensors,

@@ -1,0 +1,421 @@
+// Attention of new queries over a paged KV cache (decode / speculative /
+// chunked prefill), gfx950.
+//
+// Page "why FA is 2x on A100 but 1.5x on Ascend 910", section 5: inference
+// keeps the KV cache in pages handed out by a page table (PagedAttention) and
+// is limited by moving K and V, not by arithmetic.  Key j of sequence s is row
+// j % page_size of page block_table[s][j / page_size]; the new queries of s
+// (rows cu_q[s] .. cu_q[s+1] of q) attend to its seqlens_k[s] keys, causal
+// with bottom-right alignment.  The attention is the one of page "Intro to
+// FlashAttention on Ascend CANN" (online softmax over key tiles, "the first
+// pitfall"), and key ranges split over workgroups are combined from their
+// partial results and log-sum-exps, which that section's merge rule makes
+// exact.
+//
+// Design (bound by HBM: K and V of every (sequence, KV head) are read once):
+//  * The MFMA's 32 query columns hold (query, head-of-group) pairs of one KV
+//    head: row r = qi * group + g.  A decode step of a GQA model (1 query, 8
+//    heads per KV head) fills 8 columns and reads each K/V byte once for all
+//    8 heads.  More rows than 32 use further row blocks.
+//  * A workgroup owns (sequence, KV head, row block, key chunk); its waves take
+//    the chunk's 32-key tiles round-robin, each streaming its own tiles by LDS
+//    DMA into private double buffers (no workgroup barrier in the loop), with
+//    the page lookup done per DMA instruction.  Rows past the sequence's
+//    length or page read as zero through the buffer range check.
+//  * At the end the waves merge (m, l, O) through LDS; the workgroup writes the
+//    final output, or a normalised partial and its base-2 LSE when the key
+//    range is split, and decode_merge_kernel combines the parts.
+
+#include "decode_internal.h"
+#include "attn_device.h"
+
+#include <math.h>
+
+namespace attnfwd {
+namespace {
+
+constexpr int kTileKeys = 32;
+
+
+// 32-row tile fragments in the chunk-major layout (rows permuted in the block).
+template <int D>
+struct Frag32 {
+  using L = PipeLayout<D>;
+  int rd[2];
+  int tr[2];
+  __device__ __forceinline__ void init(int lane) {
+    const int l32 = lane & 31, hh = lane >> 5;
+    rd[0] = L::at(l32, hh, L::GK);
+    rd[1] = L::at(l32, 2 + hh, L::GK);
+    const int u = (lane & 15) >> 2;
+    const int vcc = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+    tr[0] = L::at(4 * hh + u, vcc, L::GK) + 8 * (lane & 1);
+    tr[1] = L::at(8 + 4 * hh + u, vcc, L::GK) + 8 * (lane & 1);
+  }
+  // rows 0..31 (LDS order), dims 16 s .. 16 s + 15
+  __device__ __forceinline__ bf16x8 row(const unsigned char* t, int s) const {
+    return *reinterpret_cast<const bf16x8*>(t + rd[s & 1] + 16 * L::R * 2 * (s & ~1));
+  }
+  // dims 32 db .. 32 db + 31 by natural rows 16 tt .. 16 tt + 15
+  __device__ __forceinline__ bf16x8 trn(const unsigned char* t, int tt, int db) const {
+    const int cst = (16 * tt / L::R) * L::GK + 16 * L::R * 4 * db;
+    const uint2 lo = ds_read_tr16(reinterpret_cast<const uint16_t*>(t + tr[0] + cst));
+    const uint2 hi = ds_read_tr16(reinterpret_cast<const uint16_t*>(t + tr[1] + cst));
+    return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+  }
+};
+
+template <int D>
+constexpr int tile32_bytes() { return (kTileKeys / PipeLayout<D>::R) * PipeLayout<D>::GK; }
+
+// Pages of one 32-key tile: its two aligned 16-key groups (the same page when
+// page_size >= 32).  A group past the sequence, past the table row or naming a
+// page outside the pool is dead: its loads get an empty buffer range, so its
+// lanes read zeros and nothing is dereferenced.
+struct TilePages {
+  const uint16_t* kbase[2];
+  const uint16_t* vbase[2];
+  uint32_t bytes[2];
+  int pstart[2];
+};
+
+template <int D>
+__device__ __forceinline__ TilePages tile_pages(const DecodeArgs& a, const int32_t* table_row,
+                                                int lk, int kvh, int t) {
+  TilePages tp;
+  const uint32_t row_bytes = (uint32_t)a.hkv * D * 2;
+  int pidx[2], page[2];
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    const int key0 = t * kTileKeys + 16 * g;
+    pidx[g] = key0 / a.page_size;
+    // both table reads are issued before either is used (clamped into the row)
+    page[g] = table_row[min(pidx[g], a.max_pages - 1)];
+  }
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    const int key0 = t * kTileKeys + 16 * g;
+    const int pg = __builtin_amdgcn_readfirstlane(page[g]);
+    const bool live = key0 < lk && pidx[g] < a.max_pages && pg >= 0 && pg < a.num_pages;
+    tp.pstart[g] = pidx[g] * a.page_size;
+    const int valid = min(a.page_size, lk - tp.pstart[g]);  // >= 1 when key0 < lk
+    const int64_t off = ((int64_t)(live ? pg : 0) * a.page_size * a.hkv + kvh) * D;
+    tp.kbase[g] = a.k_cache + off;
+    tp.vbase[g] = a.v_cache + off;
+    tp.bytes[g] = live ? (uint32_t)(valid - 1) * row_bytes + D * 2 : 0u;
+  }
+  return tp;
+}
+
+// DMA of keys 32 t .. 32 t + 31 of one (sequence, KV head) from the cache into
+// a 32-row tile at LDS byte address `tile`.  Instruction q carries tile rows
+// q R .. q R + R - 1, whose source keys (key_of_row of the row) lie in the
+// aligned 16-key group (q R) / 16, hence in one page (page_size is a multiple
+// of 16).
+template <int D>
+__device__ __forceinline__ void dma_tile(const TilePages& tp, bool is_v, int hkv, int t,
+                                         uint32_t tile, int lane) {
+  using L = PipeLayout<D>;
+  constexpr int R = L::R;
+  constexpr int NI = kTileKeys / R;
+  const int c = lane / R;
+  const uint32_t row_bytes = (uint32_t)hkv * D * 2;
+#pragma unroll
+  for (int q = 0; q < NI; ++q) {
+    const int g = (q * R) >> 4;
+    const int row = q * R + ((lane % R) ^ L::rot(c));
+    const int key = t * kTileKeys + key_of_row(row);
+    const u32x4 desc = make_desc(is_v ? tp.vbase[g] : tp.kbase[g], tp.bytes[g]);
+    const uint32_t voff = (uint32_t)(key - tp.pstart[g]) * row_bytes + (uint32_t)c * 16;
+    dma16(desc, voff, __builtin_amdgcn_readfirstlane(tile + q * L::GK));
+  }
+}
+
+template <int NI>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NI) : "memory");
+}
+
+template <int D, int WAVES, int NBUF>
+__global__ __launch_bounds__(WAVES * 64, 1) void attn_decode_kernel(const DecodeArgs a) {
+  constexpr int NDS = D / 16, NDB = D / 32;
+  constexpr int TB = tile32_bytes<D>();
+  constexpr int NI = kTileKeys / PipeLayout<D>::R;  // DMA instructions per tile per tensor
+  constexpr int WAVE_LDS = NBUF * 2 * TB;           // NBUF stages of K and V
+  constexpr int MERGE_LDS = WAVES * (32 * D + 64) * 4;
+  constexpr int LDS = WAVES * WAVE_LDS > MERGE_LDS ? WAVES * WAVE_LDS : MERGE_LDS;
+  static_assert(NBUF >= 2 && NBUF <= 4, "stage count");
+  static_assert(6 * NI <= 63, "vmcnt range");
+  __shared__ __attribute__((aligned(16))) unsigned char lds[LDS];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hh = lane >> 5;
+  int x = blockIdx.x;
+  const int part = x % a.n_split;
+  x /= a.n_split;
+  const int rb = x % a.n_rb;
+  x /= a.n_rb;
+  const int kvh = x % a.hkv;
+  const int seq = x / a.hkv;
+
+  const DecodeRange dr = decode_range(a, seq, rb);
+  if (dr.rows <= 0) return;
+  const int parts = decode_parts(a, dr.n_kt);
+  if (part >= parts) return;
+  const int t_begin = part * a.chunk_tiles;
+  const int t_end = a.n_split > 1 ? min(dr.n_kt, t_begin + a.chunk_tiles) : dr.n_kt;
+
+  // this lane's column: row r of the block -> (query, head)
+  const int r = rb * 32 + l32;
+  const bool col_ok = r < dr.rows;
+  const int qi = col_ok ? r / a.group : 0;
+  const int hq = kvh * a.group + (col_ok ? r % a.group : 0);
+  const int lim = !col_ok ? -1 : (a.causal ? min(dr.lk - 1, qi + dr.lk - dr.lq) : dr.lk - 1);
+
+  bf16x8 qf[NDS];
+  {
+    const uint16_t* qp = a.q + ((int64_t)(dr.q0 + qi) * a.hq + hq) * D + hh * 8;
+#pragma unroll
+    for (int s = 0; s < NDS; ++s)
+      qf[s] = col_ok ? as_bf16x8(ld16(qp + 16 * s)) : bf16x8{};
+  }
+
+  const int32_t* table_row = a.block_table + (int64_t)seq * a.max_pages;
+  const uint32_t my_lds = lds_addr(lds) + wave * WAVE_LDS;
+  const unsigned char* my_tiles = lds + wave * WAVE_LDS;
+  Frag32<D> fr;
+  fr.init(lane);
+
+  float m = -INFINITY, l = 0.f;
+  f32x16 oacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
+
+  auto issue = [&](int t, int buf) {
+    const uint32_t b = my_lds + buf * 2 * TB;
+    const TilePages tp = tile_pages<D>(a, table_row, dr.lk, kvh, t);
+    dma_tile<D>(tp, false, a.hkv, t, b, lane);
+    dma_tile<D>(tp, true, a.hkv, t, b + TB, lane);
+  };
+
+  // this wave's tiles: t_begin + wave + WAVES * j, j < n_mine; NBUF - 1 in flight
+  const int first = t_begin + wave;
+  const int n_mine = first < t_end ? (t_end - first + WAVES - 1) / WAVES : 0;
+#pragma unroll
+  for (int j = 0; j < NBUF - 1; ++j)
+    if (j < n_mine) issue(first + j * WAVES, j);
+  for (int j = 0; j < n_mine; ++j) {
+    const int t = first + j * WAVES;
+    const int buf = j % NBUF;
+    if (j + NBUF - 1 < n_mine) issue(t + (NBUF - 1) * WAVES, (j + NBUF - 1) % NBUF);
+    // tiles issued after tile j that may stay in flight
+    const int after = min(NBUF - 1, n_mine - 1 - j);
+    if (after >= 3) wait_vm<6 * NI>();
+    else if (after == 2) wait_vm<4 * NI>();
+    else if (after == 1) wait_vm<2 * NI>();
+    else wait_vm<0>();
+    const unsigned char* kt = my_tiles + buf * 2 * TB;
+    const unsigned char* vt = kt + TB;
+    f32x16 st = f32x16{};
+#pragma unroll
+    for (int s = 0; s < NDS; ++s)
+      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.row(kt, s), qf[s], st, 0, 0, 0);
+    // register e holds key 32 t + 16 (e / 8) + 8 hh + e % 8 for this column
+    const int kbase = t * kTileKeys + hh * 8;
+    float mt = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int key = kbase + ((e >> 3) << 4) + (e & 7);
+      const float v = key <= lim ? st[e] * a.c : -INFINITY;
+      st[e] = v;
+      mt = fmaxf(mt, v);
+    }
+    mt = half_max(mt);
+    const float mn = fmaxf(m, mt);
+    const float mu = mn == -INFINITY ? 0.f : mn;
+    const float alpha = __builtin_amdgcn_exp2f(m - mu);
+    m = mn;
+    float rs = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      st[e] = __builtin_amdgcn_exp2f(st[e] - mu);
+      rs += st[e];
+    }
+    l = l * alpha + rs;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+    bf16x8 pf[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      uint4 w;
+      w.x = pack_bf16x2(st[8 * tt + 0], st[8 * tt + 1]);
+      w.y = pack_bf16x2(st[8 * tt + 2], st[8 * tt + 3]);
+      w.z = pack_bf16x2(st[8 * tt + 4], st[8 * tt + 5]);
+      w.w = pack_bf16x2(st[8 * tt + 6], st[8 * tt + 7]);
+      pf[tt] = as_bf16x8(w);
+    }
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.trn(vt, tt, db), pf[tt], oacc[db],
+                                                           0, 0, 0);
+  }
+  l = half_sum(l);
+
+  // ---- merge the waves through LDS (the tile buffers are free after the barrier)
+  __syncthreads();
+  float* mo = reinterpret_cast<float*>(lds);  // [WAVES][32][D] then m, l [WAVES][32] each
+  float* mm = mo + WAVES * 32 * D;
+  float* ml = mm + WAVES * 32;
+  {
+    float* op = mo + (wave * 32 + l32) * D + hh * 4;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<float4*>(op + db * 32 + 8 * g) =
+            make_float4(oacc[db][4 * g], oacc[db][4 * g + 1], oacc[db][4 * g + 2], oacc[db][4 * g + 3]);
+    if (hh == 0) {
+      mm[wave * 32 + l32] = m;
+      ml[wave * 32 + l32] = l;
+    }
+  }
+  __syncthreads();
+  constexpr int CH = D / 4;  // float4 chunks per row
+  for (int i = tid; i < 32 * CH; i += WAVES * 64) {
+    const int col = i / CH, ch = i - col * CH;
+    const int rr = rb * 32 + col;
+    if (rr >= dr.rows) continue;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) mx = fmaxf(mx, mm[w * 32 + col]);
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    float lsum = 0.f;
+    if (mx != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < WAVES; ++w) {
+        const float f = __builtin_amdgcn_exp2f(mm[w * 32 + col] - mx);
+        const float4 v = *reinterpret_cast<const float4*>(mo + (w * 32 + col) * D + 4 * ch);
+        acc.x += f * v.x;
+        acc.y += f * v.y;
+        acc.z += f * v.z;
+        acc.w += f * v.w;
+        lsum += f * ml[w * 32 + col];
+      }
+    }
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    acc.x *= inv;
+    acc.y *= inv;
+    acc.z *= inv;
+    acc.w *= inv;
+    const float lse2 = lsum > 0.f ? mx + __log2f(lsum) : -INFINITY;
+    const int cq = rr / a.group;
+    const int ch_q = kvh * a.group + rr % a.group;
+    if (a.n_split > 1) {
+      const int64_t pr = (((int64_t)seq * a.hkv + kvh) * a.n_rb + rb) * a.n_split + part;
+      *reinterpret_cast<float4*>(a.part_o + (pr * 32 + col) * D + 4 * ch) = acc;
+      if (ch == 0) a.part_lse[pr * 32 + col] = lse2;
+    } else {
+      *reinterpret_cast<float4*>(a.o + ((int64_t)(dr.q0 + cq) * a.hq + ch_q) * D + 4 * ch) = acc;
+      if (ch == 0 && a.lse != nullptr)
+        a.lse[(int64_t)ch_q * a.tq + dr.q0 + cq] = lse2 == -INFINITY ? -INFINITY : lse2 * kLn2;
+    }
+  }
+}
+
+// Combines the parts of split key ranges: O = sum_p 2^(L_p - L) O_p with
+// L = log2 sum_p 2^(L_p).  One workgroup per (sequence, KV head, row block):
+// 8 threads per row, D / 8 outputs each.
+template <int D>
+__global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeArgs a) {
+  int x = blockIdx.x;
+  const int rb = x % a.n_rb;
+  x /= a.n_rb;
+  const int kvh = x % a.hkv;
+  const int seq = x / a.hkv;
+  const DecodeRange dr = decode_range(a, seq, rb);
+  const int col = threadIdx.x >> 3, sub = threadIdx.x & 7;
+  const int rr = rb * 32 + col;
+  if (dr.rows <= 0 || rr >= dr.rows) return;
+  const int parts = decode_parts(a, dr.n_kt);
+  const int64_t pr0 = (((int64_t)seq * a.hkv + kvh) * a.n_rb + rb) * a.n_split;
+  float mx = -INFINITY;
+  for (int p = 0; p < parts; ++p) mx = fmaxf(mx, a.part_lse[(pr0 + p) * 32 + col]);
+  constexpr int PER = D / 8;
+  float acc[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) acc[i] = 0.f;
+  float s = 0.f;
+  if (mx != -INFINITY) {
+    for (int p = 0; p < parts; ++p) {
+      const float f = __builtin_amdgcn_exp2f(a.part_lse[(pr0 + p) * 32 + col] - mx);
+      s += f;
+      const float* src = a.part_o + ((pr0 + p) * 32 + col) * D + sub * 4;
+#pragma unroll
+      for (int i = 0; i < PER / 4; ++i) {
+        const float4 v = *reinterpret_cast<const float4*>(src + 32 * i);
+        acc[4 * i] += f * v.x;
+        acc[4 * i + 1] += f * v.y;
+        acc[4 * i + 2] += f * v.z;
+        acc[4 * i + 3] += f * v.w;
+      }
+    }
+  }
+  const float inv = s > 0.f ? 1.f / s : 0.f;
+  const int cq = rr / a.group;
+  const int hq = kvh * a.group + rr % a.group;
+  float* dst = a.o + ((int64_t)(dr.q0 + cq) * a.hq + hq) * D + sub * 4;
+#pragma unroll
+  for (int i = 0; i < PER / 4; ++i)
+    *reinterpret_cast<float4*>(dst + 32 * i) =
+        make_float4(acc[4 * i] * inv, acc[4 * i + 1] * inv, acc[4 * i + 2] * inv, acc[4 * i + 3] * inv);
+  if (sub == 0 && a.lse != nullptr)
+    a.lse[(int64_t)hq * a.tq + dr.q0 + cq] = s > 0.f ? (mx + __log2f(s)) * kLn2 : -INFINITY;
+}
+
+// Waves per workgroup and LDS stages per wave.  One workgroup fills a CU's
+// LDS, so the product of the two is fixed by the tile size; the variants trade
+// waves (latency hiding of the softmax/MFMA work) for stages (tiles in flight
+// per wave).  d=128: 0 = 4 waves x 2 stages, 1 = 3 x 3, 2 = 2 x 4; d=64 has
+// room for 4 x 4.
+template <int D, int W, int NB>
+hipError_t launch_v(const DecodeArgs& a, int64_t grid, hipStream_t stream) {
+  hipLaunchKernelGGL((attn_decode_kernel<D, W, NB>), dim3((unsigned)grid), dim3(W * 64), 0, stream,
+                     a);
+  return hipSuccess;
+}
+
+template <int D>
+hipError_t launch_d(const DecodeArgs& a, int variant, hipStream_t stream) {
+  const int64_t grid = (int64_t)a.nseq * a.hkv * a.n_rb * a.n_split;
+  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  if (grid == 0) return hipSuccess;
+  if constexpr (D == 128) {
+    if (variant == 1) launch_v<D, 3, 3>(a, grid, stream);
+    else if (variant == 2) launch_v<D, 2, 4>(a, grid, stream);
+    else launch_v<D, 4, 2>(a, grid, stream);  // measured fastest: default
+  } else {
+    launch_v<D, 4, 4>(a, grid, stream);
+  }
+  if (a.n_split > 1) {
+    const int64_t gm = (int64_t)a.nseq * a.hkv * a.n_rb;
+    hipLaunchKernelGGL((decode_merge_kernel<D>), dim3((unsigned)gm), dim3(256), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs& a, int head_dim, int variant, hipStream_t stream) {
+  switch (head_dim) {
+    case 64: return launch_d<64>(a, variant, stream);
+    case 128: return launch_d<128>(a, variant, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace attnfwd
