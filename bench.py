@@ -283,6 +283,41 @@ def run_backward(torch, t, names, flush):
     return rows
 
 
+def run_paged(torch, t, names, flush):
+    """attn_fwd_paged per paged-cache workload (with its split workspace).
+    The bound is HBM: algorithmic bytes are K and V of every sequence read
+    once per KV head, q read once, out (fp32) and lse written once."""
+    import numpy as np
+    from synth import gen
+    rows = []
+    for name in names:
+        w = gen.build_paged(name)
+        dev = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to("cuda").view(torch.bfloat16)
+        i32 = lambda x: torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).to("cuda")
+        q, kc, vc = dev(w.q), dev(w.k_cache), dev(w.v_cache)
+        cq, sk, bt = i32(w.cu_seqlens_q), i32(w.seqlens_k), i32(w.block_table)
+        o = torch.empty(w.q.shape, dtype=torch.float32, device="cuda")
+        lse = torch.empty((w.hq, w.q.shape[0]), dtype=torch.float32, device="cuda")
+        nseq = len(w.lengths_q)
+        ws = t.paged_workspace(nseq, w.max_seqlen_q, w.max_seqlen_k, w.hq, w.hkv, w.d)
+        fn = lambda: t.attn_fwd_paged(q, kc, vc, cq, sk, bt, w.max_seqlen_q, w.max_seqlen_k,
+                                      scale=float(w.scale), causal=w.causal, out=o, lse=lse,
+                                      workspace=ws)
+        by = (int(w.seqlens_k.sum()) * w.hkv * w.d * 2 * 2 + w.q.size * 2 + w.q.size * 4
+              + w.hq * w.q.shape[0] * 4)
+        probe = time_calls(torch, fn, 3, 2)
+        iters = int(min(30, max(5, 0.25e6 / max(1.0, statistics.median(probe)))))
+        cold = time_calls(torch, fn, iters, 1, flush=flush)
+        med = statistics.median(cold)
+        gbs = by / (med * 1e-6) / 1e9
+        rows.append({"workload": name, "us_median_cold": round(med, 1), "mb": round(by / 1e6, 1),
+                     "gbs": round(gbs, 1), "pct_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 1),
+                     "split_workspace_mb": round((ws.numel() if ws is not None else 0) / 1e6, 2)})
+        del q, kc, vc, o, lse, ws, cq, sk, bt
+        torch.cuda.empty_cache()
+    return rows
+
+
 # ------------------------------------------------------------------------- CPU baseline
 def cpu_baseline(step_workloads, budget_s=20.0):
     """The fp64 oracle on the host, for the same padded-path step."""
@@ -325,6 +360,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--bwd-configs", default="varlen_1x8192,hdim_sweep_d128,hdim_sweep_d64",
                     help="comma list of workloads whose backward is timed, or 'none'")
+    ap.add_argument("--paged-configs", default="all",
+                    help="comma list of paged KV-cache workloads, 'all' or 'none'")
     ap.add_argument("--only-configs", action="store_true",
                     help="time only the per-workload rows (no step, no JSON contract line)")
     args = ap.parse_args()
@@ -353,6 +390,10 @@ def main():
         if args.bwd_configs != "none":
             for row in run_backward(torch, t, args.bwd_configs.split(","), lambda: flush_buf.zero_()):
                 print(json.dumps({"backward": row}), flush=True)
+        if args.paged_configs != "none":
+            pn = list(gen.PAGED_WORKLOADS) if args.paged_configs == "all" else args.paged_configs.split(",")
+            for row in run_paged(torch, t, pn, lambda: flush_buf.zero_()):
+                print(json.dumps({"paged": row}), flush=True)
         return
 
     names = ["padded_32x128_random", "padded_1x2048"]
@@ -497,6 +538,13 @@ def main():
         print("[bench] timing the backward", file=sys.stderr, flush=True)
         bwd_rows = run_backward(torch, t, args.bwd_configs.split(","), lambda: flush_buf.zero_())
         del flush_buf
+    paged_rows = []
+    if args.paged_configs != "none":
+        flush_buf = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        print("[bench] timing the paged KV-cache workloads", file=sys.stderr, flush=True)
+        pn = list(gen.PAGED_WORKLOADS) if args.paged_configs == "all" else args.paged_configs.split(",")
+        paged_rows = run_paged(torch, t, pn, lambda: flush_buf.zero_())
+        del flush_buf
 
     cpu = None
     if not args.no_cpu:
@@ -523,6 +571,7 @@ def main():
         "cpu_baseline": cpu,
         "configs": cfg_rows,
         "backward": bwd_rows,
+        "paged": paged_rows,
         "kernel_source_hash": source_hash(),
     }
     print(json.dumps(line), flush=True)

@@ -53,11 +53,13 @@ def bf16_bits_from_f32(x: np.ndarray) -> np.ndarray:
     inputs map to a quiet NaN with the input's sign; infinities stay infinite.
     """
     x = np.ascontiguousarray(x, dtype=np.float32)
-    bits = x.view(np.uint32).astype(np.uint64)
-    lsb = (bits >> np.uint64(16)) & np.uint64(1)
-    rounded = ((bits + np.uint64(0x7FFF) + lsb) >> np.uint64(16)).astype(np.uint32)
-    is_nan = (bits & np.uint64(0x7FFFFFFF)) > np.uint64(0x7F800000)
-    sign = ((bits >> np.uint64(16)) & np.uint64(0x8000)).astype(np.uint32)
+    bits = x.view(np.uint32)
+    lsb = (bits >> np.uint32(16)) & np.uint32(1)
+    # 32-bit sums cannot wrap for non-NaN patterns (at most 0xFF800000 + 0x8000);
+    # NaN patterns, which may wrap, are replaced below
+    rounded = (bits + (np.uint32(0x7FFF) + lsb)) >> np.uint32(16)
+    is_nan = (bits & np.uint32(0x7FFFFFFF)) > np.uint32(0x7F800000)
+    sign = (bits >> np.uint32(16)) & np.uint32(0x8000)
     out = np.where(is_nan, sign | np.uint32(0x7FC0), rounded)
     return out.astype(np.uint16).reshape(x.shape)
 
@@ -307,3 +309,34 @@ WORKLOADS: Dict[str, Callable[[str], Workload]] = {
 
 def build_workload(name: str) -> Workload:
     return WORKLOADS[name](name)
+
+
+def _decode(b, lq, lk_range, hq, hkv, d, page):
+    def build(name: str) -> PagedWorkload:
+        rng = np.random.Generator(np.random.PCG64(PAGED_SEEDS[name]))
+        lens = [int(x) for x in rng.integers(lk_range[0], lk_range[1] + 1, size=b)]
+        return make_paged(name, PAGED_SEEDS[name] + 1, [lq] * b, lens, hq, hkv, d, page, True,
+                          spare_pages=0)
+    return build
+
+
+# Paged KV-cache workloads (inference over a cache, page "why FA is 2x on A100
+# but 1.5x on Ascend 910", section 5): decode steps of a GQA model (64 query
+# heads over 8 KV heads, d=128), a long-context batch, speculative decode with
+# 4 new tokens, and an MHA d=64 batch.  Key counts are drawn per sequence.
+PAGED_SEEDS = {
+    "decode_paged_b32_gqa8": 6001,
+    "decode_paged_b8_32k": 6002,
+    "specdec_paged_b32_q4": 6003,
+    "decode_paged_b128_d64": 6004,
+}
+PAGED_WORKLOADS: Dict[str, Callable[[str], PagedWorkload]] = {
+    "decode_paged_b32_gqa8": _decode(32, 1, (4096, 8192), 64, 8, 128, 64),
+    "decode_paged_b8_32k": _decode(8, 1, (32768, 32768), 64, 8, 128, 64),
+    "specdec_paged_b32_q4": _decode(32, 4, (4096, 8192), 64, 8, 128, 64),
+    "decode_paged_b128_d64": _decode(128, 1, (1024, 2048), 32, 32, 64, 32),
+}
+
+
+def build_paged(name: str) -> PagedWorkload:
+    return PAGED_WORKLOADS[name](name)

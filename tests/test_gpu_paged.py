@@ -159,3 +159,12 @@ def test_full_size_decode_batch_sampled():
         o_ref, lse_ref = ref(sub)
         check_o(o[s:s + 1], o_ref, f"seq {s}")
         check_lse(lse[:, s:s + 1], lse_ref, f"seq {s}")
+
+
+@pytest.mark.parametrize("d,lk", [(128, 6000), (64, 9500)])
+def test_long_sequence_without_split(d, lk):
+    # no workspace: one workgroup walks the whole key range, more than 32 tiles
+    # per wave (the page numbers are fetched in batches of 32 tiles)
+    w = gen.make_paged(f"long{d}", 1900 + d, [1, 2], [lk, 700], 8, 2, d, 16, True,
+                       fill=float("nan"))
+    print(check(w, workspace=False))

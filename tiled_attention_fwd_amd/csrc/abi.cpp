@@ -178,11 +178,17 @@ int paged_chunk_override() {
   return (int)v;
 }
 
-// ATTN_PAGED_VARIANT=<0|1|2> picks the d=128 wave/stage layout (sweeps).
+// ATTN_PAGED_VARIANT=<0|1|2> picks the waves x stages layout (sweeps).
 int paged_variant() {
   const char* s = getenv("ATTN_PAGED_VARIANT");
-  if (s == nullptr || *s < '0' || *s > '2' || s[1] != '\0') return 0;
+  if (s == nullptr || *s < '0' || *s > '2' || s[1] != '\0') return -1;
   return *s - '0';
+}
+
+// ATTN_PAGED_ORDER=<0|1> picks the grid order (sweeps; default 1).
+int paged_order() {
+  const char* s = getenv("ATTN_PAGED_ORDER");
+  return (s != nullptr && s[0] == '0' && s[1] == '\0') ? 0 : 1;
 }
 
 struct PagedPlan {
@@ -596,6 +602,7 @@ attn_status_t attn_fwd_paged(const void* q, const void* k_cache, const void* v_c
   a.max_pages = max_pages_per_seq;
   a.c = base2_factor(scale);
   a.causal = causal ? 1 : 0;
+  a.order = paged_order();
   const int max_q = max_seqlen_q < total_q ? max_seqlen_q : total_q;
   const PagedPlan p = plan_paged(num_seqs, max_q, max_seqlen_k, a.group, num_heads_k);
   a.n_rb = p.n_rb;

@@ -24,6 +24,7 @@ struct DecodeArgs {
   int32_t chunk_tiles;  // 32-key tiles per part
   float c;              // scale * log2(e)
   int32_t causal;
+  int32_t order;        // grid order: 1 = KV head fastest, 0 = key part fastest
 };
 
 // Query rows and key tiles of one (sequence, row block).
@@ -54,7 +55,8 @@ __host__ __device__ inline int decode_parts(const DecodeArgs& a, int n_kt) {
   return p < 1 ? 1 : p;
 }
 
-// variant: d=128 wave/stage layout (0: 4x2, 1: 3x3, 2: 2x4); ignored for d=64.
+// variant: waves x stages per workgroup (d=128: 0 = 4x2, 1 = 3x3, 2 = 5x2;
+// d=64: 0 = 4x4, 1 = 8x2, 2 = 5x4); < 0 picks the measured default.
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, int variant, hipStream_t stream);
 
 }  // namespace attnfwd

@@ -37,36 +37,64 @@ namespace {
 constexpr int kTileKeys = 32;
 
 
-// 32-row tile fragments in the chunk-major layout (rows permuted in the block).
+// 32-row tiles, row-major with a 16-byte chunk swizzle.  DMA lanes are
+// row-major (lane i of an instruction carries row i / CPR, so each quad of
+// lanes reads one aligned 64-byte segment of a source row); the slot at
+// position p of row r holds chunk p ^ swz(r).  K rows hold key key_of_row(r)
+// (the accumulator order the P operand needs), V rows their own key.  The
+// swizzles make the K row fragments and the V transposed fragments free of
+// bank conflicts.
+template <int D>
+struct RowTile {
+  static constexpr int CPR = D / 8;        // 16-byte chunks per row
+  static constexpr int R = 64 / CPR;       // rows per DMA instruction
+  static constexpr int PITCH = 2 * D;      // bytes per row
+  static constexpr int BYTES = kTileKeys * PITCH;
+  static_assert(D == 64 || D == 128, "tile layout defined for head_dim 64 and 128");
+  static __device__ __forceinline__ int swz_k(int row) {
+    return D == 128 ? (row & 15) : ((row >> 1) & 7);
+  }
+  static __device__ __forceinline__ int swz_v(int row) {
+    return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
+  }
+};
+
 template <int D>
 struct Frag32 {
-  using L = PipeLayout<D>;
-  int rd[2];
-  int tr[2];
+  using L = RowTile<D>;
+  static constexpr int NDB = D / 32;
+  int rd_row;      // l32 * PITCH
+  int rd_x;        // swz_k(l32)
+  int hh;
+  int tr_base;     // (8 hh + u) * PITCH + 16 cc + 8 (lane & 1)
+  int tr_db[NDB];  // 64 * (db ^ (swz_v / 4)) per column block
   __device__ __forceinline__ void init(int lane) {
-    const int l32 = lane & 31, hh = lane >> 5;
-    rd[0] = L::at(l32, hh, L::GK);
-    rd[1] = L::at(l32, 2 + hh, L::GK);
+    const int l32 = lane & 31;
+    hh = lane >> 5;
+    rd_row = l32 * L::PITCH;
+    rd_x = L::swz_k(l32);
     const int u = (lane & 15) >> 2;
-    const int vcc = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-    tr[0] = L::at(4 * hh + u, vcc, L::GK) + 8 * (lane & 1);
-    tr[1] = L::at(8 + 4 * hh + u, vcc, L::GK) + 8 * (lane & 1);
+    const int cc = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+    tr_base = (8 * hh + u) * L::PITCH + 16 * cc + 8 * (lane & 1);
+    const int xs = L::swz_v(u) >> 2;  // swz_v of row 16 tt + 8 hh + 4 hi + u depends on u only
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) tr_db[db] = 64 * (db ^ xs);
   }
   // rows 0..31 (LDS order), dims 16 s .. 16 s + 15
   __device__ __forceinline__ bf16x8 row(const unsigned char* t, int s) const {
-    return *reinterpret_cast<const bf16x8*>(t + rd[s & 1] + 16 * L::R * 2 * (s & ~1));
+    return *reinterpret_cast<const bf16x8*>(t + rd_row + 16 * ((2 * s + hh) ^ rd_x));
   }
   // dims 32 db .. 32 db + 31 by natural rows 16 tt .. 16 tt + 15
   __device__ __forceinline__ bf16x8 trn(const unsigned char* t, int tt, int db) const {
-    const int cst = (16 * tt / L::R) * L::GK + 16 * L::R * 4 * db;
-    const uint2 lo = ds_read_tr16(reinterpret_cast<const uint16_t*>(t + tr[0] + cst));
-    const uint2 hi = ds_read_tr16(reinterpret_cast<const uint16_t*>(t + tr[1] + cst));
+    const unsigned char* p = t + tr_base + tr_db[db] + 16 * tt * L::PITCH;
+    const uint2 lo = ds_read_tr16(reinterpret_cast<const uint16_t*>(p));
+    const uint2 hi = ds_read_tr16(reinterpret_cast<const uint16_t*>(p + 4 * L::PITCH));
     return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
   }
 };
 
 template <int D>
-constexpr int tile32_bytes() { return (kTileKeys / PipeLayout<D>::R) * PipeLayout<D>::GK; }
+constexpr int tile32_bytes() { return RowTile<D>::BYTES; }
 
 // Pages of one 32-key tile: its two aligned 16-key groups (the same page when
 // page_size >= 32).  A group past the sequence, past the table row or naming a
@@ -79,25 +107,19 @@ struct TilePages {
   int pstart[2];
 };
 
+// page[g] is the table entry of the tile's 16-key group g (-1: none).
 template <int D>
-__device__ __forceinline__ TilePages tile_pages(const DecodeArgs& a, const int32_t* table_row,
-                                                int lk, int kvh, int t) {
+__device__ __forceinline__ TilePages tile_pages(const DecodeArgs& a, const int page[2], int lk,
+                                                int kvh, int t) {
   TilePages tp;
   const uint32_t row_bytes = (uint32_t)a.hkv * D * 2;
-  int pidx[2], page[2];
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
     const int key0 = t * kTileKeys + 16 * g;
-    pidx[g] = key0 / a.page_size;
-    // both table reads are issued before either is used (clamped into the row)
-    page[g] = table_row[min(pidx[g], a.max_pages - 1)];
-  }
-#pragma unroll
-  for (int g = 0; g < 2; ++g) {
-    const int key0 = t * kTileKeys + 16 * g;
-    const int pg = __builtin_amdgcn_readfirstlane(page[g]);
-    const bool live = key0 < lk && pidx[g] < a.max_pages && pg >= 0 && pg < a.num_pages;
-    tp.pstart[g] = pidx[g] * a.page_size;
+    const int pidx = key0 / a.page_size;
+    const int pg = page[g];
+    const bool live = key0 < lk && pidx < a.max_pages && pg >= 0 && pg < a.num_pages;
+    tp.pstart[g] = pidx * a.page_size;
     const int valid = min(a.page_size, lk - tp.pstart[g]);  // >= 1 when key0 < lk
     const int64_t off = ((int64_t)(live ? pg : 0) * a.page_size * a.hkv + kvh) * D;
     tp.kbase[g] = a.k_cache + off;
@@ -105,6 +127,20 @@ __device__ __forceinline__ TilePages tile_pages(const DecodeArgs& a, const int32
     tp.bytes[g] = live ? (uint32_t)(valid - 1) * row_bytes + D * 2 : 0u;
   }
   return tp;
+}
+
+// Table entries of the 16-key groups of up to 32 of this wave's tiles, one
+// per lane: lane i holds group i % 2 of tile j0 + i / 2 (-1 past the wave's
+// tiles, the sequence or the table row).  One vector load replaces a
+// dependent table read before every tile's DMA.
+__device__ __forceinline__ int load_pages(const DecodeArgs& a, const int32_t* table_row, int lk,
+                                          int first, int stride, int n_mine, int j0, int lane) {
+  const int jj = j0 + (lane >> 1);
+  const int key0 = (first + jj * stride) * kTileKeys + 16 * (lane & 1);
+  const int pidx = key0 / a.page_size;
+  int pg = -1;
+  if (jj < n_mine && key0 < lk && pidx < a.max_pages) pg = table_row[pidx];
+  return pg;
 }
 
 // DMA of keys 32 t .. 32 t + 31 of one (sequence, KV head) from the cache into
@@ -115,19 +151,20 @@ __device__ __forceinline__ TilePages tile_pages(const DecodeArgs& a, const int32
 template <int D>
 __device__ __forceinline__ void dma_tile(const TilePages& tp, bool is_v, int hkv, int t,
                                          uint32_t tile, int lane) {
-  using L = PipeLayout<D>;
+  using L = RowTile<D>;
   constexpr int R = L::R;
   constexpr int NI = kTileKeys / R;
-  const int c = lane / R;
+  const int p = lane % L::CPR;
   const uint32_t row_bytes = (uint32_t)hkv * D * 2;
 #pragma unroll
   for (int q = 0; q < NI; ++q) {
     const int g = (q * R) >> 4;
-    const int row = q * R + ((lane % R) ^ L::rot(c));
-    const int key = t * kTileKeys + key_of_row(row);
+    const int row = q * R + lane / L::CPR;
+    const int key = t * kTileKeys + (is_v ? row : key_of_row(row));
+    const int c = p ^ (is_v ? L::swz_v(row) : L::swz_k(row));
     const u32x4 desc = make_desc(is_v ? tp.vbase[g] : tp.kbase[g], tp.bytes[g]);
     const uint32_t voff = (uint32_t)(key - tp.pstart[g]) * row_bytes + (uint32_t)c * 16;
-    dma16(desc, voff, __builtin_amdgcn_readfirstlane(tile + q * L::GK));
+    dma16(desc, voff, __builtin_amdgcn_readfirstlane(tile + q * 1024));
   }
 }
 
@@ -140,7 +177,7 @@ template <int D, int WAVES, int NBUF>
 __global__ __launch_bounds__(WAVES * 64, 1) void attn_decode_kernel(const DecodeArgs a) {
   constexpr int NDS = D / 16, NDB = D / 32;
   constexpr int TB = tile32_bytes<D>();
-  constexpr int NI = kTileKeys / PipeLayout<D>::R;  // DMA instructions per tile per tensor
+  constexpr int NI = kTileKeys / RowTile<D>::R;     // DMA instructions per tile per tensor
   constexpr int WAVE_LDS = NBUF * 2 * TB;           // NBUF stages of K and V
   constexpr int MERGE_LDS = WAVES * (32 * D + 64) * 4;
   constexpr int LDS = WAVES * WAVE_LDS > MERGE_LDS ? WAVES * WAVE_LDS : MERGE_LDS;
@@ -151,13 +188,26 @@ __global__ __launch_bounds__(WAVES * 64, 1) void attn_decode_kernel(const Decode
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
+  // Grid order: KV head fastest (order 1: the workgroups that read the same
+  // cache rows, which interleave the heads, run together), or key part fastest
+  // (order 0).
   int x = blockIdx.x;
-  const int part = x % a.n_split;
-  x /= a.n_split;
-  const int rb = x % a.n_rb;
-  x /= a.n_rb;
-  const int kvh = x % a.hkv;
-  const int seq = x / a.hkv;
+  int part, rb, kvh, seq;
+  if (a.order == 1) {
+    kvh = x % a.hkv;
+    x /= a.hkv;
+    rb = x % a.n_rb;
+    x /= a.n_rb;
+    part = x % a.n_split;
+    seq = x / a.n_split;
+  } else {
+    part = x % a.n_split;
+    x /= a.n_split;
+    rb = x % a.n_rb;
+    x /= a.n_rb;
+    kvh = x % a.hkv;
+    seq = x / a.hkv;
+  }
 
   const DecodeRange dr = decode_range(a, seq, rb);
   if (dr.rows <= 0) return;
@@ -192,23 +242,36 @@ __global__ __launch_bounds__(WAVES * 64, 1) void attn_decode_kernel(const Decode
 #pragma unroll
   for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
 
-  auto issue = [&](int t, int buf) {
+  // this wave's tiles: t_begin + wave + WAVES * j, j < n_mine; NBUF - 1 in flight
+  const int first = t_begin + wave;
+  const int n_mine = first < t_end ? (t_end - first + WAVES - 1) / WAVES : 0;
+  int pagevec = load_pages(a, table_row, dr.lk, first, WAVES, n_mine, 0, lane);
+
+  // issues tile j of this wave into buffer buf; tiles are issued in order, so
+  // the page batch is reloaded when j crosses a multiple of 32 (a wave with
+  // more than 32 tiles pays one drained load per 32 tiles)
+  auto issue = [&](int j, int buf) {
+    if (j > 0 && (j & 31) == 0)
+      pagevec = load_pages(a, table_row, dr.lk, first, WAVES, n_mine, j, lane);
+    const int t = first + j * WAVES;
+    const int sel = 2 * (j & 31);
+    const int page[2] = {__builtin_amdgcn_readlane(pagevec, sel),
+                         __builtin_amdgcn_readlane(pagevec, sel + 1)};
     const uint32_t b = my_lds + buf * 2 * TB;
-    const TilePages tp = tile_pages<D>(a, table_row, dr.lk, kvh, t);
+    const TilePages tp = tile_pages<D>(a, page, dr.lk, kvh, t);
     dma_tile<D>(tp, false, a.hkv, t, b, lane);
     dma_tile<D>(tp, true, a.hkv, t, b + TB, lane);
   };
 
-  // this wave's tiles: t_begin + wave + WAVES * j, j < n_mine; NBUF - 1 in flight
-  const int first = t_begin + wave;
-  const int n_mine = first < t_end ? (t_end - first + WAVES - 1) / WAVES : 0;
+  // Every stage holds a tile in flight: a tile's K and V fragments are copied
+  // to registers as soon as it lands, which frees its stage for the tile
+  // NBUF ahead before any of the math runs.
 #pragma unroll
-  for (int j = 0; j < NBUF - 1; ++j)
-    if (j < n_mine) issue(first + j * WAVES, j);
+  for (int j = 0; j < NBUF; ++j)
+    if (j < n_mine) issue(j, j);
   for (int j = 0; j < n_mine; ++j) {
     const int t = first + j * WAVES;
     const int buf = j % NBUF;
-    if (j + NBUF - 1 < n_mine) issue(t + (NBUF - 1) * WAVES, (j + NBUF - 1) % NBUF);
     // tiles issued after tile j that may stay in flight
     const int after = min(NBUF - 1, n_mine - 1 - j);
     if (after >= 3) wait_vm<6 * NI>();
@@ -217,10 +280,21 @@ __global__ __launch_bounds__(WAVES * 64, 1) void attn_decode_kernel(const Decode
     else wait_vm<0>();
     const unsigned char* kt = my_tiles + buf * 2 * TB;
     const unsigned char* vt = kt + TB;
+    bf16x8 kfr[NDS], vfr[2][NDB];
+#pragma unroll
+    for (int s = 0; s < NDS; ++s) kfr[s] = fr.row(kt, s);
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) vfr[tt][db] = fr.trn(vt, tt, db);
+    if (j + NBUF < n_mine) {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the reads of this stage are done
+      issue(j + NBUF, buf);
+    }
     f32x16 st = f32x16{};
 #pragma unroll
     for (int s = 0; s < NDS; ++s)
-      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.row(kt, s), qf[s], st, 0, 0, 0);
+      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr[s], qf[s], st, 0, 0, 0);
     // register e holds key 32 t + 16 (e / 8) + 8 hh + e % 8 for this column
     const int kbase = t * kTileKeys + hh * 8;
     float mt = -INFINITY;
@@ -261,8 +335,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void attn_decode_kernel(const Decode
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.trn(vt, tt, db), pf[tt], oacc[db],
-                                                           0, 0, 0);
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[tt][db], pf[tt], oacc[db], 0, 0, 0);
   }
   l = half_sum(l);
 
@@ -377,11 +450,12 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeArgs a) {
     a.lse[(int64_t)hq * a.tq + dr.q0 + cq] = s > 0.f ? (mx + __log2f(s)) * kLn2 : -INFINITY;
 }
 
-// Waves per workgroup and LDS stages per wave.  One workgroup fills a CU's
-// LDS, so the product of the two is fixed by the tile size; the variants trade
-// waves (latency hiding of the softmax/MFMA work) for stages (tiles in flight
-// per wave).  d=128: 0 = 4 waves x 2 stages, 1 = 3 x 3, 2 = 2 x 4; d=64 has
-// room for 4 x 4.
+// Waves per workgroup and LDS stages per wave.  One workgroup fills most of a
+// CU's LDS, so the product of the two is bounded by the tile size; the
+// variants trade waves (latency hiding of the softmax/MFMA work) for stages
+// (tiles in flight per wave).  d=128 (16 KiB per stage): 0 = 4 waves x 2
+// stages, 1 = 3 x 3, 2 = 5 x 2; d=64 (8 KiB per stage): 0 = 4 x 4, 1 = 8 x 2,
+// 2 = 5 x 4.
 template <int D, int W, int NB>
 hipError_t launch_v(const DecodeArgs& a, int64_t grid, hipStream_t stream) {
   hipLaunchKernelGGL((attn_decode_kernel<D, W, NB>), dim3((unsigned)grid), dim3(W * 64), 0, stream,
@@ -394,12 +468,17 @@ hipError_t launch_d(const DecodeArgs& a, int variant, hipStream_t stream) {
   const int64_t grid = (int64_t)a.nseq * a.hkv * a.n_rb * a.n_split;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   if (grid == 0) return hipSuccess;
+  // Defaults (variant < 0) from the measured sweep: more waves beat more
+  // stages (d=128 decode: 4x2 3.8, 3x3 3.4, 5x2 4.2 TB/s; d=64: 4x4 3.4,
+  // 8x2 4.3, 5x4 3.8 TB/s).
   if constexpr (D == 128) {
-    if (variant == 1) launch_v<D, 3, 3>(a, grid, stream);
-    else if (variant == 2) launch_v<D, 2, 4>(a, grid, stream);
-    else launch_v<D, 4, 2>(a, grid, stream);  // measured fastest: default
+    if (variant == 0) launch_v<D, 4, 2>(a, grid, stream);
+    else if (variant == 1) launch_v<D, 3, 3>(a, grid, stream);
+    else launch_v<D, 5, 2>(a, grid, stream);
   } else {
-    launch_v<D, 4, 4>(a, grid, stream);
+    if (variant == 0) launch_v<D, 4, 4>(a, grid, stream);
+    else if (variant == 2) launch_v<D, 5, 4>(a, grid, stream);
+    else launch_v<D, 8, 2>(a, grid, stream);
   }
   if (a.n_split > 1) {
     const int64_t gm = (int64_t)a.nseq * a.hkv * a.n_rb;

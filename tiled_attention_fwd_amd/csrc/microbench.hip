@@ -3,7 +3,10 @@
 // rates, LDS 16-byte read bandwidth, a plain 16-byte copy kernel (its known
 // byte count calibrates the HBM traffic counters), and the MFMA rate with
 // independent VALU, exp and LDS work mixed in at 2 waves per SIMD (the
-// ceiling for the attention loop's instruction mix).
+// ceiling for the attention loop's instruction mix), and two read-only HBM
+// streams (16-byte loads into registers; LDS DMA of 1 KiB per wave
+// instruction with a few groups in flight) that bound the memory-bound
+// kernels.
 //
 // Prints one JSON object.  Every kernel only touches buffers it allocates, with
 // indices bounded by the launch shape.
@@ -12,8 +15,10 @@
 #include <stdio.h>
 #include <stdlib.h>
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+#include "attn_device.h"
+
+using attnfwd::bf16x8;
+using attnfwd::f32x16;
 
 #define CHECK(x)                                                             \
   do {                                                                       \
@@ -102,6 +107,57 @@ __global__ __launch_bounds__(256) void copy_kernel(const uint4* __restrict__ src
   long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
   long stride = (long)gridDim.x * blockDim.x;
   for (; i < n; i += stride) dst[i] = src[i];
+}
+
+// Read-only stream into registers: four independent 16-byte loads per thread
+// in flight, XOR-folded so the loads are not dead.
+__global__ __launch_bounds__(256) void read_kernel(const uint4* __restrict__ src, long n,
+                                                  unsigned* __restrict__ out) {
+  const long stride = (long)gridDim.x * blockDim.x;
+  long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  uint4 acc = make_uint4(0, 0, 0, 0);
+  for (; i + 3 * stride < n; i += 4 * stride) {
+    const uint4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
+    acc.x ^= a.x ^ b.x ^ c.x ^ d.x;
+    acc.y ^= a.y ^ b.y ^ c.y ^ d.y;
+    acc.z ^= a.z ^ b.z ^ c.z ^ d.z;
+    acc.w ^= a.w ^ b.w ^ c.w ^ d.w;
+  }
+  for (; i < n; i += stride) {
+    const uint4 a = src[i];
+    acc.x ^= a.x;
+    acc.y ^= a.y;
+    acc.z ^= a.z;
+    acc.w ^= a.w;
+  }
+  out[(long)blockIdx.x * blockDim.x + threadIdx.x] = acc.x ^ acc.y ^ acc.z ^ acc.w;
+}
+
+// Read-only stream through LDS DMA: each wave moves groups of 4 KiB (four
+// 1 KiB buffer_load ... lds instructions) into its own STAGES-deep ring and
+// keeps STAGES - 1 groups in flight.  n_groups * 4096 bytes must lie inside
+// the descriptor (the caller passes the buffer size).
+template <int STAGES>
+__global__ __launch_bounds__(256) void read_dma_kernel(const void* src, uint32_t bytes, long n_groups,
+                                                      unsigned* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds[4 * STAGES * 4096];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const attnfwd::u32x4 desc = attnfwd::make_desc(src, bytes);
+  const uint32_t base = attnfwd::lds_addr(lds) + wave * STAGES * 4096;
+  const long step = (long)gridDim.x * 4;
+  int s = 0;
+  for (long g = (long)blockIdx.x * 4 + wave; g < n_groups; g += step) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      attnfwd::dma16(desc, (uint32_t)(g * 4096 + j * 1024 + lane * 16),
+                     __builtin_amdgcn_readfirstlane(base + s * 4096 + j * 1024));
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * (STAGES - 1)) : "memory");
+    s = s + 1 == STAGES ? 0 : s + 1;
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  out[(long)blockIdx.x * blockDim.x + threadIdx.x] =
+      reinterpret_cast<const unsigned*>(lds)[threadIdx.x];
 }
 
 // Per MFMA: NV independent v_fma_f32, NX v_exp_f32, NL 16-byte LDS reads
@@ -213,13 +269,27 @@ int main(int argc, char** argv) {
   ms = time_ms([&] { hipLaunchKernelGGL(copy_kernel, dim3(cus * 16), dim3(256), 0, 0, src, dst, n); }, 10);
   const double copy_gbs = 2.0 * n * 16 / (ms * 1e-3) / 1e9;
 
+  unsigned* rout;
+  const int rblocks = cus * 8;
+  CHECK(hipMalloc(&rout, (size_t)rblocks * 256 * sizeof(unsigned)));
+  ms = time_ms([&] { hipLaunchKernelGGL(read_kernel, dim3(rblocks), dim3(256), 0, 0, src, n, rout); }, 10);
+  const double read_gbs = (double)n * 16 / (ms * 1e-3) / 1e9;
+  const long groups = n * 16 / 4096;
+  const uint32_t span = (uint32_t)(groups * 4096 < 0xffffffffL ? groups * 4096 : 0xffffffffL);
+  ms = time_ms([&] { hipLaunchKernelGGL(read_dma_kernel<4>, dim3(cus * 2), dim3(256), 0, 0, src, span, groups, rout); }, 10);
+  const double read_dma_gbs = (double)groups * 4096 / (ms * 1e-3) / 1e9;
+  ms = time_ms([&] { hipLaunchKernelGGL(read_dma_kernel<2>, dim3(cus * 4), dim3(256), 0, 0, src, span, groups, rout); }, 10);
+  const double read_dma2_gbs = (double)groups * 4096 / (ms * 1e-3) / 1e9;
+  CHECK(hipFree(rout));
+
   printf("{\"device\": \"%s\", \"cus\": %d, \"clock_mhz\": %d, "
+         "\"read_gbs\": %.1f, \"read_lds_dma_4stage_gbs\": %.1f, \"read_lds_dma_2stage_gbs\": %.1f, "
          "\"mfma_bf16_32x32x16_tflops\": %.1f, \"exp2_plus_sub_tops\": %.3f, "
          "\"exp2_tops\": %.3f, \"fma_tops\": %.3f, \"lds_read_tbs\": %.2f, "
          "\"copy_gbs\": %.1f, \"copy_bytes_each_way\": %ld, "
          "\"mfma_mix_2w_tflops\": {\"mfma_only\": %.1f, \"plus_4_fma\": %.1f, "
          "\"plus_1_exp\": %.1f, \"plus_1_lds16\": %.1f, \"plus_4_fma_1_exp_1_lds16\": %.1f}}\n",
-         prop.name, cus, prop.clockRate / 1000, mfma_tflops, exp_sub_rate, exp_rate, fma_rate,
+         prop.name, cus, prop.clockRate / 1000, read_gbs, read_dma_gbs, read_dma2_gbs, mfma_tflops, exp_sub_rate, exp_rate, fma_rate,
          lds_tbs, copy_gbs, n * 16, mix_pure, mix_v4, mix_x1, mix_l1, mix_all);
   CHECK(hipFree(src));
   CHECK(hipFree(dst));
