@@ -36,7 +36,7 @@ from .attention import (  # noqa: F401
     attention_varlen,
     attention_query,
 )
-from .layout import unpad_gather, pad_scatter  # noqa: F401
+from .layout import unpad_gather, pad_scatter, mask_to_varlen  # noqa: F401
 from .paged import gather_pages, attention_paged  # noqa: F401
 from .backward import (  # noqa: F401
     attention_backward_one,

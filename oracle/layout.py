@@ -8,6 +8,14 @@ silent: rows of the padded result that no index names hold +0.0 (the page's
 pad path runs a fill kernel before the index write, section 6).
 
 Both functions work on whole rows of bytes, so they are exact for any dtype.
+
+mask_to_varlen derives the unpad inputs from a padding mask (section 1: the
+indices name the rows that are not padding; the varlen attention on the
+compact rows needs the sequence offsets).  Reading where the page is silent:
+the padded tensor is B slots of L rows, a nonzero mask byte marks a valid row,
+each slot's valid rows (in row order) form one sequence, indices list the valid
+rows in row-major order, cu_seqlens are the running sums of the per-slot
+counts (empty slots give empty sequences), and max_seqlen is the largest count.
 """
 
 from __future__ import annotations
@@ -44,3 +52,14 @@ def pad_scatter(src: np.ndarray, indices: np.ndarray, n_rows_total: int) -> np.n
     for r, idx in enumerate(np.asarray(indices, dtype=np.int64)):
         out[idx] = rows[r]
     return out.reshape((n_rows_total,) + tuple(row_shape))
+
+
+def mask_to_varlen(mask: np.ndarray):
+    """mask (B, L), nonzero = valid row.  Returns (indices int32 (n_valid,),
+    cu_seqlens int32 (B + 1,), max_seqlen int)."""
+    m = np.asarray(mask) != 0
+    indices = np.flatnonzero(m.reshape(-1)).astype(np.int32)
+    counts = m.sum(axis=1).astype(np.int64)
+    cu = np.zeros(m.shape[0] + 1, dtype=np.int64)
+    np.cumsum(counts, out=cu[1:])
+    return indices, cu.astype(np.int32), int(counts.max()) if counts.size else 0
