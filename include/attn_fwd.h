@@ -187,6 +187,30 @@ attn_status_t attn_unpad_gather(const void* const* src, void* const* dst, int32_
                                 int64_t row_bytes, void* stream);
 
 /*
+ * attn_mask_to_varlen -- the unpad inputs from a padding mask, on the device.
+ *
+ * Passage: page "Lesson 5: IAW model FA2 vs FA3 measured", section 1 (unpad
+ * gathers the non-padding rows named by indices; the varlen attention takes
+ * the packing offsets).
+ *
+ * mask (batch, seqlen) bytes, device: the padded tensor's rows as `batch`
+ *      slots of `seqlen` rows; nonzero = valid row.  Slot b's valid rows (in
+ *      row order) form sequence b; an all-padding slot is an empty sequence.
+ * indices (device int32, capacity batch * seqlen): the valid rows b * seqlen +
+ *      i in increasing order; only the first n_valid entries are written.
+ * cu_seqlens (device int32, batch + 1): cu_seqlens[b] = valid rows in slots
+ *      0..b-1.
+ * stats (device int32, 2): {n_valid, max_seqlen}.  Read them back (one small
+ *      copy) when the host needs the sizes; seqlen is always a valid
+ *      max_seqlen bound for the attention calls.
+ * Three launches on `stream`; nothing is allocated.  batch * seqlen < 2^31.
+ * The results equal those of the oracle's definition exactly (integer work).
+ */
+attn_status_t attn_mask_to_varlen(const void* mask, int32_t batch, int32_t seqlen,
+                                  int32_t* indices, int32_t* cu_seqlens, int32_t* stats,
+                                  void* stream);
+
+/*
  * attn_pad_scatter -- put compact rows back into the padded layout.
  *
  * Passage: page "Lesson 5: IAW model FA2 vs FA3 measured", section 1 (pad:

@@ -18,6 +18,7 @@ from . import _lib
 __all__ = ["attn_fwd_varlen", "attn_fwd_dense", "attn_fwd_padded", "attn_unpad_gather",
            "attn_pad_scatter", "attn_bwd_varlen", "attn_bwd_dense", "attn_bwd_workspace_bytes",
            "attn_fwd_paged", "attn_fwd_paged_workspace_bytes", "paged_workspace",
+           "attn_mask_to_varlen",
            "attn_fwd_workspace_bytes", "workspace", "abi_version", "AttnError"]
 
 AttnError = _lib.AttnError
@@ -399,3 +400,26 @@ def attn_fwd_paged(q, k_cache, v_cache, cu_seqlens_q, seqlens_k, block_table,
                             _ptr(lse), ws_ptr, ws_bytes, _stream_ptr(q.device, stream))
     _lib.check("attn_fwd_paged", st)
     return out, lse
+
+
+def attn_mask_to_varlen(mask, stream=None):
+    """mask (B, L) bool/uint8/int8 GPU tensor, nonzero = valid row.  Returns
+    (indices (B*L,) int32 whose first n_valid entries are the valid rows,
+    cu_seqlens (B+1,) int32, stats (2,) int32 = [n_valid, max_seqlen]), all on
+    the GPU; nothing is synchronised."""
+    torch = _torch()
+    lib = _lib.load()
+    if not mask.is_cuda or mask.dim() != 2 or not mask.is_contiguous():
+        raise ValueError("mask must be a contiguous 2-D GPU tensor")
+    if mask.dtype == torch.bool:
+        mask = mask.view(torch.uint8)
+    if mask.element_size() != 1:
+        raise ValueError("mask must hold bytes (bool, uint8 or int8)")
+    b, l = mask.shape
+    indices = torch.empty(max(b * l, 1), dtype=torch.int32, device=mask.device)
+    cu = torch.empty(b + 1, dtype=torch.int32, device=mask.device)
+    stats = torch.empty(2, dtype=torch.int32, device=mask.device)
+    st = lib.attn_mask_to_varlen(_ptr(mask), b, l, _ptr(indices), _ptr(cu), _ptr(stats),
+                                 _stream_ptr(mask.device, stream))
+    _lib.check("attn_mask_to_varlen", st)
+    return indices, cu, stats

@@ -55,6 +55,8 @@ SIGNATURES = {
                                  c_void_p, c_int64, c_void_p]),
     "attn_fwd_paged_workspace_bytes": (c_int64, [c_int32, c_int32, c_int32, c_int32, c_int32,
                                                  c_int32]),
+    "attn_mask_to_varlen": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p,
+                                      c_void_p]),
     "attn_status_str": (ctypes.c_char_p, [c_int32]),
     "attn_abi_version": (c_int32, []),
 }

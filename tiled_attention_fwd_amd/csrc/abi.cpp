@@ -620,6 +620,21 @@ attn_status_t attn_fwd_paged(const void* q, const void* k_cache, const void* v_c
   return e == hipSuccess ? ATTN_OK : (e == hipErrorInvalidConfiguration ? ATTN_ERR_SHAPE : ATTN_ERR_HIP);
 }
 
+attn_status_t attn_mask_to_varlen(const void* mask, int32_t batch, int32_t seqlen,
+                                  int32_t* indices, int32_t* cu_seqlens, int32_t* stats,
+                                  void* stream) {
+  if (batch < 0 || seqlen < 0) return ATTN_ERR_SHAPE;
+  if ((int64_t)batch * seqlen >= (1LL << 31)) return ATTN_ERR_SHAPE;
+  if (cu_seqlens == nullptr || stats == nullptr) return ATTN_ERR_NULL;
+  if (batch > 0 && seqlen > 0 && (mask == nullptr || indices == nullptr)) return ATTN_ERR_NULL;
+  if (!aligned4(cu_seqlens) || !aligned4(stats) || (indices && !aligned4(indices)))
+    return ATTN_ERR_ALIGN;
+  const hipError_t e = attnfwd::launch_mask_to_varlen(
+      static_cast<const uint8_t*>(mask), batch, seqlen, indices, cu_seqlens, stats,
+      static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
 attn_status_t attn_unpad_gather(const void* const* src, void* const* dst, int32_t n_tensors,
                                 const int32_t* indices, int32_t n_valid, int32_t n_rows_src,
                                 int64_t row_bytes, void* stream) {

@@ -114,4 +114,10 @@ hipError_t launch_gather(const void* const* src, void* const* dst, int n_tensors
 hipError_t launch_scatter(const void* src, void* dst, const int32_t* indices, int n_valid,
                           int n_rows_total, int64_t row_bytes, hipStream_t stream);
 
+// Padding mask (B slots x L rows, nonzero = valid) -> indices of the valid
+// rows in row-major order, cu_seqlens (B + 1) and stats = {n_valid,
+// max_seqlen}.  indices must hold B * L entries.
+hipError_t launch_mask_to_varlen(const uint8_t* mask, int B, int L, int32_t* indices,
+                                 int32_t* cu_seqlens, int32_t* stats, hipStream_t stream);
+
 }  // namespace attnfwd

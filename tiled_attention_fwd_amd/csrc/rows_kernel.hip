@@ -127,6 +127,98 @@ __global__ __launch_bounds__(kThreads) void scatter_rows_kernel(
   }
 }
 
+// ---- padding mask -> (indices, cu_seqlens, n_valid, max_seqlen)
+//
+// Page "Lesson 5: IAW model FA2 vs FA3 measured", section 1: unpad gathers
+// the non-padding rows named by `indices`, and the varlen attention needs the
+// sequence offsets.  The padded tensor is B slots of L rows; a nonzero mask
+// byte marks a valid row; slot b's valid rows form sequence b.  Three small
+// launches: per-slot counts, one scan, per-slot index writes in row order.
+
+__global__ __launch_bounds__(256) void mask_count_kernel(const uint8_t* __restrict__ mask, int L,
+                                                         int32_t* __restrict__ cu) {
+  __shared__ int part[4];
+  const uint8_t* row = mask + (int64_t)blockIdx.x * L;
+  int n = 0;
+  for (int i = threadIdx.x; i < L; i += 256) n += row[i] != 0;
+  for (int off = 32; off > 0; off >>= 1) n += __shfl_xor(n, off);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = n;
+  __syncthreads();
+  if (threadIdx.x == 0) cu[blockIdx.x + 1] = part[0] + part[1] + part[2] + part[3];
+}
+
+// In-place running sums of cu[1..B] (the counts), cu[0] = 0, and
+// stats = {n_valid, max count}.  One workgroup of 1024 threads.
+__global__ __launch_bounds__(1024) void mask_scan_kernel(int32_t* __restrict__ cu, int B,
+                                                         int32_t* __restrict__ stats) {
+  __shared__ int wsum[16];
+  __shared__ int wmax[16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int carry = 0, mx = 0;
+  for (int base = 0; base < B; base += 1024) {
+    const int i = base + tid;
+    const int v = i < B ? cu[i + 1] : 0;
+    mx = max(mx, v);
+    int x = v;
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(x, off);
+      if (lane >= off) x += y;
+    }
+    if (lane == 63) wsum[wave] = x;
+    __syncthreads();
+    if (wave == 0) {
+      int w = lane < 16 ? wsum[lane] : 0;
+      for (int off = 1; off < 16; off <<= 1) {
+        const int y = __shfl_up(w, off);
+        if (lane >= off) w += y;
+      }
+      if (lane < 16) wsum[lane] = w;
+    }
+    __syncthreads();
+    if (i < B) cu[i + 1] = carry + (wave > 0 ? wsum[wave - 1] : 0) + x;
+    carry += wsum[15];
+    __syncthreads();
+  }
+  for (int off = 32; off > 0; off >>= 1) mx = max(mx, __shfl_xor(mx, off));
+  if (lane == 0) wmax[wave] = mx;
+  __syncthreads();
+  if (tid == 0) {
+    int m = 0;
+    for (int w = 0; w < 16; ++w) m = max(m, wmax[w]);
+    cu[0] = 0;
+    stats[0] = carry;
+    stats[1] = m;
+  }
+}
+
+__global__ __launch_bounds__(256) void mask_index_kernel(const uint8_t* __restrict__ mask, int L,
+                                                         const int32_t* __restrict__ cu,
+                                                         int32_t* __restrict__ indices) {
+  __shared__ int wcnt[4];
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint8_t* row = mask + (int64_t)b * L;
+  const int out0 = cu[b];
+  int carry = 0;
+  for (int c0 = 0; c0 < L; c0 += 256) {
+    const int i = c0 + tid;
+    const bool v = i < L && row[i] != 0;
+    const uint64_t bal = __ballot(v);
+    const int before = __popcll(bal & ((1ull << lane) - 1ull));
+    if (lane == 0) wcnt[wave] = __popcll(bal);
+    __syncthreads();
+    int pre = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int c = wcnt[w];
+      pre += w < wave ? c : 0;
+      tot += c;
+    }
+    if (v) indices[out0 + carry + pre + before] = b * L + i;
+    carry += tot;
+    __syncthreads();
+  }
+}
+
 }  // namespace
 
 hipError_t launch_gather(const void* const* src, void* const* dst, int n_tensors,
@@ -156,6 +248,20 @@ hipError_t launch_scatter(const void* src, void* dst, const int32_t* indices, in
   hipLaunchKernelGGL(scatter_rows_kernel, dim3(blocks), dim3(kThreads), 0, stream,
                      static_cast<const uint4*>(src), static_cast<uint4*>(dst), indices, n_valid,
                      n_rows_total, cpr);
+  return hipGetLastError();
+}
+
+}  // namespace attnfwd
+
+namespace attnfwd {
+
+hipError_t launch_mask_to_varlen(const uint8_t* mask, int B, int L, int32_t* indices,
+                                 int32_t* cu_seqlens, int32_t* stats, hipStream_t stream) {
+  if (B > 0)  // L == 0 is fine: every count is 0
+    hipLaunchKernelGGL(mask_count_kernel, dim3(B), dim3(256), 0, stream, mask, L, cu_seqlens);
+  hipLaunchKernelGGL(mask_scan_kernel, dim3(1), dim3(1024), 0, stream, cu_seqlens, B, stats);
+  if (B > 0)
+    hipLaunchKernelGGL(mask_index_kernel, dim3(B), dim3(256), 0, stream, mask, L, cu_seqlens, indices);
   return hipGetLastError();
 }
 
