@@ -18,6 +18,9 @@ Attention over a paged KV cache (paged.py) reads each sequence's keys and
 values through its page table (page "why FA is 2x on A100 but 1.5x on Ascend
 910", section 5, PagedAttention) and then applies the same definition.
 
+Attention on fp8 inputs (fp8.py) decodes OCP E4M3 bytes with per-tensor
+factors and applies the same definition.
+
 The gradients (backward.py) follow the page's statement that the backward pass
 recomputes the forward (same page, the second pitfall) and are the exact
 chain-rule derivative of the definition above.
@@ -38,6 +41,7 @@ from .attention import (  # noqa: F401
 )
 from .layout import unpad_gather, pad_scatter, mask_to_varlen  # noqa: F401
 from .paged import gather_pages, attention_paged  # noqa: F401
+from .fp8 import e4m3_to_f64, attention_fp8_varlen, attention_fp8_dense  # noqa: F401
 from .backward import (  # noqa: F401
     attention_backward_one,
     attention_backward_varlen,

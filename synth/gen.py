@@ -75,6 +75,61 @@ def upstream_grad_bf16(seed: int, shape) -> np.ndarray:
     return normal_bf16(np.random.Generator(np.random.PCG64(seed + 7_000_000)), shape)
 
 
+def e4m3_bytes_from_f32(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to OCP E4M3 bytes (round to nearest even) with
+    torch's CPU cast; inputs must lie within +-448."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def normal_e4m3(rng: np.random.Generator, shape, sigma: float = 1.0) -> np.ndarray:
+    """N(0, sigma^2) float32 draws in C order, rounded to E4M3 bytes."""
+    return e4m3_bytes_from_f32(rng.standard_normal(size=shape, dtype=np.float32) * np.float32(sigma))
+
+
+@dataclasses.dataclass
+class Fp8Workload:
+    """fp8 (E4M3) attention inputs with per-tensor dequantisation factors."""
+
+    name: str
+    causal: bool
+    hq: int
+    hkv: int
+    d: int
+    scale: np.float32
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    q_scale: np.float32
+    k_scale: np.float32
+    v_scale: np.float32
+    cu_seqlens_q: np.ndarray
+    cu_seqlens_k: np.ndarray
+    lengths_q: List[int]
+    lengths_k: List[int]
+    max_seqlen: int
+    seed: int
+
+
+def make_fp8_varlen(name: str, seed: int, lengths_q, hq: int, hkv: int, d: int, causal: bool,
+                    lengths_k=None, factors=(1.0, 1.0, 1.0)) -> "Fp8Workload":
+    """Packed fp8 inputs; the stored bytes are N(0,1) draws divided by each
+    tensor's factor, so dequantised values are N(0,1)-like."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    lengths_q = [int(x) for x in lengths_q]
+    lengths_k = list(lengths_q) if lengths_k is None else [int(x) for x in lengths_k]
+    fq, fk, fv = (np.float32(f) for f in factors)
+    q = normal_e4m3(rng, (sum(lengths_q), hq, d), 1.0 / float(fq))
+    k = normal_e4m3(rng, (sum(lengths_k), hkv, d), 1.0 / float(fk))
+    v = normal_e4m3(rng, (sum(lengths_k), hkv, d), 1.0 / float(fv))
+    return Fp8Workload(name=name, causal=causal, hq=hq, hkv=hkv, d=d, scale=default_scale(d),
+                       q=q, k=k, v=v, q_scale=fq, k_scale=fk, v_scale=fv,
+                       cu_seqlens_q=cu_seqlens_from_lengths(lengths_q),
+                       cu_seqlens_k=cu_seqlens_from_lengths(lengths_k), lengths_q=lengths_q,
+                       lengths_k=lengths_k, max_seqlen=max(lengths_q + lengths_k + [0]), seed=seed)
+
+
 def cu_seqlens_from_lengths(lengths) -> np.ndarray:
     """Packing offsets [0, L0, L0+L1, ...] as int32."""
     lens = np.asarray(lengths, dtype=np.int64)
