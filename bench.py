@@ -34,6 +34,7 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["tiled_attention_fwd_amd/csrc/attn_device.h",
                   "tiled_attention_fwd_amd/csrc/attn_kernel.hip",
@@ -318,6 +319,34 @@ def run_paged(torch, t, names, flush):
     return rows
 
 
+def run_fp8(torch, t, names, flush):
+    """attn_fwd_fp8_varlen per fp8 workload (cold cache); FLOPs as for bf16."""
+    import numpy as np
+    from synth import gen
+    rows = []
+    for name in names:
+        w = gen.build_fp8(name)
+        u8 = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to("cuda")
+        q, k, v = u8(w.q), u8(w.k), u8(w.v)
+        cq, ck = u8(w.cu_seqlens_q), u8(w.cu_seqlens_k)
+        o = torch.empty(w.q.shape, dtype=torch.float32, device="cuda")
+        lse = torch.empty((w.hq, w.q.shape[0]), dtype=torch.float32, device="cuda")
+        fn = lambda: t.attn_fwd_fp8_varlen(q, k, v, cq, ck, w.max_seqlen, scale=float(w.scale),
+                                           causal=w.causal, out=o, lse=lse)
+        fl = 4.0 * w.d * w.hq * visible_pairs(w.lengths_q, w.lengths_k, w.causal)
+        probe = time_calls(torch, fn, 3, 2)
+        iters = int(min(30, max(5, 0.25e6 / max(1.0, statistics.median(probe)))))
+        cold = time_calls(torch, fn, iters, 1, flush=flush)
+        med = statistics.median(cold)
+        tf = fl / (med * 1e-6) / 1e12
+        rows.append({"workload": name, "us_median_cold": round(med, 1), "gflop": round(fl / 1e9, 2),
+                     "tflops": round(tf, 1), "pct_fp8_peak": round(100 * tf / PEAK_FP8_TFLOPS, 1),
+                     "pct_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 1)})
+        del q, k, v, o, lse
+        torch.cuda.empty_cache()
+    return rows
+
+
 # ------------------------------------------------------------------------- CPU baseline
 def cpu_baseline(step_workloads, budget_s=20.0):
     """The fp64 oracle on the host, for the same padded-path step."""
@@ -362,6 +391,8 @@ def main():
                     help="comma list of workloads whose backward is timed, or 'none'")
     ap.add_argument("--paged-configs", default="all",
                     help="comma list of paged KV-cache workloads, 'all' or 'none'")
+    ap.add_argument("--fp8-configs", default="all",
+                    help="comma list of fp8 workloads, 'all' or 'none'")
     ap.add_argument("--only-configs", action="store_true",
                     help="time only the per-workload rows (no step, no JSON contract line)")
     args = ap.parse_args()
@@ -394,6 +425,10 @@ def main():
             pn = list(gen.PAGED_WORKLOADS) if args.paged_configs == "all" else args.paged_configs.split(",")
             for row in run_paged(torch, t, pn, lambda: flush_buf.zero_()):
                 print(json.dumps({"paged": row}), flush=True)
+        if args.fp8_configs != "none":
+            fn_ = list(gen.FP8_WORKLOADS) if args.fp8_configs == "all" else args.fp8_configs.split(",")
+            for row in run_fp8(torch, t, fn_, lambda: flush_buf.zero_()):
+                print(json.dumps({"fp8": row}), flush=True)
         return
 
     names = ["padded_32x128_random", "padded_1x2048"]
@@ -545,6 +580,13 @@ def main():
         pn = list(gen.PAGED_WORKLOADS) if args.paged_configs == "all" else args.paged_configs.split(",")
         paged_rows = run_paged(torch, t, pn, lambda: flush_buf.zero_())
         del flush_buf
+    fp8_rows = []
+    if args.fp8_configs != "none":
+        flush_buf = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        print("[bench] timing the fp8 workloads", file=sys.stderr, flush=True)
+        fn_ = list(gen.FP8_WORKLOADS) if args.fp8_configs == "all" else args.fp8_configs.split(",")
+        fp8_rows = run_fp8(torch, t, fn_, lambda: flush_buf.zero_())
+        del flush_buf
 
     cpu = None
     if not args.no_cpu:
@@ -572,6 +614,7 @@ def main():
         "configs": cfg_rows,
         "backward": bwd_rows,
         "paged": paged_rows,
+        "fp8": fp8_rows,
         "kernel_source_hash": source_hash(),
     }
     print(json.dumps(line), flush=True)

@@ -317,6 +317,45 @@ int64_t attn_fwd_paged_workspace_bytes(int32_t num_seqs, int32_t max_seqlen_q,
                                        int32_t num_heads_k, int32_t head_dim);
 
 /*
+ * attn_fwd_fp8_varlen -- attention on fp8 (OCP E4M3) inputs, packed layout.
+ *
+ * Passage: the pages name FP8 only as FA-3's direction (page "Lesson 5: IAW
+ * model FA2 vs FA3 measured", closing note) and narrower data as a way to halve
+ * the bytes moved (page "why FA is 2x on A100 but 1.5x on Ascend 910", section
+ * 5); the computation is the attention of attn_fwd_varlen on the dequantised
+ * values q_scale * q, k_scale * k, v_scale * v.
+ *
+ * q (total_q, num_heads_q, head_dim), k, v (total_k, num_heads_k, head_dim):
+ *      E4M3 bytes (1 sign, 4 exponent bits with bias 7, 3 mantissa bits;
+ *      S.1111.111 is NaN), row-major, contiguous.
+ * q_scale, k_scale, v_scale: the per-tensor dequantisation factors (> 0,
+ *      finite).  Everything else (cu_seqlens, max_seqlen, scale, causal, out,
+ *      lse, GQA, alignment) as in attn_fwd_varlen.
+ * Precision: the scores and the row sums are exact products in fp32; the
+ * probabilities enter the P*V product as E4M3 (after scaling by 2^8), so the
+ * output carries their rounding (at most 2^-4 relative per probability).
+ * head_dim 64 or 128 (else ATTN_ERR_UNSUPPORTED).  One launch.
+ */
+attn_status_t attn_fwd_fp8_varlen(const void* q, const void* k, const void* v,
+                                  const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                  int32_t num_seqs, int32_t total_q, int32_t total_k,
+                                  int32_t num_heads_q, int32_t num_heads_k, int32_t head_dim,
+                                  int32_t max_seqlen, float scale, float q_scale, float k_scale,
+                                  float v_scale, int32_t causal, float* out, float* lse,
+                                  void* stream);
+
+/*
+ * attn_fwd_fp8_dense -- attention on fp8 inputs, dense (batch, seqlen, heads,
+ * head_dim) contiguous layout; out (B, Sq, Hq, D) fp32, lse (B, Hq, Sq) fp32.
+ * Rules as for attn_fwd_fp8_varlen.
+ */
+attn_status_t attn_fwd_fp8_dense(const void* q, const void* k, const void* v, int32_t batch,
+                                 int32_t seqlen_q, int32_t seqlen_k, int32_t num_heads_q,
+                                 int32_t num_heads_k, int32_t head_dim, float scale,
+                                 float q_scale, float k_scale, float v_scale, int32_t causal,
+                                 float* out, float* lse, void* stream);
+
+/*
  * attn_bwd_varlen -- gradients of attn_fwd_varlen with respect to q, k and v.
  *
  * Passage: page "Intro to FlashAttention on Ascend CANN", section on the

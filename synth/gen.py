@@ -395,3 +395,16 @@ PAGED_WORKLOADS: Dict[str, Callable[[str], PagedWorkload]] = {
 
 def build_paged(name: str) -> PagedWorkload:
     return PAGED_WORKLOADS[name](name)
+
+
+# fp8 (E4M3) versions of the d=128 prefill workloads, plus a non-causal batch.
+FP8_SEEDS = {"fp8_hdim128_s4096": 7001, "fp8_varlen_1x8192": 7002, "fp8_b4_s4096_full": 7003}
+FP8_WORKLOADS: Dict[str, Callable[[str], "Fp8Workload"]] = {
+    "fp8_hdim128_s4096": lambda n: make_fp8_varlen(n, FP8_SEEDS[n], [4096], 32, 32, 128, True),
+    "fp8_varlen_1x8192": lambda n: make_fp8_varlen(n, FP8_SEEDS[n], [8192], 16, 16, 128, True),
+    "fp8_b4_s4096_full": lambda n: make_fp8_varlen(n, FP8_SEEDS[n], [4096] * 4, 16, 16, 128, False),
+}
+
+
+def build_fp8(name: str) -> "Fp8Workload":
+    return FP8_WORKLOADS[name](name)

@@ -18,7 +18,7 @@ from . import _lib
 __all__ = ["attn_fwd_varlen", "attn_fwd_dense", "attn_fwd_padded", "attn_unpad_gather",
            "attn_pad_scatter", "attn_bwd_varlen", "attn_bwd_dense", "attn_bwd_workspace_bytes",
            "attn_fwd_paged", "attn_fwd_paged_workspace_bytes", "paged_workspace",
-           "attn_mask_to_varlen",
+           "attn_mask_to_varlen", "attn_fwd_fp8_varlen", "attn_fwd_fp8_dense",
            "attn_fwd_workspace_bytes", "workspace", "abi_version", "AttnError"]
 
 AttnError = _lib.AttnError
@@ -423,3 +423,67 @@ def attn_mask_to_varlen(mask, stream=None):
                                  _stream_ptr(mask.device, stream))
     _lib.check("attn_mask_to_varlen", st)
     return indices, cu, stats
+
+
+def _check_u8(name, t):
+    torch = _torch()
+    if not t.is_cuda or t.element_size() != 1 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous GPU tensor of E4M3 bytes "
+                         "(uint8 or float8_e4m3fn)")
+    if t.dtype not in (torch.uint8, torch.int8, getattr(torch, "float8_e4m3fn", torch.uint8)):
+        raise ValueError(f"{name} must hold E4M3 bytes")
+
+
+def attn_fwd_fp8_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen: int,
+                        scale: Optional[float] = None, q_scale: float = 1.0, k_scale: float = 1.0,
+                        v_scale: float = 1.0, causal: bool = False, out=None, lse=None,
+                        return_lse: bool = True, stream=None):
+    """Packed attention on E4M3 bytes q (Tq, Hq, D), k/v (Tk, Hkv, D) with
+    per-tensor factors.  Returns (out fp32, lse (Hq, Tq) fp32 or None)."""
+    torch = _torch()
+    lib = _lib.load()
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _check_u8(n, t)
+    if q.dim() != 3 or k.dim() != 3 or k.shape != v.shape or q.shape[2] != k.shape[2]:
+        raise ValueError("q must be (Tq, Hq, D) and k, v (Tk, Hkv, D)")
+    tq, hq, d = q.shape
+    tk, hkv, _ = k.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((tq, hq, d), dtype=torch.float32, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty((hq, tq), dtype=torch.float32, device=q.device)
+    st = lib.attn_fwd_fp8_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+                                 cu_seqlens_q.numel() - 1, tq, tk, hq, hkv, d, int(max_seqlen),
+                                 float(scale), float(q_scale), float(k_scale), float(v_scale),
+                                 int(bool(causal)), _ptr(out), _ptr(lse),
+                                 _stream_ptr(q.device, stream))
+    _lib.check("attn_fwd_fp8_varlen", st)
+    return out, lse
+
+
+def attn_fwd_fp8_dense(q, k, v, scale: Optional[float] = None, q_scale: float = 1.0,
+                       k_scale: float = 1.0, v_scale: float = 1.0, causal: bool = False, out=None,
+                       lse=None, return_lse: bool = True, stream=None):
+    """Dense attention on E4M3 bytes q (B, Sq, Hq, D), k/v (B, Sk, Hkv, D),
+    contiguous.  Returns (out (B, Sq, Hq, D) fp32, lse (B, Hq, Sq) fp32 or None)."""
+    torch = _torch()
+    lib = _lib.load()
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _check_u8(n, t)
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape or q.shape[3] != k.shape[3]:
+        raise ValueError("q must be (B, Sq, Hq, D) and k, v (B, Sk, Hkv, D)")
+    b, sq, hq, d = q.shape
+    _, sk, hkv, _ = k.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((b, sq, hq, d), dtype=torch.float32, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty((b, hq, sq), dtype=torch.float32, device=q.device)
+    st = lib.attn_fwd_fp8_dense(_ptr(q), _ptr(k), _ptr(v), b, sq, sk, hq, hkv, d, float(scale),
+                                float(q_scale), float(k_scale), float(v_scale), int(bool(causal)),
+                                _ptr(out), _ptr(lse), _stream_ptr(q.device, stream))
+    _lib.check("attn_fwd_fp8_dense", st)
+    return out, lse

@@ -57,6 +57,13 @@ SIGNATURES = {
                                                  c_int32]),
     "attn_mask_to_varlen": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p,
                                       c_void_p]),
+    "attn_fwd_fp8_varlen": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32,
+                                      c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,
+                                      c_float, c_float, c_float, c_float, c_int32, c_void_p,
+                                      c_void_p, c_void_p]),
+    "attn_fwd_fp8_dense": (c_int32, [c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32,
+                                     c_int32, c_int32, c_int32, c_float, c_float, c_float, c_float,
+                                     c_int32, c_void_p, c_void_p, c_void_p]),
     "attn_status_str": (ctypes.c_char_p, [c_int32]),
     "attn_abi_version": (c_int32, []),
 }

@@ -228,6 +228,24 @@ int64_t paged_workspace_bytes(const PagedPlan& p, int nseq, int hkv, int d) {
   return (int64_t)nseq * hkv * p.n_rb * p.n_split * 32 * (int64_t)(d + 1) * 4;
 }
 
+
+attn_status_t check_fp8(int32_t hq, int32_t hkv, int32_t d, float scale, float qs, float ks,
+                        float vs) {
+  attn_status_t st = check_common(hq, hkv, d, scale);
+  if (st != ATTN_OK) return st;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  for (float f : {qs, ks, vs})
+    if (!(f > 0.f) || !isfinite(f)) return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+attn_status_t launch_fp8(AttnArgs& a, int d, bool varlen, int max_q, float scale, float qs,
+                         float ks, float vs, hipStream_t stream) {
+  a.c = (float)((double)scale * qs * ks * 1.4426950408889634074);
+  a.n_qb = (max_q + 127) / 128;
+  const hipError_t e = attnfwd::launch_attention_fp8(a, d, varlen, vs, stream);
+  return e == hipSuccess ? ATTN_OK : (e == hipErrorInvalidConfiguration ? ATTN_ERR_SHAPE : ATTN_ERR_HIP);
+}
 }  // namespace
 
 extern "C" {
@@ -633,6 +651,98 @@ attn_status_t attn_mask_to_varlen(const void* mask, int32_t batch, int32_t seqle
       static_cast<const uint8_t*>(mask), batch, seqlen, indices, cu_seqlens, stats,
       static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+attn_status_t attn_fwd_fp8_varlen(const void* q, const void* k, const void* v,
+                                  const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                  int32_t num_seqs, int32_t total_q, int32_t total_k,
+                                  int32_t num_heads_q, int32_t num_heads_k, int32_t head_dim,
+                                  int32_t max_seqlen, float scale, float q_scale, float k_scale,
+                                  float v_scale, int32_t causal, float* out, float* lse,
+                                  void* stream) {
+  if (num_seqs < 0 || total_q < 0 || total_k < 0 || max_seqlen < 0) return ATTN_ERR_SHAPE;
+  attn_status_t st = check_fp8(num_heads_q, num_heads_k, head_dim, scale, q_scale, k_scale, v_scale);
+  if (st != ATTN_OK) return st;
+  if (num_seqs == 0 || total_q == 0 || num_heads_q == 0) return ATTN_OK;
+  if (max_seqlen == 0) return ATTN_ERR_SHAPE;
+  if (q == nullptr || out == nullptr || cu_seqlens_q == nullptr || cu_seqlens_k == nullptr)
+    return ATTN_ERR_NULL;
+  if (total_k > 0 && (k == nullptr || v == nullptr)) return ATTN_ERR_NULL;
+  if (!aligned16(q) || !aligned16(out) || (total_k > 0 && (!aligned16(k) || !aligned16(v))))
+    return ATTN_ERR_ALIGN;
+  if (!aligned4(cu_seqlens_q) || !aligned4(cu_seqlens_k) || (lse && !aligned4(lse)))
+    return ATTN_ERR_ALIGN;
+  AttnArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = out;
+  a.lse = lse;
+  a.cu_q = cu_seqlens_q;
+  a.cu_k = cu_seqlens_k;
+  a.q_ss = (int64_t)num_heads_q * head_dim;  // bytes
+  a.q_hs = head_dim;
+  a.k_ss = (int64_t)num_heads_k * head_dim;
+  a.k_hs = head_dim;
+  a.v_ss = a.k_ss;
+  a.v_hs = head_dim;
+  a.o_ss = (int64_t)num_heads_q * head_dim;  // fp32 elements
+  a.o_hs = head_dim;
+  a.lse_hs = total_q;
+  a.nseq = num_seqs;
+  a.hq = num_heads_q;
+  a.hkv = num_heads_k;
+  a.group = num_heads_q / num_heads_k;
+  a.causal = causal ? 1 : 0;
+  if ((int64_t)total_q * a.q_ss >= (1LL << 32) || (int64_t)total_k * a.k_ss >= (1LL << 32))
+    return ATTN_ERR_SHAPE;
+  const int max_q = max_seqlen < total_q ? max_seqlen : total_q;
+  return launch_fp8(a, head_dim, true, max_q, scale, q_scale, k_scale, v_scale,
+                    static_cast<hipStream_t>(stream));
+}
+
+attn_status_t attn_fwd_fp8_dense(const void* q, const void* k, const void* v, int32_t batch,
+                                 int32_t seqlen_q, int32_t seqlen_k, int32_t num_heads_q,
+                                 int32_t num_heads_k, int32_t head_dim, float scale,
+                                 float q_scale, float k_scale, float v_scale, int32_t causal,
+                                 float* out, float* lse, void* stream) {
+  if (batch < 0 || seqlen_q < 0 || seqlen_k < 0) return ATTN_ERR_SHAPE;
+  attn_status_t st = check_fp8(num_heads_q, num_heads_k, head_dim, scale, q_scale, k_scale, v_scale);
+  if (st != ATTN_OK) return st;
+  if (batch == 0 || seqlen_q == 0 || num_heads_q == 0) return ATTN_OK;
+  if (q == nullptr || out == nullptr) return ATTN_ERR_NULL;
+  if (seqlen_k > 0 && (k == nullptr || v == nullptr)) return ATTN_ERR_NULL;
+  if (!aligned16(q) || !aligned16(out) || (seqlen_k > 0 && (!aligned16(k) || !aligned16(v))))
+    return ATTN_ERR_ALIGN;
+  if (lse && !aligned4(lse)) return ATTN_ERR_ALIGN;
+  AttnArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = out;
+  a.lse = lse;
+  a.q_hs = head_dim;
+  a.q_ss = (int64_t)num_heads_q * head_dim;
+  a.k_hs = head_dim;
+  a.k_ss = (int64_t)num_heads_k * head_dim;
+  a.v_hs = head_dim;
+  a.v_ss = a.k_ss;
+  a.o_hs = head_dim;
+  a.o_ss = (int64_t)num_heads_q * head_dim;
+  a.o_bs = a.o_ss * seqlen_q;
+  a.lse_hs = seqlen_q;
+  a.lse_bs = (int64_t)num_heads_q * seqlen_q;
+  a.nseq = batch;
+  a.hq = num_heads_q;
+  a.hkv = num_heads_k;
+  a.group = num_heads_q / num_heads_k;
+  a.sq = seqlen_q;
+  a.sk = seqlen_k;
+  a.causal = causal ? 1 : 0;
+  if ((int64_t)seqlen_q * a.q_ss >= (1LL << 32) || (int64_t)seqlen_k * a.k_ss >= (1LL << 32))
+    return ATTN_ERR_SHAPE;
+  return launch_fp8(a, head_dim, false, seqlen_q, scale, q_scale, k_scale, v_scale,
+                    static_cast<hipStream_t>(stream));
 }
 
 attn_status_t attn_unpad_gather(const void* const* src, void* const* dst, int32_t n_tensors,

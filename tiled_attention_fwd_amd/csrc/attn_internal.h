@@ -114,6 +114,11 @@ hipError_t launch_gather(const void* const* src, void* const* dst, int n_tensors
 hipError_t launch_scatter(const void* src, void* dst, const int32_t* indices, int n_valid,
                           int n_rows_total, int64_t row_bytes, hipStream_t stream);
 
+// fp8 (E4M3) attention: q/k/v hold bytes (strides in bytes), a.c includes the
+// q and k factors, o_mul = the v factor.  head_dim 64 or 128; BM 128.
+hipError_t launch_attention_fp8(const AttnArgs& a, int head_dim, bool varlen, float o_mul,
+                                hipStream_t stream);
+
 // Padding mask (B slots x L rows, nonzero = valid) -> indices of the valid
 // rows in row-major order, cu_seqlens (B + 1) and stats = {n_valid,
 // max_seqlen}.  indices must hold B * L entries.
