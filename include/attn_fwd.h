@@ -30,6 +30,13 @@
  *    error nothing is launched and the status says why.  Device-side faults (for
  *    example cu_seqlens that do not match the tensors) surface at the caller's
  *    next synchronisation; the preconditions below say what must hold.
+ *  - Debug mode: with the environment variable ATTN_FWD_DEBUG set (to anything
+ *    but "0"), every call that takes device-resident metadata first checks it
+ *    on the device (cu_seqlens start at 0, never decrease, end at the total,
+ *    lengths within max_seqlen; indices strictly increasing and, where
+ *    required, in range; seqlens_k within max_seqlen_k), synchronises the
+ *    stream, and returns ATTN_ERR_SHAPE without launching the work if a check
+ *    fails.
  *  - Zero work (no sequences, no rows, zero-length tensors) returns ATTN_OK
  *    without launching.
  *  - No exception crosses the ABI.  The library keeps no per-call state; calls

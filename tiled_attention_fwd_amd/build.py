@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libattnfwd.so")
 MICROBENCH = os.path.join(PKG, "microbench")  # bench-only executable (unit rates, copy bandwidth)
-SOURCES = ["attn_kernel.hip", "attn_bwd.hip", "decode_kernel.hip", "fp8_kernel.hip", "rows_kernel.hip", "abi.cpp"]
+SOURCES = ["attn_kernel.hip", "attn_bwd.hip", "decode_kernel.hip", "fp8_kernel.hip", "rows_kernel.hip", "debug_checks.hip", "abi.cpp"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 VALU ops.

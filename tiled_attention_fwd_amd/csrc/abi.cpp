@@ -10,6 +10,7 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#include <initializer_list>
 
 using attnfwd::AttnArgs;
 using attnfwd::TilePolicy;
@@ -246,6 +247,64 @@ attn_status_t launch_fp8(AttnArgs& a, int d, bool varlen, int max_q, float scale
   const hipError_t e = attnfwd::launch_attention_fp8(a, d, varlen, vs, stream);
   return e == hipSuccess ? ATTN_OK : (e == hipErrorInvalidConfiguration ? ATTN_ERR_SHAPE : ATTN_ERR_HIP);
 }
+
+// ATTN_FWD_DEBUG=1 (any value but 0) checks the device-resident preconditions
+// (cu_seqlens, indices, seqlens_k) with small kernels before the real work and
+// returns ATTN_ERR_SHAPE when one fails; this mode synchronises the stream.
+bool debug_mode() {
+  const char* s = getenv("ATTN_FWD_DEBUG");
+  return s != nullptr && *s != '\0' && !(s[0] == '0' && s[1] == '\0');
+}
+
+struct DebugCheck {
+  const int32_t* cu = nullptr;  // cu-style offsets: n + 1 entries
+  int n = -1, total = 0, max_len = -1;
+  const int32_t* lens = nullptr;  // per-sequence lengths: n_lens entries
+  int n_lens = 0, lens_max = 0;
+  const int32_t* idx = nullptr;  // indices: n_idx entries
+  int n_idx = 0, idx_rows = -1;
+};
+
+attn_status_t run_debug(std::initializer_list<DebugCheck> checks, hipStream_t s) {
+  if (!debug_mode()) return ATTN_OK;
+  if (attnfwd::debug_reset(s) != hipSuccess) return ATTN_ERR_HIP;
+  for (const DebugCheck& c : checks) {
+    if (c.cu && attnfwd::debug_check_cu(c.cu, c.n, c.total, c.max_len, s) != hipSuccess)
+      return ATTN_ERR_HIP;
+    if (c.lens && attnfwd::debug_check_lens(c.lens, c.n_lens, c.lens_max, s) != hipSuccess)
+      return ATTN_ERR_HIP;
+    if (c.idx && attnfwd::debug_check_indices(c.idx, c.n_idx, c.idx_rows, s) != hipSuccess)
+      return ATTN_ERR_HIP;
+  }
+  const int st = attnfwd::debug_status(s);
+  return st == 0 ? ATTN_OK : (st < 0 ? ATTN_ERR_HIP : ATTN_ERR_SHAPE);
+}
+
+DebugCheck cu_check(const int32_t* cu, int n, int total, int max_len) {
+  DebugCheck c;
+  c.cu = cu;
+  c.n = n;
+  c.total = total;
+  c.max_len = max_len;
+  return c;
+}
+
+DebugCheck idx_check(const int32_t* idx, int n, int rows) {
+  DebugCheck c;
+  c.idx = idx;
+  c.n_idx = n;
+  c.idx_rows = rows;
+  return c;
+}
+
+DebugCheck lens_check(const int32_t* lens, int n, int max_len) {
+  DebugCheck c;
+  c.lens = lens;
+  c.n_lens = n;
+  c.lens_max = max_len;
+  return c;
+}
+
 }  // namespace
 
 extern "C" {
@@ -296,6 +355,10 @@ attn_status_t attn_fwd_varlen_ws(const void* q, const void* k, const void* v,
   a.c = base2_factor(scale);
   a.causal = causal ? 1 : 0;
   if (!span_fits(total_q, a.q_ss) || !span_fits(total_k, a.k_ss)) return ATTN_ERR_SHAPE;
+  st = run_debug({cu_check(cu_seqlens_q, num_seqs, total_q, max_seqlen),
+                  cu_check(cu_seqlens_k, num_seqs, total_k, -1)},
+                 static_cast<hipStream_t>(stream));
+  if (st != ATTN_OK) return st;
   const int max_q = max_seqlen < total_q ? max_seqlen : total_q;
   return launch(a, head_dim, true, max_q, workspace, workspace_bytes,
                 static_cast<hipStream_t>(stream));
@@ -447,6 +510,13 @@ attn_status_t attn_fwd_padded(const void* q, const void* k, const void* v,
   a.c = base2_factor(scale);
   a.causal = causal ? 1 : 0;
   if (!span_fits(n_rows, a.q_ss) || !span_fits(n_rows, a.k_ss)) return ATTN_ERR_SHAPE;
+  if (n_valid > 0) {
+    const attn_status_t dst_ = run_debug(
+        {idx_check(indices, n_valid, n_rows),
+         cu_check(cu_seqlens, work ? num_seqs : -1, n_valid, max_seqlen)},
+        static_cast<hipStream_t>(stream));
+    if (dst_ != ATTN_OK) return dst_;
+  }
   // padding rows: +0.0, one pass; the attention writes every indexed row
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (attnfwd::launch_scatter(nullptr, out, indices, n_valid, n_rows, out_row_bytes, s) !=
@@ -505,6 +575,10 @@ attn_status_t attn_bwd_varlen(const void* q, const void* k, const void* v, const
   a.c = base2_factor(scale);
   a.causal = causal ? 1 : 0;
   if (!span_fits(total_q, a.q_ss) || !span_fits(total_k, a.k_ss)) return ATTN_ERR_SHAPE;
+  st = run_debug({cu_check(cu_seqlens_q, num_seqs, total_q, max_seqlen_q),
+                  cu_check(cu_seqlens_k, num_seqs, total_k, max_seqlen_k)},
+                 static_cast<hipStream_t>(stream));
+  if (st != ATTN_OK) return st;
   const int max_q = max_seqlen_q < total_q ? max_seqlen_q : total_q;
   const int max_k = max_seqlen_k < total_k ? max_seqlen_k : total_k;
   return launch_bwd(a, head_dim, true, max_q, max_k, total_q, dout, dq, dk, dv, workspace,
@@ -621,6 +695,12 @@ attn_status_t attn_fwd_paged(const void* q, const void* k_cache, const void* v_c
   a.c = base2_factor(scale);
   a.causal = causal ? 1 : 0;
   a.order = paged_order();
+  {
+    const attn_status_t dst_ = run_debug({cu_check(cu_seqlens_q, num_seqs, total_q, max_seqlen_q),
+                                          lens_check(seqlens_k, num_seqs, max_seqlen_k)},
+                                         static_cast<hipStream_t>(stream));
+    if (dst_ != ATTN_OK) return dst_;
+  }
   const int max_q = max_seqlen_q < total_q ? max_seqlen_q : total_q;
   const PagedPlan p = plan_paged(num_seqs, max_q, max_seqlen_k, a.group, num_heads_k);
   a.n_rb = p.n_rb;
@@ -696,6 +776,10 @@ attn_status_t attn_fwd_fp8_varlen(const void* q, const void* k, const void* v,
   a.causal = causal ? 1 : 0;
   if ((int64_t)total_q * a.q_ss >= (1LL << 32) || (int64_t)total_k * a.k_ss >= (1LL << 32))
     return ATTN_ERR_SHAPE;
+  st = run_debug({cu_check(cu_seqlens_q, num_seqs, total_q, max_seqlen),
+                  cu_check(cu_seqlens_k, num_seqs, total_k, -1)},
+                 static_cast<hipStream_t>(stream));
+  if (st != ATTN_OK) return st;
   const int max_q = max_seqlen < total_q ? max_seqlen : total_q;
   return launch_fp8(a, head_dim, true, max_q, scale, q_scale, k_scale, v_scale,
                     static_cast<hipStream_t>(stream));
@@ -775,6 +859,11 @@ attn_status_t attn_pad_scatter(const void* src, void* dst, const int32_t* indice
   if (!aligned16(dst) || (n_valid > 0 && (!aligned16(src) || !aligned4(indices))))
     return ATTN_ERR_ALIGN;
   if ((int64_t)n_rows_total * (row_bytes / 16) >= (1LL << 31)) return ATTN_ERR_SHAPE;
+  if (n_valid > 0) {
+    const attn_status_t dst_ =
+        run_debug({idx_check(indices, n_valid, -1)}, static_cast<hipStream_t>(stream));
+    if (dst_ != ATTN_OK) return dst_;
+  }
   hipError_t e = attnfwd::launch_scatter(src, dst, indices, n_valid, n_rows_total, row_bytes,
                                          static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;

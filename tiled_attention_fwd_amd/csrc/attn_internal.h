@@ -119,6 +119,15 @@ hipError_t launch_scatter(const void* src, void* dst, const int32_t* indices, in
 hipError_t launch_attention_fp8(const AttnArgs& a, int head_dim, bool varlen, float o_mul,
                                 hipStream_t stream);
 
+// Debug-mode checks of device-resident preconditions (debug_checks.hip).  The
+// checks OR bits into one device status word; debug_status synchronises the
+// stream and reads it (0 = consistent, -1 = HIP error).
+hipError_t debug_reset(hipStream_t s);
+hipError_t debug_check_cu(const int32_t* cu, int n, int total, int max_len, hipStream_t s);
+hipError_t debug_check_lens(const int32_t* lens, int n, int max_len, hipStream_t s);
+hipError_t debug_check_indices(const int32_t* idx, int n, int n_rows, hipStream_t s);
+int debug_status(hipStream_t s);
+
 // Padding mask (B slots x L rows, nonzero = valid) -> indices of the valid
 // rows in row-major order, cu_seqlens (B + 1) and stats = {n_valid,
 // max_seqlen}.  indices must hold B * L entries.
