@@ -27,6 +27,7 @@
 #include "attn_device.h"
 
 #include <math.h>
+#include <stdlib.h>
 
 namespace attnfwd {
 namespace {
@@ -285,9 +286,13 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(const AttnArgs a, c
 // dK, dV: 4 waves x 32 keys; Q/dO tiles of 64 queries in two LDS buffers,
 // walked for every query head of the group.
 // ---------------------------------------------------------------------------
-template <int D, bool VARLEN>
-__global__ __launch_bounds__(256, D >= 128 ? 1 : 2) void attn_bwd_dkdv_kernel(
-    const AttnArgs a, const uint16_t* dout, float* dk, float* dv, int n_kb) {
+// MODE 0: dK and dV together; 1: dV only (S and P^T dO); 2: dK only (S, dP
+// and Q^T dS).  The split modes hold fewer registers per wave, so more waves
+// share a SIMD, at the price of computing S in both.
+template <int D, bool VARLEN, int MODE>
+__global__ __launch_bounds__(256, MODE == 1 ? 3 : (MODE == 2 ? 2 : (D >= 128 ? 1 : 2)))
+void attn_bwd_dkdv_kernel(const AttnArgs a, const uint16_t* dout, float* dk, float* dv, int n_kb) {
+  constexpr bool DO_DK = MODE != 1, DO_DV = MODE != 2;
   constexpr int BKEYS = 128, BQ = 64;
   constexpr int NDS = D / 16, NDB = D / 32;
   constexpr int TB = tile_bytes<D>();
@@ -337,10 +342,13 @@ __global__ __launch_bounds__(256, D >= 128 ? 1 : 2) void attn_bwd_dkdv_kernel(
 #pragma unroll
     for (int s = 0; s < NDS; ++s) {
       u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(krs, (int)(kb_ + 32 * s), 0, 0);
-      u32x4 y = __builtin_amdgcn_raw_buffer_load_b128(vrs, (int)(vb_ + 32 * s), 0, 0);
-      asm volatile("" : "+v"(x), "+v"(y));
+      asm volatile("" : "+v"(x));
       kf[s] = __builtin_bit_cast(bf16x8, x);
-      vf[s] = __builtin_bit_cast(bf16x8, y);
+      if constexpr (DO_DK) {
+        u32x4 y = __builtin_amdgcn_raw_buffer_load_b128(vrs, (int)(vb_ + 32 * s), 0, 0);
+        asm volatile("" : "+v"(y));
+        vf[s] = __builtin_bit_cast(bf16x8, y);
+      }
     }
   }
 
@@ -415,9 +423,15 @@ __global__ __launch_bounds__(256, D >= 128 ? 1 : 2) void attn_bwd_dkdv_kernel(
 #pragma unroll
       for (int s = 0; s < NDS; ++s) {
         s_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.row(qt, blk, s), kf[s], s_acc, 0, 0, 0);
-        p_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.row(dt, blk, s), vf[s], p_acc, 0, 0, 0);
+        if constexpr (DO_DK)
+          p_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.row(dt, blk, s), vf[s], p_acc, 0, 0, 0);
       }
-      // register r = 8 tt + e holds query iq0 + 32 blk + 16 tt + 8 hh + e
+      // register r = 8 tt + e holds query iq0 + 32 blk + 16 tt + 8 hh + e.
+      // Only the causal test needs evaluating, and only on tiles that cross
+      // the diagonal: queries past the sequence (and rows with no visible key)
+      // carry LSE = +inf, so their P is 0; a key past the sequence only feeds
+      // its own dK/dV column, which is never stored.
+      const bool diag = a.causal && (kw0 + 31 > iq0 + 32 * blk + off);
       bf16x8 pf[2], dsf[2];
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
@@ -433,32 +447,37 @@ __global__ __launch_bounds__(256, D >= 128 ? 1 : 2) void attn_bwd_dkdv_kernel(
         for (int e = 0; e < 8; ++e) {
           const int r = 8 * tt + e;
           const int i = iq0 + qi + e;
-          float x = s_acc[r] * a.c - lz[e];
-          const bool vis = key < lk && i < lq && (!a.causal || key <= i + off);
-          if (!vis) x = -INFINITY;
+          float x = fmaf(s_acc[r], a.c, -lz[e]);
+          if (diag && key > i + off) x = -INFINITY;
           pv[e] = __builtin_amdgcn_exp2f(x);
-          dsv[e] = pv[e] * (p_acc[r] - dz[e]);
+          if constexpr (DO_DK) dsv[e] = pv[e] * (p_acc[r] - dz[e]);
         }
         uint4 w;
-        w.x = pack_bf16x2(pv[0], pv[1]);
-        w.y = pack_bf16x2(pv[2], pv[3]);
-        w.z = pack_bf16x2(pv[4], pv[5]);
-        w.w = pack_bf16x2(pv[6], pv[7]);
-        pf[tt] = as_bf16x8(w);
-        w.x = pack_bf16x2(dsv[0], dsv[1]);
-        w.y = pack_bf16x2(dsv[2], dsv[3]);
-        w.z = pack_bf16x2(dsv[4], dsv[5]);
-        w.w = pack_bf16x2(dsv[6], dsv[7]);
-        dsf[tt] = as_bf16x8(w);
+        if constexpr (DO_DV) {
+          w.x = pack_bf16x2(pv[0], pv[1]);
+          w.y = pack_bf16x2(pv[2], pv[3]);
+          w.z = pack_bf16x2(pv[4], pv[5]);
+          w.w = pack_bf16x2(pv[6], pv[7]);
+          pf[tt] = as_bf16x8(w);
+        }
+        if constexpr (DO_DK) {
+          w.x = pack_bf16x2(dsv[0], dsv[1]);
+          w.y = pack_bf16x2(dsv[2], dsv[3]);
+          w.z = pack_bf16x2(dsv[4], dsv[5]);
+          w.w = pack_bf16x2(dsv[6], dsv[7]);
+          dsf[tt] = as_bf16x8(w);
+        }
       }
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-          dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.trn(dt, blk, tt, db), pf[tt],
-                                                              dvacc[db], 0, 0, 0);
-          dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.trn(qt, blk, tt, db), dsf[tt],
-                                                              dkacc[db], 0, 0, 0);
+          if constexpr (DO_DV)
+            dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.trn(dt, blk, tt, db), pf[tt],
+                                                                dvacc[db], 0, 0, 0);
+          if constexpr (DO_DK)
+            dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.trn(qt, blk, tt, db), dsf[tt],
+                                                                dkacc[db], 0, 0, 0);
         }
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -484,10 +503,18 @@ __global__ __launch_bounds__(256, D >= 128 ? 1 : 2) void attn_bwd_dkdv_kernel(
         u.y = dvacc[db][4 * g + 1];
         u.z = dvacc[db][4 * g + 2];
         u.w = dvacc[db][4 * g + 3];
-        *reinterpret_cast<float4*>(kp + db * 32 + 8 * g) = w;
-        *reinterpret_cast<float4*>(vp + db * 32 + 8 * g) = u;
+        if constexpr (DO_DK) *reinterpret_cast<float4*>(kp + db * 32 + 8 * g) = w;
+        if constexpr (DO_DV) *reinterpret_cast<float4*>(vp + db * 32 + 8 * g) = u;
       }
   }
+}
+
+// ATTN_BWD_SPLIT=1 runs dV and dK as two passes (sweeps); the default is the
+// fused pass, measured faster at both head dims (1x8192 causal d=128: 1365 us
+// fused, 1428 us split; d=64 4096 causal: 701 vs 821 us).
+int bwd_split_mode(int) {
+  const char* s = getenv("ATTN_BWD_SPLIT");
+  return (s != nullptr && s[0] == '1' && s[1] == '\0') ? 1 : 0;
 }
 
 template <int D, bool VARLEN>
@@ -503,9 +530,17 @@ hipError_t bwd_d(const AttnArgs& a, const uint16_t* dout, float* dq, float* dk, 
   if (gq > 0)
     hipLaunchKernelGGL((attn_bwd_dq_kernel<D, VARLEN>), dim3((unsigned)gq), dim3(256), 0, stream, a,
                        dout, dq);
-  if (gk > 0)
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, VARLEN>), dim3((unsigned)gk), dim3(256), 0, stream, a,
-                       dout, dk, dv, n_kb);
+  if (gk > 0) {
+    if (bwd_split_mode(D)) {
+      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, VARLEN, 1>), dim3((unsigned)gk), dim3(256), 0,
+                         stream, a, dout, dk, dv, n_kb);
+      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, VARLEN, 2>), dim3((unsigned)gk), dim3(256), 0,
+                         stream, a, dout, dk, dv, n_kb);
+    } else {
+      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, VARLEN, 0>), dim3((unsigned)gk), dim3(256), 0,
+                         stream, a, dout, dk, dv, n_kb);
+    }
+  }
   return hipGetLastError();
 }
 
