@@ -40,7 +40,7 @@ from .attention import (  # noqa: F401
     attention_query,
 )
 from .layout import unpad_gather, pad_scatter, mask_to_varlen  # noqa: F401
-from .paged import gather_pages, attention_paged  # noqa: F401
+from .paged import gather_pages, attention_paged, attention_paged_fp8kv  # noqa: F401
 from .fp8 import e4m3_to_f64, attention_fp8_varlen, attention_fp8_dense  # noqa: F401
 from .backward import (  # noqa: F401
     attention_backward_one,

@@ -393,6 +393,19 @@ PAGED_WORKLOADS: Dict[str, Callable[[str], PagedWorkload]] = {
 }
 
 
+def paged_cache_e4m3(w: PagedWorkload, seed: int, factors=(1.0, 1.0)):
+    """E4M3 K and V pools shaped like w's caches: N(0,1) / factor draws rounded
+    to E4M3; rows no sequence owns keep the draws (or NaN bytes when w was
+    made with a NaN fill)."""
+    rng = np.random.Generator(np.random.PCG64(seed + 9_000_000))
+    k8 = normal_e4m3(rng, w.k_cache.shape, 1.0 / float(factors[0]))
+    v8 = normal_e4m3(rng, w.v_cache.shape, 1.0 / float(factors[1]))
+    nan_rows = (w.k_cache == 0x7FC0) | (w.k_cache == 0xFFC0)
+    k8[nan_rows] = 0x7F
+    v8[nan_rows] = 0x7F
+    return k8, v8
+
+
 def build_paged(name: str) -> PagedWorkload:
     return PAGED_WORKLOADS[name](name)
 

@@ -200,3 +200,27 @@ def test_pins_reject_planted_mistakes(kind):
                            w.block_table, w.scale, True)
     ob, lb = brute(w)
     assert not np.allclose(o, ob, atol=1e-9)
+
+
+def test_fp8kv_equals_bf16_oracle_on_shared_values():
+    # every E4M3 value is exact in bf16, so the fp8 cache oracle must equal the
+    # (pinned) bf16 paged oracle on the same values, with factors applied exactly
+    import oracle.fp8 as of8
+    w = gen.make_paged("f8kv", 91, [1, 3, 2], [40, 9, 33], 8, 2, 64, 16, True)
+    k8, v8 = gen.paged_cache_e4m3(w, 91)
+    to_bf16 = lambda x8, f: gen.bf16_bits_from_f32((of8.e4m3_to_f64(x8) * f).astype(np.float32))
+    for kf, vf in ((1.0, 1.0), (0.5, 4.0)):
+        o8, l8 = oracle.attention_paged_fp8kv(w.q, k8, v8, w.cu_seqlens_q, w.seqlens_k,
+                                              w.block_table, w.scale, kf, vf, True)
+        ob, lb = oracle.attention_paged(w.q, to_bf16(k8, kf), to_bf16(v8, vf), w.cu_seqlens_q,
+                                        w.seqlens_k, w.block_table, w.scale, True)
+        assert np.array_equal(o8, ob) and np.array_equal(l8, lb)
+
+
+def test_fp8kv_unowned_nan_rows_never_read():
+    w = gen.make_paged("f8nan", 92, [1, 2], [21, 6], 4, 2, 64, 16, True, fill=float("nan"))
+    k8, v8 = gen.paged_cache_e4m3(w, 92)
+    assert (k8 == 0x7F).any()
+    o, lse = oracle.attention_paged_fp8kv(w.q, k8, v8, w.cu_seqlens_q, w.seqlens_k,
+                                          w.block_table, w.scale, 1.0, 1.0, True)
+    assert np.isfinite(o).all()
