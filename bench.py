@@ -295,16 +295,20 @@ def run_paged(torch, t, names, flush):
         w = gen.build_paged(name)
         dev = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to("cuda").view(torch.bfloat16)
         i32 = lambda x: torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).to("cuda")
-        q, kc, vc = dev(w.q), dev(w.k_cache), dev(w.v_cache)
+        fp8kv = w.k_cache8 is not None
+        u8 = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to("cuda")
+        q = dev(w.q)
+        kc, vc = (u8(w.k_cache8), u8(w.v_cache8)) if fp8kv else (dev(w.k_cache), dev(w.v_cache))
         cq, sk, bt = i32(w.cu_seqlens_q), i32(w.seqlens_k), i32(w.block_table)
         o = torch.empty(w.q.shape, dtype=torch.float32, device="cuda")
         lse = torch.empty((w.hq, w.q.shape[0]), dtype=torch.float32, device="cuda")
         nseq = len(w.lengths_q)
         ws = t.paged_workspace(nseq, w.max_seqlen_q, w.max_seqlen_k, w.hq, w.hkv, w.d)
-        fn = lambda: t.attn_fwd_paged(q, kc, vc, cq, sk, bt, w.max_seqlen_q, w.max_seqlen_k,
-                                      scale=float(w.scale), causal=w.causal, out=o, lse=lse,
-                                      workspace=ws)
-        by = (int(w.seqlens_k.sum()) * w.hkv * w.d * 2 * 2 + w.q.size * 2 + w.q.size * 4
+        call = t.attn_fwd_paged_fp8kv if fp8kv else t.attn_fwd_paged
+        fn = lambda: call(q, kc, vc, cq, sk, bt, w.max_seqlen_q, w.max_seqlen_k,
+                          scale=float(w.scale), causal=w.causal, out=o, lse=lse, workspace=ws)
+        elem = 1 if fp8kv else 2
+        by = (int(w.seqlens_k.sum()) * w.hkv * w.d * elem * 2 + w.q.size * 2 + w.q.size * 4
               + w.hq * w.q.shape[0] * 4)
         probe = time_calls(torch, fn, 3, 2)
         iters = int(min(30, max(5, 0.25e6 / max(1.0, statistics.median(probe)))))
@@ -312,6 +316,7 @@ def run_paged(torch, t, names, flush):
         med = statistics.median(cold)
         gbs = by / (med * 1e-6) / 1e9
         rows.append({"workload": name, "us_median_cold": round(med, 1), "mb": round(by / 1e6, 1),
+                     "tokens_per_s": round(len(w.q) / (med * 1e-6), 1),
                      "gbs": round(gbs, 1), "pct_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 1),
                      "split_workspace_mb": round((ws.numel() if ws is not None else 0) / 1e6, 2)})
         del q, kc, vc, o, lse, ws, cq, sk, bt

@@ -315,6 +315,31 @@ attn_status_t attn_fwd_paged(const void* q, const void* k_cache, const void* v_c
                              int64_t workspace_bytes, void* stream);
 
 /*
+ * attn_fwd_paged_fp8kv -- attn_fwd_paged over a cache of 8-bit floats.
+ *
+ * Passage: page "why FA is 2x on A100 but 1.5x on Ascend 910", section 5 (a
+ * narrower KV cache halves the bytes the HBM-bound inference moves), with the
+ * E4M3 format and per-tensor factors of attn_fwd_fp8_varlen.
+ *
+ * k_cache, v_cache (num_pages, page_size, num_heads_k, head_dim): E4M3 bytes;
+ * the keys and values are k_scale * K and v_scale * V (factors > 0, finite).
+ * q stays bf16.  Every other argument, the workspace and the size rules are
+ * those of attn_fwd_paged (the page-size limit counts one byte per element).
+ * The cache bytes are dequantised to bf16 in registers (E4M3 values are exact
+ * in bf16) and the products are the bf16 MFMAs of attn_fwd_paged, so the
+ * results carry the same rounding as the bf16 path on the dequantised values.
+ */
+attn_status_t attn_fwd_paged_fp8kv(const void* q, const void* k_cache, const void* v_cache,
+                                   const int32_t* cu_seqlens_q, const int32_t* seqlens_k,
+                                   const int32_t* block_table, int32_t num_seqs, int32_t total_q,
+                                   int32_t num_pages, int32_t page_size, int32_t max_pages_per_seq,
+                                   int32_t num_heads_q, int32_t num_heads_k, int32_t head_dim,
+                                   int32_t max_seqlen_q, int32_t max_seqlen_k, float scale,
+                                   float k_scale, float v_scale, int32_t causal, float* out,
+                                   float* lse, void* workspace, int64_t workspace_bytes,
+                                   void* stream);
+
+/*
  * attn_fwd_paged_workspace_bytes -- workspace that lets attn_fwd_paged split
  * key ranges for this shape; 0 when it would not split (or for invalid
  * arguments).  Pure host computation.

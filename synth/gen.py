@@ -276,6 +276,8 @@ class PagedWorkload:
     cu_seqlens_q: np.ndarray
     lengths_q: List[int]
     seed: int
+    k_cache8: Optional[np.ndarray] = None  # E4M3 pools (fp8-cache workloads only)
+    v_cache8: Optional[np.ndarray] = None
 
     @property
     def max_seqlen_q(self) -> int:
@@ -385,12 +387,24 @@ PAGED_SEEDS = {
     "specdec_paged_b32_q4": 6003,
     "decode_paged_b128_d64": 6004,
 }
+def _fp8kv(base: str):
+    def build(name: str) -> PagedWorkload:
+        w = PAGED_WORKLOADS[base](base)
+        w.name = name
+        w.k_cache8, w.v_cache8 = paged_cache_e4m3(w, PAGED_SEEDS[base])
+        return w
+    return build
+
+
 PAGED_WORKLOADS: Dict[str, Callable[[str], PagedWorkload]] = {
     "decode_paged_b32_gqa8": _decode(32, 1, (4096, 8192), 64, 8, 128, 64),
     "decode_paged_b8_32k": _decode(8, 1, (32768, 32768), 64, 8, 128, 64),
     "specdec_paged_b32_q4": _decode(32, 4, (4096, 8192), 64, 8, 128, 64),
     "decode_paged_b128_d64": _decode(128, 1, (1024, 2048), 32, 32, 64, 32),
 }
+# the same decode batches over E4M3 caches
+PAGED_WORKLOADS["decode_paged_b32_gqa8_fp8kv"] = _fp8kv("decode_paged_b32_gqa8")
+PAGED_WORKLOADS["decode_paged_b8_32k_fp8kv"] = _fp8kv("decode_paged_b8_32k")
 
 
 def paged_cache_e4m3(w: PagedWorkload, seed: int, factors=(1.0, 1.0)):

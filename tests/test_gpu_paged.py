@@ -168,3 +168,41 @@ def test_long_sequence_without_split(d, lk):
     w = gen.make_paged(f"long{d}", 1900 + d, [1, 2], [lk, 700], 8, 2, d, 16, True,
                        fill=float("nan"))
     print(check(w, workspace=False))
+
+
+# ---------------------------------------------------------------- E4M3 cache
+def run_f8(w, k8, v8, kf, vf, workspace):
+    import torch
+    t = api()
+    u8 = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to("cuda")
+    ws = None
+    if workspace:
+        ws = t.paged_workspace(len(w.lengths_q), max(w.max_seqlen_q, 1), max(w.max_seqlen_k, 1),
+                               w.hq, w.hkv, w.d)
+    o, lse = t.attn_fwd_paged_fp8kv(dev_bf16(w.q), u8(k8), u8(v8), dev_i32(w.cu_seqlens_q),
+                                    dev_i32(w.seqlens_k), dev_i32(w.block_table),
+                                    max(w.max_seqlen_q, 1), w.max_seqlen_k, scale=float(w.scale),
+                                    k_scale=kf, v_scale=vf, causal=w.causal, workspace=ws)
+    return host(o), host(lse)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("page,workspace", [(16, False), (64, True), (48, True)])
+def test_fp8_cache_decode_and_spec(d, page, workspace):
+    w = gen.make_paged(f"f8c{d}", 2500 + d + page, [1, 4, 2, 1, 0], [7, 300, 1000, 64, 5], 8, 2,
+                       d, page, True, fill=float("nan"))
+    for kf, vf in ((1.0, 1.0), (0.5, 2.0)):
+        k8, v8 = gen.paged_cache_e4m3(w, 2500 + d, (kf, vf))
+        o, lse = run_f8(w, k8, v8, kf, vf, workspace)
+        o_ref, lse_ref = oracle.attention_paged_fp8kv(w.q, k8, v8, w.cu_seqlens_q, w.seqlens_k,
+                                                      w.block_table, w.scale, kf, vf, True)
+        print(check_o(o, o_ref), check_lse(lse, lse_ref))
+
+
+def test_fp8_cache_chunked_prefill_noncausal():
+    w = gen.make_paged("f8cp", 2600, [70, 5], [200, 40], 8, 2, 128, 32, False, fill=float("nan"))
+    k8, v8 = gen.paged_cache_e4m3(w, 2600)
+    o, lse = run_f8(w, k8, v8, 1.0, 1.0, False)
+    o_ref, lse_ref = oracle.attention_paged_fp8kv(w.q, k8, v8, w.cu_seqlens_q, w.seqlens_k,
+                                                  w.block_table, w.scale, 1.0, 1.0, False)
+    print(check_o(o, o_ref), check_lse(lse, lse_ref))

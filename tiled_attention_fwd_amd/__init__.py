@@ -19,6 +19,7 @@ __all__ = ["attn_fwd_varlen", "attn_fwd_dense", "attn_fwd_padded", "attn_unpad_g
            "attn_pad_scatter", "attn_bwd_varlen", "attn_bwd_dense", "attn_bwd_workspace_bytes",
            "attn_fwd_paged", "attn_fwd_paged_workspace_bytes", "paged_workspace",
            "attn_mask_to_varlen", "attn_fwd_fp8_varlen", "attn_fwd_fp8_dense",
+           "attn_fwd_paged_fp8kv",
            "attn_fwd_workspace_bytes", "workspace", "abi_version", "AttnError"]
 
 AttnError = _lib.AttnError
@@ -486,4 +487,44 @@ def attn_fwd_fp8_dense(q, k, v, scale: Optional[float] = None, q_scale: float = 
                                 float(q_scale), float(k_scale), float(v_scale), int(bool(causal)),
                                 _ptr(out), _ptr(lse), _stream_ptr(q.device, stream))
     _lib.check("attn_fwd_fp8_dense", st)
+    return out, lse
+
+
+def attn_fwd_paged_fp8kv(q, k_cache, v_cache, cu_seqlens_q, seqlens_k, block_table,
+                         max_seqlen_q: int, max_seqlen_k: int, scale: Optional[float] = None,
+                         k_scale: float = 1.0, v_scale: float = 1.0, causal: bool = True,
+                         out=None, lse=None, return_lse: bool = True, workspace=None,
+                         stream=None):
+    """attn_fwd_paged over E4M3 caches (num_pages, page_size, Hkv, D) bytes with
+    per-tensor factors; q (Tq, Hq, D) bf16.  Returns (out fp32, lse or None)."""
+    torch = _torch()
+    lib = _lib.load()
+    _check_bf16("q", q)
+    for n, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _check_u8(n, t)
+    if q.dim() != 3 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
+        raise ValueError("q must be (Tq, Hq, D) and the caches (num_pages, page_size, Hkv, D)")
+    for n, t in (("cu_seqlens_q", cu_seqlens_q), ("seqlens_k", seqlens_k),
+                 ("block_table", block_table)):
+        if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{n} must be a contiguous int32 GPU tensor")
+    tq, hq, d = q.shape
+    num_pages, page_size, hkv, dk = k_cache.shape
+    if dk != d:
+        raise ValueError("head_dim of q and the caches differ")
+    nseq = cu_seqlens_q.numel() - 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((tq, hq, d), dtype=torch.float32, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty((hq, tq), dtype=torch.float32, device=q.device)
+    ws_ptr, ws_bytes = _ws_args(workspace)
+    st = lib.attn_fwd_paged_fp8kv(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cu_seqlens_q),
+                                  _ptr(seqlens_k), _ptr(block_table), nseq, tq, num_pages,
+                                  page_size, block_table.shape[1], hq, hkv, d, int(max_seqlen_q),
+                                  int(max_seqlen_k), float(scale), float(k_scale), float(v_scale),
+                                  int(bool(causal)), _ptr(out), _ptr(lse), ws_ptr, ws_bytes,
+                                  _stream_ptr(q.device, stream))
+    _lib.check("attn_fwd_paged_fp8kv", st)
     return out, lse

@@ -53,6 +53,11 @@ SIGNATURES = {
                                  c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,
                                  c_int32, c_int32, c_int32, c_float, c_int32, c_void_p, c_void_p,
                                  c_void_p, c_int64, c_void_p]),
+    "attn_fwd_paged_fp8kv": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                       c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32,
+                                       c_int32, c_int32, c_int32, c_int32, c_int32, c_float,
+                                       c_float, c_float, c_int32, c_void_p, c_void_p, c_void_p,
+                                       c_int64, c_void_p]),
     "attn_fwd_paged_workspace_bytes": (c_int64, [c_int32, c_int32, c_int32, c_int32, c_int32,
                                                  c_int32]),
     "attn_mask_to_varlen": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p,

@@ -305,6 +305,87 @@ DebugCheck lens_check(const int32_t* lens, int n, int max_len) {
   return c;
 }
 
+
+attn_status_t paged_impl(const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* cu_seqlens_q, const int32_t* seqlens_k,
+                         const int32_t* block_table, int32_t num_seqs, int32_t total_q,
+                         int32_t num_pages, int32_t page_size, int32_t max_pages_per_seq,
+                         int32_t num_heads_q, int32_t num_heads_k, int32_t head_dim,
+                         int32_t max_seqlen_q, int32_t max_seqlen_k, float scale, int32_t causal,
+                         float* out, float* lse, void* workspace, int64_t workspace_bytes,
+                         bool kv_fp8, float k_scale, float v_scale, void* stream) {
+  if (num_seqs < 0 || total_q < 0 || num_pages < 0 || max_pages_per_seq < 0 ||
+      max_seqlen_q < 0 || max_seqlen_k < 0)
+    return ATTN_ERR_SHAPE;
+  attn_status_t st = check_common(num_heads_q, num_heads_k, head_dim, scale);
+  if (st != ATTN_OK) return st;
+  if (head_dim != 64 && head_dim != 128) return ATTN_ERR_UNSUPPORTED;
+  if (page_size < 16 || page_size % 16 != 0) return ATTN_ERR_UNSUPPORTED;
+  if (kv_fp8)
+    for (float f : {k_scale, v_scale})
+      if (!(f > 0.f) || !isfinite(f)) return ATTN_ERR_UNSUPPORTED;
+  st = check_workspace(workspace, workspace_bytes);
+  if (st != ATTN_OK) return st;
+  if (num_seqs == 0 || total_q == 0 || num_heads_q == 0) return ATTN_OK;
+  if (max_seqlen_q == 0) return ATTN_ERR_SHAPE;
+  if ((int64_t)max_seqlen_k > (int64_t)max_pages_per_seq * page_size) return ATTN_ERR_SHAPE;
+  if (q == nullptr || out == nullptr || cu_seqlens_q == nullptr || seqlens_k == nullptr)
+    return ATTN_ERR_NULL;
+  if (max_seqlen_k > 0 && (k_cache == nullptr || v_cache == nullptr || block_table == nullptr))
+    return ATTN_ERR_NULL;
+  if (!aligned16(q) || !aligned16(out) ||
+      (max_seqlen_k > 0 && (!aligned16(k_cache) || !aligned16(v_cache))))
+    return ATTN_ERR_ALIGN;
+  if (!aligned4(cu_seqlens_q) || !aligned4(seqlens_k) || (block_table && !aligned4(block_table)) ||
+      (lse && !aligned4(lse)))
+    return ATTN_ERR_ALIGN;
+  const int64_t page_bytes = (int64_t)page_size * num_heads_k * head_dim * (kv_fp8 ? 1 : 2);
+  if (page_bytes >= (1LL << 32)) return ATTN_ERR_SHAPE;
+  attnfwd::DecodeArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k_cache = static_cast<const uint16_t*>(k_cache);
+  a.v_cache = static_cast<const uint16_t*>(v_cache);
+  a.block_table = block_table;
+  a.seqlens_k = seqlens_k;
+  a.cu_q = cu_seqlens_q;
+  a.o = out;
+  a.lse = lse;
+  a.nseq = num_seqs;
+  a.tq = total_q;
+  a.hq = num_heads_q;
+  a.hkv = num_heads_k;
+  a.group = num_heads_q / num_heads_k;
+  a.num_pages = num_pages;
+  a.page_size = page_size;
+  a.max_pages = max_pages_per_seq;
+  a.c = kv_fp8 ? (float)((double)scale * k_scale * 1.4426950408889634074) : base2_factor(scale);
+  a.causal = causal ? 1 : 0;
+  a.order = paged_order();
+  a.kv_fp8 = kv_fp8 ? 1 : 0;
+  a.o_mul = kv_fp8 ? v_scale : 1.f;
+  {
+    const attn_status_t dst_ = run_debug({cu_check(cu_seqlens_q, num_seqs, total_q, max_seqlen_q),
+                                          lens_check(seqlens_k, num_seqs, max_seqlen_k)},
+                                         static_cast<hipStream_t>(stream));
+    if (dst_ != ATTN_OK) return dst_;
+  }
+  const int max_q = max_seqlen_q < total_q ? max_seqlen_q : total_q;
+  const PagedPlan p = plan_paged(num_seqs, max_q, max_seqlen_k, a.group, num_heads_k);
+  a.n_rb = p.n_rb;
+  a.n_split = 1;
+  a.chunk_tiles = 0;
+  const int64_t need = paged_workspace_bytes(p, num_seqs, num_heads_k, head_dim);
+  if (need > 0 && workspace != nullptr && workspace_bytes >= need) {
+    a.n_split = p.n_split;
+    a.chunk_tiles = p.chunk_tiles;
+    a.part_o = static_cast<float*>(workspace);
+    a.part_lse = a.part_o + (int64_t)num_seqs * num_heads_k * p.n_rb * p.n_split * 32 * head_dim;
+  }
+  const hipError_t e =
+      attnfwd::launch_decode(a, head_dim, paged_variant(), static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : (e == hipErrorInvalidConfiguration ? ATTN_ERR_SHAPE : ATTN_ERR_HIP);
+}
+
 }  // namespace
 
 extern "C" {
@@ -651,71 +732,25 @@ attn_status_t attn_fwd_paged(const void* q, const void* k_cache, const void* v_c
                              int32_t max_seqlen_q, int32_t max_seqlen_k, float scale,
                              int32_t causal, float* out, float* lse, void* workspace,
                              int64_t workspace_bytes, void* stream) {
-  if (num_seqs < 0 || total_q < 0 || num_pages < 0 || max_pages_per_seq < 0 ||
-      max_seqlen_q < 0 || max_seqlen_k < 0)
-    return ATTN_ERR_SHAPE;
-  attn_status_t st = check_common(num_heads_q, num_heads_k, head_dim, scale);
-  if (st != ATTN_OK) return st;
-  if (head_dim != 64 && head_dim != 128) return ATTN_ERR_UNSUPPORTED;
-  if (page_size < 16 || page_size % 16 != 0) return ATTN_ERR_UNSUPPORTED;
-  st = check_workspace(workspace, workspace_bytes);
-  if (st != ATTN_OK) return st;
-  if (num_seqs == 0 || total_q == 0 || num_heads_q == 0) return ATTN_OK;
-  if (max_seqlen_q == 0) return ATTN_ERR_SHAPE;
-  if ((int64_t)max_seqlen_k > (int64_t)max_pages_per_seq * page_size) return ATTN_ERR_SHAPE;
-  if (q == nullptr || out == nullptr || cu_seqlens_q == nullptr || seqlens_k == nullptr)
-    return ATTN_ERR_NULL;
-  if (max_seqlen_k > 0 && (k_cache == nullptr || v_cache == nullptr || block_table == nullptr))
-    return ATTN_ERR_NULL;
-  if (!aligned16(q) || !aligned16(out) ||
-      (max_seqlen_k > 0 && (!aligned16(k_cache) || !aligned16(v_cache))))
-    return ATTN_ERR_ALIGN;
-  if (!aligned4(cu_seqlens_q) || !aligned4(seqlens_k) || (block_table && !aligned4(block_table)) ||
-      (lse && !aligned4(lse)))
-    return ATTN_ERR_ALIGN;
-  const int64_t page_bytes = (int64_t)page_size * num_heads_k * head_dim * 2;
-  if (page_bytes >= (1LL << 32)) return ATTN_ERR_SHAPE;
-  attnfwd::DecodeArgs a{};
-  a.q = static_cast<const uint16_t*>(q);
-  a.k_cache = static_cast<const uint16_t*>(k_cache);
-  a.v_cache = static_cast<const uint16_t*>(v_cache);
-  a.block_table = block_table;
-  a.seqlens_k = seqlens_k;
-  a.cu_q = cu_seqlens_q;
-  a.o = out;
-  a.lse = lse;
-  a.nseq = num_seqs;
-  a.tq = total_q;
-  a.hq = num_heads_q;
-  a.hkv = num_heads_k;
-  a.group = num_heads_q / num_heads_k;
-  a.num_pages = num_pages;
-  a.page_size = page_size;
-  a.max_pages = max_pages_per_seq;
-  a.c = base2_factor(scale);
-  a.causal = causal ? 1 : 0;
-  a.order = paged_order();
-  {
-    const attn_status_t dst_ = run_debug({cu_check(cu_seqlens_q, num_seqs, total_q, max_seqlen_q),
-                                          lens_check(seqlens_k, num_seqs, max_seqlen_k)},
-                                         static_cast<hipStream_t>(stream));
-    if (dst_ != ATTN_OK) return dst_;
-  }
-  const int max_q = max_seqlen_q < total_q ? max_seqlen_q : total_q;
-  const PagedPlan p = plan_paged(num_seqs, max_q, max_seqlen_k, a.group, num_heads_k);
-  a.n_rb = p.n_rb;
-  a.n_split = 1;
-  a.chunk_tiles = 0;
-  const int64_t need = paged_workspace_bytes(p, num_seqs, num_heads_k, head_dim);
-  if (need > 0 && workspace != nullptr && workspace_bytes >= need) {
-    a.n_split = p.n_split;
-    a.chunk_tiles = p.chunk_tiles;
-    a.part_o = static_cast<float*>(workspace);
-    a.part_lse = a.part_o + (int64_t)num_seqs * num_heads_k * p.n_rb * p.n_split * 32 * head_dim;
-  }
-  const hipError_t e =
-      attnfwd::launch_decode(a, head_dim, paged_variant(), static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? ATTN_OK : (e == hipErrorInvalidConfiguration ? ATTN_ERR_SHAPE : ATTN_ERR_HIP);
+  return paged_impl(q, k_cache, v_cache, cu_seqlens_q, seqlens_k, block_table, num_seqs, total_q,
+                    num_pages, page_size, max_pages_per_seq, num_heads_q, num_heads_k, head_dim,
+                    max_seqlen_q, max_seqlen_k, scale, causal, out, lse, workspace,
+                    workspace_bytes, false, 1.f, 1.f, stream);
+}
+
+attn_status_t attn_fwd_paged_fp8kv(const void* q, const void* k_cache, const void* v_cache,
+                                   const int32_t* cu_seqlens_q, const int32_t* seqlens_k,
+                                   const int32_t* block_table, int32_t num_seqs, int32_t total_q,
+                                   int32_t num_pages, int32_t page_size, int32_t max_pages_per_seq,
+                                   int32_t num_heads_q, int32_t num_heads_k, int32_t head_dim,
+                                   int32_t max_seqlen_q, int32_t max_seqlen_k, float scale,
+                                   float k_scale, float v_scale, int32_t causal, float* out,
+                                   float* lse, void* workspace, int64_t workspace_bytes,
+                                   void* stream) {
+  return paged_impl(q, k_cache, v_cache, cu_seqlens_q, seqlens_k, block_table, num_seqs, total_q,
+                    num_pages, page_size, max_pages_per_seq, num_heads_q, num_heads_k, head_dim,
+                    max_seqlen_q, max_seqlen_k, scale, causal, out, lse, workspace,
+                    workspace_bytes, true, k_scale, v_scale, stream);
 }
 
 attn_status_t attn_mask_to_varlen(const void* mask, int32_t batch, int32_t seqlen,

@@ -8,7 +8,7 @@ namespace attnfwd {
 
 struct DecodeArgs {
   const uint16_t* q;           // (tq, hq, D) bf16
-  const uint16_t* k_cache;     // (num_pages, page_size, hkv, D) bf16
+  const uint16_t* k_cache;     // (num_pages, page_size, hkv, D) bf16, or E4M3 bytes
   const uint16_t* v_cache;
   const int32_t* block_table;  // (nseq, max_pages)
   const int32_t* seqlens_k;    // (nseq)
@@ -25,6 +25,8 @@ struct DecodeArgs {
   float c;              // scale * log2(e)
   int32_t causal;
   int32_t order;        // grid order: 1 = KV head fastest, 0 = key part fastest
+  int32_t kv_fp8;       // 1: the caches hold E4M3 bytes (dequantised to bf16 in registers)
+  float o_mul;          // factor on the output (the v factor of an E4M3 cache; else 1)
 };
 
 // Query rows and key tiles of one (sequence, row block).
@@ -55,8 +57,10 @@ __host__ __device__ inline int decode_parts(const DecodeArgs& a, int n_kt) {
   return p < 1 ? 1 : p;
 }
 
-// variant: waves x stages per workgroup (d=128: 0 = 4x2, 1 = 3x3, 2 = 5x2;
-// d=64: 0 = 4x4, 1 = 8x2, 2 = 5x4); < 0 picks the measured default.
+// variant: waves x stages per workgroup (bf16 cache, d=128: 0 = 4x2, 1 = 3x3,
+// 2 = 5x2; d=64: 0 = 4x4, 1 = 8x2, 2 = 5x4; E4M3 cache, d=128: 0 = 4x4,
+// 1 = 8x2, 2 = 5x4; d=64: 0 = 4x4, 1 = 8x4, 2 = 5x4); < 0 picks the measured
+// default.
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, int variant, hipStream_t stream);
 
 }  // namespace attnfwd

@@ -31,6 +31,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 namespace attnfwd {
 namespace {
 
@@ -96,23 +98,83 @@ struct Frag32 {
 template <int D>
 constexpr int tile32_bytes() { return RowTile<D>::BYTES; }
 
+// E4M3 cache tiles: 32 rows of D bytes, row-major DMA lanes, chunk swizzles
+// (K: (row / 2) mod 8 at d=128, (row / 4) mod 4 at d=64; V: row mod 8 and
+// 2 ((row / 4) mod 2)) that keep the fragment reads below free of bank
+// conflicts.  The fragments are dequantised to bf16 in registers (E4M3 values
+// are exact in bf16), so the products stay bf16 MFMAs with exact operands.
+template <int D>
+struct RowTile8 {
+  static constexpr int CPR = D / 16;   // 16-byte chunks per row
+  static constexpr int R = 64 / CPR;   // rows per DMA instruction
+  static constexpr int PITCH = D;
+  static constexpr int BYTES = kTileKeys * PITCH;
+  static __device__ __forceinline__ int swz_k(int r) { return D == 128 ? ((r >> 1) & 7) : ((r >> 2) & 3); }
+  static __device__ __forceinline__ int swz_v(int r) { return D == 128 ? (r & 7) : (((r >> 2) & 1) << 1); }
+};
+
+typedef int i32x2v __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// K: one 16-byte read per pair of score MFMAs.  Pair j covers dims 32 j ..
+// 32 j + 31: lane half hh holds dims 32 j + 16 hh + 8 sub + e for MFMA
+// (j, sub) (Q uses the same assignment, which is all the MFMA needs).
+// V: ds_read_b64_tr_b8 gives a lane 8 consecutive keys of one dim.
+template <int D>
+struct Frag32F8 {
+  using L = RowTile8<D>;
+  static constexpr int NDB = D / 32;
+  int rd_row, rd_x, hh, tr_base;
+  __device__ __forceinline__ void init(int lane) {
+    const int l32 = lane & 31;
+    hh = lane >> 5;
+    rd_row = l32 * L::PITCH;
+    rd_x = L::swz_k(l32);
+    const int vg = (lane >> 4) & 1, vi = lane & 15;
+    // natural row 16 tt + 8 hh + vi / 2: swz_v depends on vi only
+    tr_base = (8 * hh + (vi >> 1)) * L::PITCH + 8 * (vi & 1) + 16 * vg;
+    tr_x = L::swz_v(vi >> 1);
+    tr_vg = vg;
+  }
+  int tr_x, tr_vg;
+  __device__ __forceinline__ void krow(const unsigned char* t, int j, bf16x8& a0, bf16x8& a1) const {
+    const uint4 x = *reinterpret_cast<const uint4*>(t + rd_row + 16 * ((2 * j + hh) ^ rd_x));
+    a0 = e4m3x8_to_bf16(x.x, x.y);
+    a1 = e4m3x8_to_bf16(x.z, x.w);
+  }
+  __device__ __forceinline__ bf16x8 vtr(const unsigned char* t, int tt, int db) const {
+    const int c = 2 * db + tr_vg;
+    const unsigned char* p = t + tr_base - 16 * tr_vg + 16 * (c ^ tr_x) + 16 * tt * L::PITCH;
+    const i32x2v x = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+        (__attribute__((address_space(3))) i32x2v*)(p));
+    return e4m3x8_to_bf16((uint32_t)x[0], (uint32_t)x[1]);
+  }
+};
+
 // Pages of one 32-key tile: its two aligned 16-key groups (the same page when
 // page_size >= 32).  A group past the sequence, past the table row or naming a
 // page outside the pool is dead: its loads get an empty buffer range, so its
 // lanes read zeros and nothing is dereferenced.
 struct TilePages {
-  const uint16_t* kbase[2];
-  const uint16_t* vbase[2];
+  const unsigned char* kbase[2];
+  const unsigned char* vbase[2];
   uint32_t bytes[2];
   int pstart[2];
 };
 
 // page[g] is the table entry of the tile's 16-key group g (-1: none).
-template <int D>
+template <int D, int ES>
 __device__ __forceinline__ TilePages tile_pages(const DecodeArgs& a, const int page[2], int lk,
                                                 int kvh, int t) {
   TilePages tp;
-  const uint32_t row_bytes = (uint32_t)a.hkv * D * 2;
+  const uint32_t row_bytes = (uint32_t)a.hkv * D * ES;
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
     const int key0 = t * kTileKeys + 16 * g;
@@ -121,10 +183,10 @@ __device__ __forceinline__ TilePages tile_pages(const DecodeArgs& a, const int p
     const bool live = key0 < lk && pidx < a.max_pages && pg >= 0 && pg < a.num_pages;
     tp.pstart[g] = pidx * a.page_size;
     const int valid = min(a.page_size, lk - tp.pstart[g]);  // >= 1 when key0 < lk
-    const int64_t off = ((int64_t)(live ? pg : 0) * a.page_size * a.hkv + kvh) * D;
-    tp.kbase[g] = a.k_cache + off;
-    tp.vbase[g] = a.v_cache + off;
-    tp.bytes[g] = live ? (uint32_t)(valid - 1) * row_bytes + D * 2 : 0u;
+    const int64_t off = ((int64_t)(live ? pg : 0) * a.page_size * a.hkv + kvh) * D * ES;
+    tp.kbase[g] = reinterpret_cast<const unsigned char*>(a.k_cache) + off;
+    tp.vbase[g] = reinterpret_cast<const unsigned char*>(a.v_cache) + off;
+    tp.bytes[g] = live ? (uint32_t)(valid - 1) * row_bytes + D * ES : 0u;
   }
   return tp;
 }
@@ -148,14 +210,17 @@ __device__ __forceinline__ int load_pages(const DecodeArgs& a, const int32_t* ta
 // q R .. q R + R - 1, whose source keys (key_of_row of the row) lie in the
 // aligned 16-key group (q R) / 16, hence in one page (page_size is a multiple
 // of 16).
-template <int D>
+template <int D, int ES>
+using TileOf = typename std::conditional<ES == 2, RowTile<D>, RowTile8<D>>::type;
+
+template <int D, int ES>
 __device__ __forceinline__ void dma_tile(const TilePages& tp, bool is_v, int hkv, int t,
                                          uint32_t tile, int lane) {
-  using L = RowTile<D>;
+  using L = TileOf<D, ES>;
   constexpr int R = L::R;
   constexpr int NI = kTileKeys / R;
   const int p = lane % L::CPR;
-  const uint32_t row_bytes = (uint32_t)hkv * D * 2;
+  const uint32_t row_bytes = (uint32_t)hkv * D * ES;
 #pragma unroll
   for (int q = 0; q < NI; ++q) {
     const int g = (q * R) >> 4;
@@ -173,11 +238,12 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NI) : "memory");
 }
 
-template <int D, int WAVES, int NBUF>
+template <int D, int WAVES, int NBUF, int ES>
 __global__ __launch_bounds__(WAVES * 64, 1) void attn_decode_kernel(const DecodeArgs a) {
   constexpr int NDS = D / 16, NDB = D / 32;
-  constexpr int TB = tile32_bytes<D>();
-  constexpr int NI = kTileKeys / RowTile<D>::R;     // DMA instructions per tile per tensor
+  using L = TileOf<D, ES>;
+  constexpr int TB = L::BYTES;
+  constexpr int NI = kTileKeys / L::R;              // DMA instructions per tile per tensor
   constexpr int WAVE_LDS = NBUF * 2 * TB;           // NBUF stages of K and V
   constexpr int MERGE_LDS = WAVES * (32 * D + 64) * 4;
   constexpr int LDS = WAVES * WAVE_LDS > MERGE_LDS ? WAVES * WAVE_LDS : MERGE_LDS;
@@ -223,18 +289,23 @@ __global__ __launch_bounds__(WAVES * 64, 1) void attn_decode_kernel(const Decode
   const int hq = kvh * a.group + (col_ok ? r % a.group : 0);
   const int lim = !col_ok ? -1 : (a.causal ? min(dr.lk - 1, qi + dr.lk - dr.lq) : dr.lk - 1);
 
+  // Q as the B operand.  bf16 cache: MFMA s takes dims 16 s + 8 hh + e; E4M3
+  // cache: MFMA 2 j + sub takes dims 32 j + 16 hh + 8 sub + e (the order of
+  // the dequantised K fragments).
   bf16x8 qf[NDS];
   {
-    const uint16_t* qp = a.q + ((int64_t)(dr.q0 + qi) * a.hq + hq) * D + hh * 8;
+    const uint16_t* qp = a.q + ((int64_t)(dr.q0 + qi) * a.hq + hq) * D;
 #pragma unroll
-    for (int s = 0; s < NDS; ++s)
-      qf[s] = col_ok ? as_bf16x8(ld16(qp + 16 * s)) : bf16x8{};
+    for (int s = 0; s < NDS; ++s) {
+      const int dim0 = ES == 2 ? 16 * s + 8 * hh : 32 * (s >> 1) + 16 * hh + 8 * (s & 1);
+      qf[s] = col_ok ? as_bf16x8(ld16(qp + dim0)) : bf16x8{};
+    }
   }
 
   const int32_t* table_row = a.block_table + (int64_t)seq * a.max_pages;
   const uint32_t my_lds = lds_addr(lds) + wave * WAVE_LDS;
   const unsigned char* my_tiles = lds + wave * WAVE_LDS;
-  Frag32<D> fr;
+  typename std::conditional<ES == 2, Frag32<D>, Frag32F8<D>>::type fr;
   fr.init(lane);
 
   float m = -INFINITY, l = 0.f;
@@ -258,9 +329,9 @@ __global__ __launch_bounds__(WAVES * 64, 1) void attn_decode_kernel(const Decode
     const int page[2] = {__builtin_amdgcn_readlane(pagevec, sel),
                          __builtin_amdgcn_readlane(pagevec, sel + 1)};
     const uint32_t b = my_lds + buf * 2 * TB;
-    const TilePages tp = tile_pages<D>(a, page, dr.lk, kvh, t);
-    dma_tile<D>(tp, false, a.hkv, t, b, lane);
-    dma_tile<D>(tp, true, a.hkv, t, b + TB, lane);
+    const TilePages tp = tile_pages<D, ES>(a, page, dr.lk, kvh, t);
+    dma_tile<D, ES>(tp, false, a.hkv, t, b, lane);
+    dma_tile<D, ES>(tp, true, a.hkv, t, b + TB, lane);
   };
 
   // Every stage holds a tile in flight: a tile's K and V fragments are copied
@@ -281,12 +352,21 @@ __global__ __launch_bounds__(WAVES * 64, 1) void attn_decode_kernel(const Decode
     const unsigned char* kt = my_tiles + buf * 2 * TB;
     const unsigned char* vt = kt + TB;
     bf16x8 kfr[NDS], vfr[2][NDB];
+    if constexpr (ES == 2) {
 #pragma unroll
-    for (int s = 0; s < NDS; ++s) kfr[s] = fr.row(kt, s);
+      for (int s = 0; s < NDS; ++s) kfr[s] = fr.row(kt, s);
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
+      for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) vfr[tt][db] = fr.trn(vt, tt, db);
+        for (int db = 0; db < NDB; ++db) vfr[tt][db] = fr.trn(vt, tt, db);
+    } else {
+#pragma unroll
+      for (int j2 = 0; j2 < NDS / 2; ++j2) fr.krow(kt, j2, kfr[2 * j2], kfr[2 * j2 + 1]);
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) vfr[tt][db] = fr.vtr(vt, tt, db);
+    }
     if (j + NBUF < n_mine) {
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the reads of this stage are done
       issue(j + NBUF, buf);
@@ -380,7 +460,8 @@ __global__ __launch_bounds__(WAVES * 64, 1) void attn_decode_kernel(const Decode
         lsum += f * ml[w * 32 + col];
       }
     }
-    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    // a split part stays normalised by its own sum; the v factor is applied once
+    const float inv = lsum > 0.f ? (a.n_split > 1 ? 1.f : a.o_mul) / lsum : 0.f;
     acc.x *= inv;
     acc.y *= inv;
     acc.z *= inv;
@@ -438,7 +519,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeArgs a) {
       }
     }
   }
-  const float inv = s > 0.f ? 1.f / s : 0.f;
+  const float inv = s > 0.f ? a.o_mul / s : 0.f;
   const int cq = rr / a.group;
   const int hq = kvh * a.group + rr % a.group;
   float* dst = a.o + ((int64_t)(dr.q0 + cq) * a.hq + hq) * D + sub * 4;
@@ -456,10 +537,10 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeArgs a) {
 // (tiles in flight per wave).  d=128 (16 KiB per stage): 0 = 4 waves x 2
 // stages, 1 = 3 x 3, 2 = 5 x 2; d=64 (8 KiB per stage): 0 = 4 x 4, 1 = 8 x 2,
 // 2 = 5 x 4.
-template <int D, int W, int NB>
+template <int D, int W, int NB, int ES>
 hipError_t launch_v(const DecodeArgs& a, int64_t grid, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_decode_kernel<D, W, NB>), dim3((unsigned)grid), dim3(W * 64), 0, stream,
-                     a);
+  hipLaunchKernelGGL((attn_decode_kernel<D, W, NB, ES>), dim3((unsigned)grid), dim3(W * 64), 0,
+                     stream, a);
   return hipSuccess;
 }
 
@@ -468,17 +549,28 @@ hipError_t launch_d(const DecodeArgs& a, int variant, hipStream_t stream) {
   const int64_t grid = (int64_t)a.nseq * a.hkv * a.n_rb * a.n_split;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   if (grid == 0) return hipSuccess;
-  // Defaults (variant < 0) from the measured sweep: more waves beat more
-  // stages (d=128 decode: 4x2 3.8, 3x3 3.4, 5x2 4.2 TB/s; d=64: 4x4 3.4,
-  // 8x2 4.3, 5x4 3.8 TB/s).
-  if constexpr (D == 128) {
-    if (variant == 0) launch_v<D, 4, 2>(a, grid, stream);
-    else if (variant == 1) launch_v<D, 3, 3>(a, grid, stream);
-    else launch_v<D, 5, 2>(a, grid, stream);
+  // Defaults (variant < 0) from measured sweeps: more waves beat more stages
+  // for bf16 caches (d=128 decode: 4x2 3.8, 3x3 3.6, 5x2 4.5 TB/s; d=64: 4x4
+  // 3.4, 8x2 4.5, 5x4 4.2 TB/s).  E4M3 caches halve the stage size.
+  if (a.kv_fp8) {
+    // E4M3 caches, d=128 decode b32 GQA-8 (cold): 4x4 195, 8x2 173, 5x4 184 us
+    if constexpr (D == 128) {
+      if (variant == 0) launch_v<D, 4, 4, 1>(a, grid, stream);
+      else if (variant == 2) launch_v<D, 5, 4, 1>(a, grid, stream);
+      else launch_v<D, 8, 2, 1>(a, grid, stream);
+    } else {
+      if (variant == 0) launch_v<D, 4, 4, 1>(a, grid, stream);
+      else if (variant == 2) launch_v<D, 5, 4, 1>(a, grid, stream);
+      else launch_v<D, 8, 4, 1>(a, grid, stream);
+    }
+  } else if constexpr (D == 128) {
+    if (variant == 0) launch_v<D, 4, 2, 2>(a, grid, stream);
+    else if (variant == 1) launch_v<D, 3, 3, 2>(a, grid, stream);
+    else launch_v<D, 5, 2, 2>(a, grid, stream);
   } else {
-    if (variant == 0) launch_v<D, 4, 4>(a, grid, stream);
-    else if (variant == 2) launch_v<D, 5, 4>(a, grid, stream);
-    else launch_v<D, 8, 2>(a, grid, stream);
+    if (variant == 0) launch_v<D, 4, 4, 2>(a, grid, stream);
+    else if (variant == 2) launch_v<D, 5, 4, 2>(a, grid, stream);
+    else launch_v<D, 8, 2, 2>(a, grid, stream);
   }
   if (a.n_split > 1) {
     const int64_t gm = (int64_t)a.nseq * a.hkv * a.n_rb;
