@@ -209,3 +209,44 @@ def test_backward_argument_checks(lib):
     assert g(P, P, P, P, P, P, 1, 8, 8, 2, 2, 64, 0.125, 1, P, P, P, P, 63, None) == SHAPE
     assert g(None, None, None, None, None, None, 0, 8, 8, 2, 2, 64, 0.125, 1, None, None, None,
              None, 0, None) == OK
+
+
+def test_paged_fp8_and_mask_argument_checks(lib):
+    P = ctypes.c_void_p(16)
+    f = lib.attn_fwd_paged
+
+    # q, k, v, cu_q, seqlens_k, table, nseq, tq, num_pages, page_size, max_pages, hq, hkv, d,
+    # max_q, max_k, scale, causal, out, lse, ws, ws_bytes, stream
+    def paged(**kw):
+        a = dict(dict(ps=16, d=128, mq=1, mk=32, maxp=2, hq=8, hkv=2, out=P, ws=None, wsb=0), **kw)
+        return f(P, P, P, P, P, P, 2, 2, 8, a["ps"], a["maxp"], a["hq"], a["hkv"], a["d"], a["mq"],
+                 a["mk"], 0.125, 1, a["out"], None, a["ws"], a["wsb"], None)
+    assert paged(ps=8) == UNSUP and paged(ps=24) == UNSUP      # page size: a multiple of 16
+    assert paged(d=32) == UNSUP and paged(d=256) == UNSUP
+    assert paged(mk=33) == SHAPE                                # > max_pages * page_size
+    assert paged(mq=0) == SHAPE
+    assert paged(hq=6, hkv=4) == SHAPE
+    assert paged(out=None) == NULL
+    assert paged(ws=ctypes.c_void_p(24), wsb=1024) == ALIGN
+    g = lib.attn_fwd_paged_fp8kv
+    base = (P, P, P, P, P, P, 2, 2, 8, 16, 2, 8, 2, 128, 1, 32, 0.125)
+    assert g(*base, 0.0, 1.0, 1, P, None, None, 0, None) == UNSUP   # k factor
+    assert g(*base, 1.0, float("inf"), 1, P, None, None, 0, None) == UNSUP
+    ws = lib.attn_fwd_paged_workspace_bytes
+    assert ws(32, 1, 8192, 64, 8, 128) > 0                      # few workgroups: splits
+    assert ws(32, 1, 8192, 64, 8, 96) == 0 and ws(0, 1, 8, 8, 8, 128) == 0
+    h = lib.attn_fwd_fp8_varlen
+    # q, k, v, cu_q, cu_k, nseq, tq, tk, hq, hkv, d, max, scale, qs, ks, vs, causal, out, lse, s
+    assert h(P, P, P, P, P, 1, 8, 8, 2, 2, 32, 8, 0.125, 1.0, 1.0, 1.0, 1, P, None, None) == UNSUP
+    assert h(P, P, P, P, P, 1, 8, 8, 2, 2, 64, 8, 0.125, -1.0, 1.0, 1.0, 1, P, None, None) == UNSUP
+    assert h(P, P, P, P, P, 1, 8, 8, 2, 2, 64, 0, 0.125, 1.0, 1.0, 1.0, 1, P, None, None) == SHAPE
+    assert h(None, P, P, P, P, 1, 8, 8, 2, 2, 64, 8, 0.125, 1.0, 1.0, 1.0, 1, P, None, None) == NULL
+    d = lib.attn_fwd_fp8_dense
+    assert d(P, P, P, 1, 8, 8, 2, 2, 256, 0.125, 1.0, 1.0, 1.0, 1, P, None, None) == UNSUP
+    assert d(P, P, P, 0, 8, 8, 2, 2, 128, 0.125, 1.0, 1.0, 1.0, 1, None, None, None) == OK
+    m = lib.attn_mask_to_varlen
+    assert m(P, -1, 4, P, P, P, None) == SHAPE
+    assert m(P, 1 << 16, 1 << 16, P, P, P, None) == SHAPE      # batch * seqlen >= 2^31
+    assert m(P, 2, 4, P, None, P, None) == NULL
+    assert m(None, 2, 4, P, P, P, None) == NULL
+    assert m(P, 2, 4, P, ctypes.c_void_p(18), P, None) == ALIGN
