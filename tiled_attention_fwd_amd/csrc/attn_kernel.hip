@@ -120,7 +120,7 @@ __global__ __launch_bounds__(WAVES * 64, MINW) void attn_fwd_kernel(const AttnAr
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kg = wave / QW;     // key group of this wave
   const int qw = wave - kg * QW;
   const int l32 = lane & 31;
@@ -510,7 +510,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_pingpong_kernel(const AttnArg
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = wave >> 2;
   const int gtid = tid & (GT - 1);
   const int l32 = lane & 31;
@@ -858,7 +858,7 @@ __global__ __launch_bounds__(WAVES * 64, D == 256 ? 1 : 2) void attn_fwd_dma_ker
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kg = wave / QW;
   const int qw = wave - kg * QW;
   const int l32 = lane & 31;
