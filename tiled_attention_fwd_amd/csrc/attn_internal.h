@@ -32,7 +32,9 @@ struct AttnArgs {
   int32_t n_qb;      // query blocks per (sequence, head) in the grid
   float c;           // scale * log2(e): scores enter exp2 in base-2 units
   int32_t causal;
-  int32_t xcd_remap; // 1: spread (sequence, head) rows so each XCD gets a contiguous slice
+  int32_t xcd_remap; // 1: spread (sequence, head) rows so each XCD gets a contiguous slice;
+                     // 2 (DMA-staged kernel, hq % 8 == 0): sequence-major order, each
+                     //   XCD keeping hq/8 fixed heads of the current sequence
   // Split key ranges (DMA-staged kernel only).  n_split == 1: off.  Otherwise
   // a query block whose key loop has more than split_tiles tiles of split_bn
   // keys is cut into up to n_split even parts; each part writes its

@@ -864,16 +864,31 @@ __global__ __launch_bounds__(WAVES * 64, D == 256 ? 1 : 2) void attn_fwd_dma_ker
   const int l32 = lane & 31;
   const int hh = lane >> 5;
 
-  const int rows = a.nseq * a.hq;
   const int id = blockIdx.x;
-  const int per_qb = rows * a.n_split;
-  const int qb_rev = id / per_qb;
-  const int rem = id - qb_rev * per_qb;
-  const int part = rem / rows;
-  int p = rem - part * rows;
-  if (a.xcd_remap) p = (p & 7) * (rows >> 3) + (p >> 3);
-  const int seq = p / a.hq;
-  const int h = p - seq * a.hq;
+  int seq, h, qb_rev, part;
+  if (a.xcd_remap == 2) {
+    // sequence-major: all blocks of one sequence (longest first), its heads
+    // spread so each XCD keeps hq/8 fixed heads and their K/V in its L2
+    const int per_level = a.n_split * a.hq;
+    const int per_seq = a.n_qb * per_level;
+    seq = id / per_seq;
+    int r = id - seq * per_seq;
+    qb_rev = r / per_level;
+    r -= qb_rev * per_level;
+    part = r / a.hq;
+    const int j = r - part * a.hq;
+    h = (j & 7) * (a.hq >> 3) + (j >> 3);
+  } else {
+    const int rows = a.nseq * a.hq;
+    const int per_qb = rows * a.n_split;
+    qb_rev = id / per_qb;
+    const int rem = id - qb_rev * per_qb;
+    part = rem / rows;
+    int p = rem - part * rows;
+    if (a.xcd_remap) p = (p & 7) * (rows >> 3) + (p >> 3);
+    seq = p / a.hq;
+    h = p - seq * a.hq;
+  }
   const int qb = a.causal ? (a.n_qb - 1 - qb_rev) : qb_rev;
   int lq, lk;
   int64_t qoff, koff, voff, ooff, lseoff;
