@@ -123,10 +123,16 @@ attn_status_t launch(AttnArgs& a, int d, bool varlen, int max_q, void* ws, int64
   // workgroup order, so the workgroups an XCD runs at once share a few heads'
   // K/V in its L2 (a 64K-token pack of 17 sequences: 2072 -> 1406 us).
   const bool dma_kernel = (pid >= 11 && pid <= 13) || pid == 17;
+  const bool pipe_kernel = pid >= 14 && pid <= 16;
   if (dma_kernel && a.nseq > 1 && a.hq % 8 == 0) a.xcd_remap = 2;
+  // Otherwise, on several sequences: unit-major order, every block of one
+  // (sequence, head) on one XCD in a row (ViT batch, 149 x 12 heads, d=64:
+  // 770 -> 712 us).  Not with split parts (their plan needs the block order).
+  const bool unit_major = (dma_kernel || pipe_kernel) && a.nseq > 1 && a.xcd_remap != 2;
   a.n_split = 1;
   const SplitPlan sp = plan_split(pol, pid, rows, a.n_qb, max_q, a.causal != 0);
   const int64_t need = split_workspace_bytes(sp, rows, a.n_qb, d);
+  if (unit_major && !(need > 0 && ws != nullptr && ws_bytes >= need)) a.xcd_remap = 3;
   if (need > 0 && ws != nullptr && ws_bytes >= need) {
     a.n_split = sp.n_split;
     a.split_tiles = sp.split_tiles;

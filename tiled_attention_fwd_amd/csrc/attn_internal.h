@@ -34,7 +34,10 @@ struct AttnArgs {
   int32_t causal;
   int32_t xcd_remap; // 1: spread (sequence, head) rows so each XCD gets a contiguous slice;
                      // 2 (DMA-staged kernel, hq % 8 == 0): sequence-major order, each
-                     //   XCD keeping hq/8 fixed heads of the current sequence
+                     //   XCD keeping hq/8 fixed heads of the current sequence;
+                     // 3 (DMA-staged and pipelined kernels): (sequence, head) units
+                     //   dealt to the XCDs, all blocks of a unit in a row (grid
+                     //   padded to whole rounds of 8 units)
   // Split key ranges (DMA-staged kernel only).  n_split == 1: off.  Otherwise
   // a query block whose key loop has more than split_tiles tiles of split_bn
   // keys is cut into up to n_split even parts; each part writes its

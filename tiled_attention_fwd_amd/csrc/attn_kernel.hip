@@ -878,6 +878,17 @@ __global__ __launch_bounds__(WAVES * 64, D == 256 ? 1 : 2) void attn_fwd_dma_ker
     part = r / a.hq;
     const int j = r - part * a.hq;
     h = (j & 7) * (a.hq >> 3) + (j >> 3);
+  } else if (a.xcd_remap == 3) {
+    // (sequence, head) units dealt round-robin to the XCDs, all blocks of a
+    // unit in a row on its XCD (no split parts in this order)
+    const int local = id >> 3;
+    const int u = local / a.n_qb;
+    qb_rev = local - u * a.n_qb;
+    const int p = u * 8 + (id & 7);
+    if (p >= a.nseq * a.hq) return;
+    seq = p / a.hq;
+    h = p - seq * a.hq;
+    part = 0;
   } else {
     const int rows = a.nseq * a.hq;
     const int per_qb = rows * a.n_split;
@@ -1329,9 +1340,20 @@ __global__ __launch_bounds__(WAVES * 64, MINW) void attn_fwd_pipe_kernel(const A
 
   const int rows = a.nseq * a.hq;
   const int id = blockIdx.x;
-  const int qb_rev = id / rows;
-  int p = id - qb_rev * rows;
-  if (a.xcd_remap) p = (p & 7) * (rows >> 3) + (p >> 3);
+  int qb_rev, p;
+  if (a.xcd_remap == 3) {
+    // (sequence, head) units dealt round-robin to the XCDs; all blocks of a
+    // unit in a row on its XCD, so they read its K/V from that L2
+    const int local = id >> 3;
+    const int u = local / a.n_qb;
+    qb_rev = local - u * a.n_qb;
+    p = u * 8 + (id & 7);
+    if (p >= rows) return;
+  } else {
+    qb_rev = id / rows;
+    p = id - qb_rev * rows;
+    if (a.xcd_remap) p = (p & 7) * (rows >> 3) + (p >> 3);
+  }
   const int seq = p / a.hq;
   const int h = p - seq * a.hq;
   const int qb = a.causal ? (a.n_qb - 1 - qb_rev) : qb_rev;
@@ -1661,7 +1683,8 @@ constexpr int minw_for() { return D == 256 ? 1 : 2; }
 template <int D, bool VARLEN>
 hipError_t launch_d(const AttnArgs& a, int policy_id, hipStream_t stream) {
   const int64_t rows = (int64_t)a.nseq * a.hq;
-  const int64_t grid = rows * a.n_qb * a.n_split;
+  // unit-major order deals (sequence, head) units to the 8 XCDs: whole rounds of 8
+  const int64_t grid = (a.xcd_remap == 3 ? (rows + 7) / 8 * 8 : rows) * a.n_qb * a.n_split;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   const dim3 g((unsigned)grid);
