@@ -196,11 +196,11 @@ def test_future_perturbation_leaves_prefix_bitwise():
 
 
 # Policies the library does not compile for a head_dim (register or LDS budget).
-NOT_COMPILED = {256: {"2", "8", "9", "10", "11", "12", "14", "15", "16", "17"},
-                32: {"11", "14", "15", "16"}}
+NOT_COMPILED = {256: {"2", "8", "9", "10", "11", "12", "14", "15", "16", "17", "18"},
+                32: {"11", "14", "15", "16", "18"}}
 
 
-@pytest.mark.parametrize("policy", [str(i) for i in range(18)])
+@pytest.mark.parametrize("policy", [str(i) for i in range(19)])
 @pytest.mark.parametrize("causal", [True, False])
 def test_every_compiled_tile_policy(policy, causal):
     os.environ["ATTN_FWD_TILE"] = policy
@@ -216,6 +216,19 @@ def test_every_compiled_tile_policy(policy, causal):
             check_lse(lse, lse_ref)
     finally:
         del os.environ["ATTN_FWD_TILE"]
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_default_policy_one_round_of_64_query_blocks(causal):
+    # head_dim 128, >= 512 queries and at most 256 blocks of 64 queries: the
+    # default is the four-key-group policy (its merge runs in two rounds)
+    assert "ATTN_FWD_TILE" not in os.environ
+    w = gen.make_varlen("kg4", 1210, [1024, 700], 4, 2, 128, causal)
+    o, lse = run_varlen(w)
+    o_ref, lse_ref = oracle.attention_varlen(w.q, w.k, w.v, w.cu_seqlens_q, w.cu_seqlens_k,
+                                             w.scale, causal)
+    check_o(o, o_ref)
+    check_lse(lse, lse_ref)
 
 
 # ----------------------------------------------------------------------------- gather / scatter

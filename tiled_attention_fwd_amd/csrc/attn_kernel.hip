@@ -836,7 +836,7 @@ __device__ __forceinline__ int swz_v(int row) {
 template <int D, int WAVES, int KG, int NBUF, bool VARLEN, int SUB = 1>
 __global__ __launch_bounds__(WAVES * 64, D == 256 ? 1 : 2) void attn_fwd_dma_kernel(const AttnArgs a) {
   constexpr int NT = WAVES * 64;
-  constexpr int BN0 = D == 256 ? 32 : 64;    // keys per compute sub-tile
+  constexpr int BN0 = (D == 256 || KG == 4) ? 32 : 64;  // keys per compute sub-tile
   constexpr int BN = SUB * BN0;              // keys per DMA tile (one barrier each)
   constexpr int QW = WAVES / KG;
   constexpr int BM = QW * 32;
@@ -1130,35 +1130,54 @@ __global__ __launch_bounds__(WAVES * 64, D == 256 ? 1 : 2) void attn_fwd_dma_ker
 
   // ---- key-group merge (KG > 1): partial (m, l, O) through LDS ------------------
   if constexpr (KG > 1) {
-    static_assert(KG == 2, "merge written for two key groups");
+    static_assert(KG == 2 || KG == 4, "merge written for two or four key groups");
     constexpr int NREG = NDB * 16 + 2;
     static_assert(NREG * 64 * 4 <= KG * TILE * 2, "one wave's partial must fit one tile array");
-    static_assert(QW <= 4, "merge slots: ks0, vs0, ks1, vs1");
-    uint16_t* slot16 = qw == 0 ? ks0 : qw == 1 ? vs0 : qw == 2 ? ks1 : vs1;
-    float* slot = reinterpret_cast<float*>(slot16) + lane;  // [reg][lane]
-    if (kg == 1) {
+    static_assert(QW * (KG / 2) <= 4, "merge slots: ks0, vs0, ks1, vs1");
+    auto slot_of = [&](int i) {
+      uint16_t* s16 = i == 0 ? ks0 : i == 1 ? vs0 : i == 2 ? ks1 : vs1;
+      return reinterpret_cast<float*>(s16) + lane;  // [reg][lane]
+    };
+    auto put = [&](float* slot) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) slot[(db * 16 + r) * 64] = oacc[db][r];
       slot[(NDB * 16) * 64] = m_run;
       slot[(NDB * 16 + 1) * 64] = l_run;
+    };
+    auto take = [&](const float* slot) {
+      const float m_o = slot[(NDB * 16) * 64];
+      const float l_o = slot[(NDB * 16 + 1) * 64];
+      const float m_new = fmaxf(m_run, m_o);
+      const float m_ref = m_new == -INFINITY ? 0.f : m_new;
+      const float a_self = __builtin_amdgcn_exp2f(m_run - m_ref);
+      const float a_other = __builtin_amdgcn_exp2f(m_o - m_ref);
+      m_run = m_new;
+      l_run = l_run * a_self + l_o * a_other;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          oacc[db][r] = oacc[db][r] * a_self + slot[(db * 16 + r) * 64] * a_other;
+    };
+    if constexpr (KG == 4) {
+      // groups 2 and 3 hand their partials to groups 0 and 1
+      if (kg >= 2) put(slot_of((kg - 2) * QW + qw));
+      __syncthreads();
+      if (kg >= 2) return;
+      take(slot_of(kg * QW + qw));
+      // then group 1 to group 0, through the slot group 1 has just read
+      if (kg == 1) put(slot_of(QW + qw));
+      __syncthreads();
+      if (kg == 1) return;
+      take(slot_of(QW + qw));
+    } else {
+      if (kg == 1) put(slot_of(qw));
+      __syncthreads();
+      if (kg == 1) return;
+      take(slot_of(qw));
     }
-    __syncthreads();
-    if (kg == 1) return;
-    const float m_o = slot[(NDB * 16) * 64];
-    const float l_o = slot[(NDB * 16 + 1) * 64];
-    const float m_new = fmaxf(m_run, m_o);
-    const float m_ref = m_new == -INFINITY ? 0.f : m_new;
-    const float a_self = __builtin_amdgcn_exp2f(m_run - m_ref);
-    const float a_other = __builtin_amdgcn_exp2f(m_o - m_ref);
-    m_run = m_new;
-    l_run = l_run * a_self + l_o * a_other;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        oacc[db][r] = oacc[db][r] * a_self + slot[(db * 16 + r) * 64] * a_other;
   }
 
   const float lt = half_sum(l_run);
@@ -1673,7 +1692,7 @@ __global__ __launch_bounds__(WAVES * 64, MINW) void attn_fwd_pipe_kernel(const A
 //  16: as 15 with four buffers
 //  17: DMA-staged kernel, 8 waves (BM 256), 128-key DMA tiles computed as two
 //      64-key sub-tiles (one barrier per 128 keys), two buffers
-constexpr int kNumPolicies = 18;
+constexpr int kNumPolicies = 19;
 
 template <int D>
 constexpr int bn_for() { return D == 256 ? 32 : 64; }
@@ -1780,6 +1799,13 @@ hipError_t launch_d(const AttnArgs& a, int policy_id, hipStream_t stream) {
                              stream, a);
       }
       break;
+    case 18:
+      if constexpr (D == 32 || D == 256) {
+        return hipErrorInvalidValue;
+      } else {
+        hipLaunchKernelGGL((attn_fwd_dma_kernel<D, 8, 4, 2, VARLEN>), g, dim3(512), 0, stream, a);
+      }
+      break;
     case 17:
       if constexpr (D == 256) {
         return hipErrorInvalidValue;
@@ -1807,14 +1833,15 @@ bool select_policy(int head_dim, int max_seqlen_q, bool causal, int64_t rows, in
                                                   {8, 1, 64}, {8, 1, 64, 2}, {8, 1, 32, 4},
                                                   {8, 1, 64}, {8, 1, 64, 2}, {4, 1, 64},
                                                   {8, 1, 64}, {4, 1, 32}, {4, 1, 32},
-                                                  {8, 1, 128}};
+                                                  {8, 1, 128}, {8, 1, 32, 4}};
   int id;
   if (override_id >= 0) {
     if (override_id >= kNumPolicies) return false;
     if (head_dim == 256 && (override_id == 2 || (override_id >= 8 && override_id <= 12) ||
                             override_id >= 14))
       return false;  // not compiled (register or LDS budget)
-    if (head_dim == 32 && (override_id == 11 || (override_id >= 14 && override_id <= 16)))
+    if (head_dim == 32 && (override_id == 11 || (override_id >= 14 && override_id <= 16) ||
+                           override_id == 18))
       return false;
     id = override_id;
   } else {
@@ -1830,6 +1857,9 @@ bool select_policy(int head_dim, int max_seqlen_q, bool causal, int64_t rows, in
       id = 0;
     } else if (head_dim == 128 && max_seqlen_q >= 256 && wg256 >= 256) {
       id = 11;
+    } else if (head_dim == 128 && max_seqlen_q >= 512 &&
+               rows * ((max_seqlen_q + 63) / 64) <= 256) {
+      id = 18;  // at most one round of 64-query blocks: four key groups shorten the longest
     } else if (head_dim == 128 && max_seqlen_q >= 512) {
       id = 12;
     } else if (head_dim == 64 && !causal && max_seqlen_q >= 256 && wg256 >= 256) {
