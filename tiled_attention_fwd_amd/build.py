@@ -30,6 +30,14 @@ COMMON_FLAGS = [
 ]
 
 
+# Per-source flags.  The forward kernels that need more than 256 registers
+# (head_dim 256, 1 wave per SIMD) would otherwise get MFMA accumulators in
+# AGPRs, and every score then costs a copy back to a VGPR for the softmax;
+# VGPR-form MFMAs keep scores and outputs in VGPRs and spill only a few
+# long-lived operands (head_dim 256 DMA kernel: ~900 -> ~50 AGPR copies).
+EXTRA_FLAGS = {"attn_kernel.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -39,7 +47,8 @@ def hipcc() -> str:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *COMMON_FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *COMMON_FLAGS, *EXTRA_FLAGS.get(src, []), "-x", "hip", "-c",
+           os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
