@@ -30,11 +30,13 @@ COMMON_FLAGS = [
 ]
 
 
-# Per-source flags.  The forward kernels that need more than 256 registers
-# (head_dim 256, 1 wave per SIMD) would otherwise get MFMA accumulators in
-# AGPRs, and every score then costs a copy back to a VGPR for the softmax;
-# VGPR-form MFMAs keep scores and outputs in VGPRs and spill only a few
-# long-lived operands (head_dim 256 DMA kernel: ~900 -> ~50 AGPR copies).
+# Per-source flags.  Forward kernels that need more than 256 registers (head
+# dim 256, one wave per SIMD) would otherwise get MFMA accumulators in AGPRs,
+# and every score then costs a copy back to a VGPR for the softmax; VGPR-form
+# MFMAs keep scores and outputs in VGPRs and spill only a few long-lived
+# operands (head_dim 256 DMA kernel: ~900 -> ~50 AGPR copies per two tiles).
+# Not for the backward: its dK/dV accumulators are touched by MFMAs only, and
+# keeping them in AGPRs measured faster (1x8192: 1357 vs 1468 us).
 EXTRA_FLAGS = {"attn_kernel.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
