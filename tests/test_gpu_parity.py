@@ -231,6 +231,30 @@ def test_default_policy_one_round_of_64_query_blocks(causal):
     check_lse(lse, lse_ref)
 
 
+@pytest.mark.parametrize("hq,hkv", [(8, 2), (12, 4)])
+def test_multi_sequence_block_orders_varlen(hq, hkv):
+    # several sequences on the DMA-staged kernel: sequence-major order when
+    # hq % 8 == 0, unit-major order otherwise
+    assert "ATTN_FWD_TILE" not in os.environ
+    w = gen.make_varlen(f"ord{hq}", 1300 + hq, [700, 300, 1100], hq, hkv, 128, True)
+    o, lse = run_varlen(w)
+    o_ref, lse_ref = oracle.attention_varlen(w.q, w.k, w.v, w.cu_seqlens_q, w.cu_seqlens_k,
+                                             w.scale, True)
+    check_o(o, o_ref)
+    check_lse(lse, lse_ref)
+
+
+def test_multi_sequence_block_order_pipelined_dense_batch():
+    # a batch on the software-pipelined kernel (head_dim 64, non-causal, enough
+    # blocks): unit-major order, with a grid padded to whole rounds of 8 units
+    assert "ATTN_FWD_TILE" not in os.environ
+    w = gen.make_dense("ordp", 1320, 6, 1024, 1024, 12, 12, 64, False)
+    o, lse = run_dense(w)
+    o_ref, lse_ref = oracle.attention_dense(w.q, w.k, w.v, w.scale, False)
+    check_o(o, o_ref)
+    check_lse(lse, lse_ref)
+
+
 # ----------------------------------------------------------------------------- gather / scatter
 def test_gather_scatter_bit_exact_with_nan_bits_and_bad_index():
     import torch
