@@ -1692,6 +1692,8 @@ __global__ __launch_bounds__(WAVES * 64, MINW) void attn_fwd_pipe_kernel(const A
 //  16: as 15 with four buffers
 //  17: DMA-staged kernel, 8 waves (BM 256), 128-key DMA tiles computed as two
 //      64-key sub-tiles (one barrier per 128 keys), two buffers
+//  18: DMA-staged kernel, 8 waves = 2 query waves x 4 key groups (BM 64),
+//      32-key tiles, two buffers; the groups merge in two rounds
 constexpr int kNumPolicies = 19;
 
 template <int D>
