@@ -196,11 +196,12 @@ def test_future_perturbation_leaves_prefix_bitwise():
 
 
 # Policies the library does not compile for a head_dim (register or LDS budget).
-NOT_COMPILED = {256: {"2", "8", "9", "10", "11", "12", "14", "15", "16", "17", "18"},
-                32: {"11", "14", "15", "16", "18"}}
+NOT_COMPILED = {256: {"2", "8", "9", "10", "11", "12", "14", "15", "16", "17", "18", "19"},
+                64: {"19"},
+                32: {"11", "14", "15", "16", "18", "19"}}
 
 
-@pytest.mark.parametrize("policy", [str(i) for i in range(19)])
+@pytest.mark.parametrize("policy", [str(i) for i in range(20)])
 @pytest.mark.parametrize("causal", [True, False])
 def test_every_compiled_tile_policy(policy, causal):
     os.environ["ATTN_FWD_TILE"] = policy
@@ -220,8 +221,8 @@ def test_every_compiled_tile_policy(policy, causal):
 
 @pytest.mark.parametrize("causal", [True, False])
 def test_default_policy_one_round_of_64_query_blocks(causal):
-    # head_dim 128, >= 512 queries and at most 256 blocks of 64 queries: the
-    # default is the four-key-group policy (its merge runs in two rounds)
+    # head_dim 128, 512..4096 queries and at most 512 blocks of 64 queries:
+    # the default is the four-key-group policy (its merge runs in two rounds)
     assert "ATTN_FWD_TILE" not in os.environ
     w = gen.make_varlen("kg4", 1210, [1024, 700], 4, 2, 128, causal)
     o, lse = run_varlen(w)
@@ -298,7 +299,7 @@ def test_scatter_search_sizes(n_valid, n_rows):
 
 
 # ----------------------------------------------------------------------------- split key ranges
-SPLIT_POLICIES = ["11", "12", "13", "17"]
+SPLIT_POLICIES = ["11", "12", "13", "17", "19"]
 
 
 def _forced_split(policy, tiles):
@@ -385,7 +386,8 @@ def test_padded_path_full_size(name, use_ws):
     idx = dev_i32(w.indices)
     qc, kc, vc = t.attn_unpad_gather([dev_bf16(w.q), dev_bf16(w.k), dev_bf16(w.v)], idx)
     ws = None
-    if use_ws:  # split path at full size: parts of at most 8 key tiles
+    if use_ws:  # split path at full size: policy 12, parts of at most 8 key tiles
+        os.environ["ATTN_FWD_TILE"] = "12"
         os.environ["ATTN_FWD_SPLIT_TILES"] = "8"
     try:
         if use_ws:
@@ -395,6 +397,7 @@ def test_padded_path_full_size(name, use_ws):
                                    w.max_seqlen, scale=float(w.scale), causal=True, workspace=ws)
     finally:
         os.environ.pop("ATTN_FWD_SPLIT_TILES", None)
+        os.environ.pop("ATTN_FWD_TILE", None)
     padded = t.attn_pad_scatter(o, idx, w.q.shape[1], out_shape=(1,) + w.q.shape[1:])
     # the oracle: gather, attention, scatter
     hd = w.q.shape[2:]

@@ -43,7 +43,7 @@ int split_override() {
   return (int)v;
 }
 
-// Key-range split of long query blocks (DMA-staged policies 11-13 only).  A
+// Key-range split of long query blocks (DMA-staged policies 11-13, 17, 19).  A
 // causal launch with few blocks is bound by its longest block: the last query
 // block walks the whole key range while most CUs sit idle.  The plan cuts a
 // block's key loop into parts of about the per-CU share of all tiles, so no
@@ -60,7 +60,7 @@ SplitPlan plan_split(const TilePolicy& pol, int pid, int64_t rows, int n_qb, int
   SplitPlan sp;
   sp.bm = pol.bm();
   sp.bn = pol.bn;
-  if (!(pid >= 11 && pid <= 13) && pid != 17) return sp;
+  if (!(pid >= 11 && pid <= 13) && pid != 17 && pid != 19) return sp;
   const int64_t bm = pol.bm(), bn = pol.bn;
   const int64_t max_tiles = (max_q + bn - 1) / bn;
   int64_t total = 0;  // key tiles summed over the blocks of one (sequence, head)
@@ -122,7 +122,7 @@ attn_status_t launch(AttnArgs& a, int d, bool varlen, int max_q, void* ws, int64
   // Several sequences (or a batch) on the DMA-staged kernel: sequence-major
   // workgroup order, so the workgroups an XCD runs at once share a few heads'
   // K/V in its L2 (a 64K-token pack of 17 sequences: 2072 -> 1406 us).
-  const bool dma_kernel = (pid >= 11 && pid <= 13) || pid == 17;
+  const bool dma_kernel = (pid >= 11 && pid <= 13) || pid >= 17;
   const bool pipe_kernel = pid >= 14 && pid <= 16;
   if (dma_kernel && a.nseq > 1 && a.hq % 8 == 0) a.xcd_remap = 2;
   // Otherwise, on several sequences: unit-major order, every block of one
