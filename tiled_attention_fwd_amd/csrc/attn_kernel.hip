@@ -1696,7 +1696,8 @@ __global__ __launch_bounds__(WAVES * 64, MINW) void attn_fwd_pipe_kernel(const A
 //      32-key tiles, two buffers; the groups merge in two rounds
 //  19: DMA-staged kernel, 8 waves (BM 256), 128-key tiles (one softmax pass
 //      and one barrier per 128 keys), two buffers
-constexpr int kNumPolicies = 20;
+//  20: as 19 with 4 waves (BM 128), two workgroups per CU
+constexpr int kNumPolicies = 21;
 
 template <int D>
 constexpr int bn_for() { return D == 256 ? 32 : 64; }
@@ -1811,10 +1812,17 @@ hipError_t launch_d(const AttnArgs& a, int policy_id, hipStream_t stream) {
       }
       break;
     case 19:
-      if constexpr (D != 128) {
+      if constexpr (D == 256) {
         return hipErrorInvalidValue;
       } else {
         hipLaunchKernelGGL((attn_fwd_dma_kernel<D, 8, 1, 2, VARLEN, 1, 1>), g, dim3(512), 0, stream, a);
+      }
+      break;
+    case 20:
+      if constexpr (D == 256) {
+        return hipErrorInvalidValue;
+      } else {
+        hipLaunchKernelGGL((attn_fwd_dma_kernel<D, 4, 1, 2, VARLEN, 1, 1>), g, dim3(256), 0, stream, a);
       }
       break;
     case 17:
@@ -1844,7 +1852,7 @@ bool select_policy(int head_dim, int max_seqlen_q, bool causal, int64_t rows, in
                                                   {8, 1, 64}, {8, 1, 64, 2}, {8, 1, 32, 4},
                                                   {8, 1, 64}, {8, 1, 64, 2}, {4, 1, 64},
                                                   {8, 1, 64}, {4, 1, 32}, {4, 1, 32},
-                                                  {8, 1, 128}, {8, 1, 32, 4}, {8, 1, 128}};
+                                                  {8, 1, 128}, {8, 1, 32, 4}, {8, 1, 128}, {4, 1, 128}};
   int id;
   if (override_id >= 0) {
     if (override_id >= kNumPolicies) return false;
@@ -1854,7 +1862,7 @@ bool select_policy(int head_dim, int max_seqlen_q, bool causal, int64_t rows, in
     if (head_dim == 32 && (override_id == 11 || (override_id >= 14 && override_id <= 16) ||
                            override_id == 18))
       return false;
-    if (override_id == 19 && head_dim != 128) return false;
+    if (override_id >= 19 && head_dim == 256) return false;
     id = override_id;
   } else {
     // Chosen from measured sweeps over the workload set (dense, varlen,
@@ -1877,7 +1885,7 @@ bool select_policy(int head_dim, int max_seqlen_q, bool causal, int64_t rows, in
     } else if (head_dim == 128 && max_seqlen_q >= 512) {
       id = 12;
     } else if (head_dim == 64 && !causal && max_seqlen_q >= 256 && wg256 >= 256) {
-      id = 14;
+      id = 20;  // ViT batch (149 x 12 heads, S1024): 650 us vs 718 on 14
     } else {
       id = 13;
     }
