@@ -115,6 +115,34 @@ def test_dense_strided_views():
     check_lse(host(lse), lse_ref)
 
 
+@pytest.mark.parametrize("policy", ["18", "19", "20"])
+def test_newer_dma_policies_dense_lq_ne_lk_and_strided(policy):
+    # the four-key-group and 128-key-tile policies on the dense layout:
+    # bottom-right causal with Lk > Lq and Lk < Lq, then BHSD storage viewed
+    # as BSHD (non-contiguous strides) with a strided output
+    import torch
+    t = api()
+    os.environ["ATTN_FWD_TILE"] = policy
+    try:
+        for sq, sk in ((300, 520), (520, 300)):
+            w = gen.make_dense(f"nd{sq}", 1700 + sq, 2, sq, sk, 4, 2, 128, True)
+            o, lse = run_dense(w)
+            o_ref, lse_ref = oracle.attention_dense(w.q, w.k, w.v, w.scale, True)
+            check_o(o, o_ref)
+            check_lse(lse, lse_ref)
+        w = gen.make_dense("ns", 1750, 2, 300, 300, 4, 4, 64, False)
+        q = dev_bf16(np.ascontiguousarray(w.q.transpose(0, 2, 1, 3))).permute(0, 2, 1, 3)
+        k = dev_bf16(np.ascontiguousarray(w.k.transpose(0, 2, 1, 3))).permute(0, 2, 1, 3)
+        v = dev_bf16(np.ascontiguousarray(w.v.transpose(0, 2, 1, 3))).permute(0, 2, 1, 3)
+        out = torch.empty((2, 4, 300, 64), dtype=torch.float32, device="cuda").permute(0, 2, 1, 3)
+        o, lse = t.attn_fwd_dense(q, k, v, scale=float(w.scale), causal=False, out=out)
+        o_ref, lse_ref = oracle.attention_dense(w.q, w.k, w.v, w.scale, False)
+        check_o(host(o.contiguous()), o_ref)
+        check_lse(host(lse), lse_ref)
+    finally:
+        del os.environ["ATTN_FWD_TILE"]
+
+
 # ----------------------------------------------------------------------------- closed forms on GPU
 @pytest.mark.parametrize("d", [64, 128])
 def test_zero_query_gives_prefix_mean_and_log_count(d):
