@@ -1871,10 +1871,12 @@ bool select_policy(int head_dim, int max_seqlen_q, bool causal, int64_t rows, in
     // to fill the chip; with fewer, two key groups per block halve the serial
     // key loop of the longest (causal) blocks.
     const int64_t wg256 = rows * ((max_seqlen_q + 255) / 256);
-    if (max_seqlen_q <= 64) {
+    if (head_dim == 128 && max_seqlen_q <= 128) {
+      // short packed sequences: the DMA-staged 128-query block (32 x 64:
+      // 11.0 us vs 11.5 on 1; 32 slots of U{1..128}: 12.5 vs 13.8 on 0)
+      id = 13;
+    } else if (max_seqlen_q <= 64) {
       id = 1;  // one 64-query block covers every sequence
-    } else if (head_dim == 128 && max_seqlen_q <= 128) {
-      id = 0;
     } else if (head_dim == 128 && max_seqlen_q >= 256 && wg256 >= 256) {
       id = 19;  // 128-key tiles: half the barriers and softmax passes of 11, 1-2 % faster
     } else if (head_dim == 128 && max_seqlen_q >= 512 && max_seqlen_q <= 4096 &&
