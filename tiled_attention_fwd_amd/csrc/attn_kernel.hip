@@ -1866,10 +1866,14 @@ bool select_policy(int head_dim, int max_seqlen_q, bool causal, int64_t rows, in
     id = override_id;
   } else {
     // Chosen from measured sweeps over the workload set (dense, varlen,
-    // packed, grouped heads; head_dim 32..256).  256-query blocks share one
-    // K/V tile among eight waves but need at least one workgroup per CU (256)
-    // to fill the chip; with fewer, two key groups per block halve the serial
-    // key loop of the longest (causal) blocks.
+    // packed, grouped heads; head_dim 32..256) and a grid of one causal
+    // sequence of 1K..8K tokens with 8..64 heads.  Large blocks share one K/V
+    // tile among more waves but need at least two rounds of workgroups over
+    // the 256 CUs: with a single round the longest causal blocks run alone at
+    // the end.  With fewer blocks, key groups (18) or split key loops (12)
+    // shorten the longest.
+    const int64_t wg64 = rows * ((max_seqlen_q + 63) / 64);
+    const int64_t wg128 = rows * ((max_seqlen_q + 127) / 128);
     const int64_t wg256 = rows * ((max_seqlen_q + 255) / 256);
     if (head_dim == 128 && max_seqlen_q <= 128) {
       // short packed sequences: the DMA-staged 128-query block (32 x 64:
@@ -1877,17 +1881,23 @@ bool select_policy(int head_dim, int max_seqlen_q, bool causal, int64_t rows, in
       id = 13;
     } else if (max_seqlen_q <= 64) {
       id = 1;  // one 64-query block covers every sequence
-    } else if (head_dim == 128 && max_seqlen_q >= 256 && wg256 >= 256) {
-      id = 19;  // 128-key tiles: half the barriers and softmax passes of 11, 1-2 % faster
+    } else if (head_dim == 128 && max_seqlen_q >= 256 && wg256 >= 512) {
+      id = 19;  // 128-key tiles: half the barriers and softmax passes of 11
     } else if (head_dim == 128 && max_seqlen_q >= 512 && max_seqlen_q <= 4096 &&
-               rows * ((max_seqlen_q + 63) / 64) <= 512) {
+               (wg64 <= 256 || (wg64 <= 512 && max_seqlen_q >= 2048))) {
       // at most two rounds of 64-query blocks: four key groups shorten the
-      // longest (longer sequences split their key loop on policy 12 instead)
+      // longest (S2048 x 16 heads 34 us; S4096 x 8 heads 53 us vs 58 on 12)
       id = 18;
+    } else if (head_dim == 128 && max_seqlen_q <= 1024 && wg128 >= 512) {
+      id = 13;  // S1024 x 64 heads: 31 us vs 35 on 12 and 19
     } else if (head_dim == 128 && max_seqlen_q >= 512) {
-      id = 12;
-    } else if (head_dim == 64 && !causal && max_seqlen_q >= 256 && wg256 >= 256) {
-      id = 20;  // ViT batch (149 x 12 heads, S1024): 650 us vs 718 on 14
+      id = 12;  // S4096 x 16 heads: 79 us vs 98 on 19; S8192 x 8 heads 142 vs 183
+    } else if (head_dim == 64 && max_seqlen_q >= 256 &&
+               (causal ? wg128 <= 1024 : wg256 >= 256)) {
+      // ViT batch (149 x 12 heads, S1024): 650 us vs 718 on 14; causal with
+      // at most four rounds of 128-query blocks: S1024 x 16 heads 16 us vs 23
+      // on 13 (with more blocks 13 is up to 8 % faster)
+      id = 20;
     } else {
       id = 13;
     }
