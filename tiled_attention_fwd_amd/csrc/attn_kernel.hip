@@ -1865,13 +1865,15 @@ bool select_policy(int head_dim, int max_seqlen_q, bool causal, int64_t rows, in
     if (override_id >= 19 && head_dim == 256) return false;
     id = override_id;
   } else {
-    // Chosen from measured sweeps over the workload set (dense, varlen,
-    // packed, grouped heads; head_dim 32..256) and a grid of one causal
-    // sequence of 1K..8K tokens with 8..64 heads.  Large blocks share one K/V
-    // tile among more waves but need at least two rounds of workgroups over
-    // the 256 CUs: with a single round the longest causal blocks run alone at
-    // the end.  With fewer blocks, key groups (18) or split key loops (12)
-    // shorten the longest.
+    // Chosen from measured sweeps: the workload set (dense, varlen, packed,
+    // grouped heads; head_dim 32..256) and grids of one sequence of 1K..8K
+    // tokens with 8..64 heads, causal and not, per head_dim.  Large blocks
+    // share one K/V tile among more waves but, causal, need at least two
+    // rounds of workgroups over the 256 CUs: with a single round the longest
+    // causal blocks run alone at the end (non-causal blocks all cost the same,
+    // so one full round is enough).  With fewer blocks, key groups (18),
+    // split key loops (12) or 128-key tiles at four waves (20) shorten the
+    // critical path.
     const int64_t wg64 = rows * ((max_seqlen_q + 63) / 64);
     const int64_t wg128 = rows * ((max_seqlen_q + 127) / 128);
     const int64_t wg256 = rows * ((max_seqlen_q + 255) / 256);
@@ -1881,25 +1883,39 @@ bool select_policy(int head_dim, int max_seqlen_q, bool causal, int64_t rows, in
       id = 13;
     } else if (max_seqlen_q <= 64) {
       id = 1;  // one 64-query block covers every sequence
-    } else if (head_dim == 128 && max_seqlen_q >= 256 && wg256 >= 512) {
-      id = 19;  // 128-key tiles: half the barriers and softmax passes of 11
-    } else if (head_dim == 128 && max_seqlen_q >= 512 && max_seqlen_q <= 4096 &&
-               (wg64 <= 256 || (wg64 <= 512 && max_seqlen_q >= 2048))) {
-      // at most two rounds of 64-query blocks: four key groups shorten the
-      // longest (S2048 x 16 heads 34 us; S4096 x 8 heads 53 us vs 58 on 12)
-      id = 18;
-    } else if (head_dim == 128 && max_seqlen_q <= 1024 && wg128 >= 512) {
-      id = 13;  // S1024 x 64 heads: 31 us vs 35 on 12 and 19
-    } else if (head_dim == 128 && max_seqlen_q >= 512) {
-      id = 12;  // S4096 x 16 heads: 79 us vs 98 on 19; S8192 x 8 heads 142 vs 183
-    } else if (head_dim == 64 && max_seqlen_q >= 256 &&
-               (causal ? wg128 <= 1024 : wg256 >= 256)) {
-      // ViT batch (149 x 12 heads, S1024): 650 us vs 718 on 14; causal with
-      // at most four rounds of 128-query blocks: S1024 x 16 heads 16 us vs 23
-      // on 13 (with more blocks 13 is up to 8 % faster)
-      id = 20;
-    } else {
+    } else if (max_seqlen_q < 256) {
       id = 13;
+    } else if (head_dim == 128) {
+      const bool few64 = max_seqlen_q >= 512 && max_seqlen_q <= 4096 &&
+                         (wg64 <= 256 || (causal && wg64 <= 512 && max_seqlen_q >= 2048));
+      if (wg256 >= (causal ? 512 : 256))
+        id = 19;  // 128-key tiles: half the barriers and softmax passes of 11
+      else if (few64)
+        id = 18;  // S2048 x 16 heads causal 34 us; S4096 x 8 heads 53 vs 58 on 12
+      else if (causal && max_seqlen_q <= 1024 && wg128 >= 512)
+        id = 13;  // S1024 x 64 heads causal: 31 us vs 35 on 12 and 19
+      else if (max_seqlen_q >= 512)
+        id = 12;  // S4096 x 16 heads causal: 79 us vs 98 on 19
+      else
+        id = 13;
+    } else if (head_dim == 64) {
+      if (causal)  // S1024 x 16 heads: 16 us vs 23 on 13; with more blocks 13 is up to 8 % faster
+        id = wg128 <= 1024 ? 20 : 13;
+      else  // S1024 x 8 heads: 15 us vs 24 on 13; ViT batch (149 x 12 heads, S1024) 593 vs 650 on 19
+        id = wg256 < 256 ? 20 : wg256 < 512 ? 19 : 13;
+    } else if (head_dim == 32) {
+      // S1024 x 16 heads causal: 12 us vs 17 on 13; S8192 x 64 heads 402 vs 449
+      id = wg256 >= (causal ? 1024 : 256) ? 19 : 20;
+    } else {
+      // head_dim 256: eight waves (3) once the blocks fill the CUs several
+      // times; four-wave staged blocks (0) when they fill about one round
+      // (S1024 x 32 heads causal 57 us vs 87 on 13)
+      if (wg128 >= (causal ? 1024 : 512))
+        id = 3;
+      else if (!causal || (wg128 > 128 && wg128 <= 256))
+        id = 0;
+      else
+        id = 13;
     }
   }
   *out = kTable[id];
