@@ -273,14 +273,65 @@ def test_multi_sequence_block_orders_varlen(hq, hkv):
 
 
 def test_multi_sequence_block_order_pipelined_dense_batch():
-    # a batch on the software-pipelined kernel (head_dim 64, non-causal, enough
-    # blocks): unit-major order, with a grid padded to whole rounds of 8 units
-    assert "ATTN_FWD_TILE" not in os.environ
-    w = gen.make_dense("ordp", 1320, 6, 1024, 1024, 12, 12, 64, False)
-    o, lse = run_dense(w)
+    # a batch on the software-pipelined kernel (policy 14, head_dim 64,
+    # non-causal): unit-major order, with a grid padded to whole rounds of 8 units
+    os.environ["ATTN_FWD_TILE"] = "14"
+    try:
+        w = gen.make_dense("ordp", 1320, 6, 1024, 1024, 12, 12, 64, False)
+        o, lse = run_dense(w)
+    finally:
+        os.environ.pop("ATTN_FWD_TILE", None)
     o_ref, lse_ref = oracle.attention_dense(w.q, w.k, w.v, w.scale, False)
     check_o(o, o_ref)
     check_lse(lse, lse_ref)
+
+
+# Shapes that reach each branch of the default tile selection (head_dim,
+# causal, number of workgroups per block size), run with a split workspace as
+# a caller that passes one would: (name, head_dim, causal, lengths, heads q/kv,
+# policy the selection picks).
+DEFAULT_BRANCHES = [
+    ("d32_c_few", 32, True, [300, 290], 4, 2, "20"),
+    ("d32_c_many", 32, True, [256] * 64, 16, 4, "19"),
+    ("d32_n_many", 32, False, [256] * 16, 16, 16, "19"),
+    ("d64_c_many", 64, True, [256] * 80, 8, 2, "13"),
+    ("d64_n_few", 64, False, [300, 290], 4, 2, "20"),
+    ("d64_n_mid", 64, False, [256] * 16, 16, 4, "19"),
+    ("d64_n_many", 64, False, [256] * 32, 16, 4, "13"),
+    ("d128_n_round", 128, False, [256] * 16, 16, 4, "19"),
+    ("d128_n_kg4", 128, False, [600], 4, 2, "18"),
+    ("d128_n_split", 128, False, [1024] * 4, 8, 2, "12"),
+    ("d128_c_1k", 128, True, [1024] * 4, 16, 4, "13"),
+    ("d256_c_many", 256, True, [256] * 64, 8, 2, "3"),
+    ("d256_c_round", 256, True, [256] * 16, 8, 2, "0"),
+    ("d256_n_few", 256, False, [300, 290], 4, 2, "0"),
+]
+
+
+@pytest.mark.parametrize("case", DEFAULT_BRANCHES, ids=[c[0] for c in DEFAULT_BRANCHES])
+def test_default_selection_branches(case):
+    name, d, causal, lens, hq, hkv, expect = case
+    assert "ATTN_FWD_TILE" not in os.environ
+    t = api()
+    w = gen.make_varlen(name, 1400 + d + len(lens), lens, hq, hkv, d, causal)
+    ws = t.workspace(len(lens), w.max_seqlen, hq, d, causal)
+    o, lse = t.attn_fwd_varlen(dev_bf16(w.q), dev_bf16(w.k), dev_bf16(w.v),
+                               dev_i32(w.cu_seqlens_q), dev_i32(w.cu_seqlens_k), w.max_seqlen,
+                               scale=float(w.scale), causal=causal, workspace=ws)
+    # the same call with the expected policy forced gives bit-identical output
+    os.environ["ATTN_FWD_TILE"] = expect
+    try:
+        o2, lse2 = t.attn_fwd_varlen(dev_bf16(w.q), dev_bf16(w.k), dev_bf16(w.v),
+                                     dev_i32(w.cu_seqlens_q), dev_i32(w.cu_seqlens_k),
+                                     w.max_seqlen, scale=float(w.scale), causal=causal,
+                                     workspace=ws)
+    finally:
+        os.environ.pop("ATTN_FWD_TILE", None)
+    o, lse, o2, lse2 = host(o), host(lse), host(o2), host(lse2)
+    assert np.array_equal(o, o2) and np.array_equal(lse, lse2), "default differs from policy " + expect
+    o_ref, lse_ref = oracle.attention_varlen(w.q, w.k, w.v, w.cu_seqlens_q, w.cu_seqlens_k,
+                                             w.scale, causal)
+    print(name, check_o(o, o_ref), check_lse(lse, lse_ref))
 
 
 # ----------------------------------------------------------------------------- gather / scatter
@@ -341,7 +392,7 @@ def _clear_forced():
 
 @pytest.mark.parametrize("policy", SPLIT_POLICIES)
 @pytest.mark.parametrize("causal", [True, False])
-@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("d", [32, 64, 128, 256])
 def test_split_key_ranges_varlen(policy, causal, d):
     """Key loops cut into parts of 1-3 tiles (several parts per block, uneven
     last parts, empty sequences, GQA) and merged, against the oracle."""
