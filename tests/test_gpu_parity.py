@@ -334,6 +334,68 @@ def test_default_selection_branches(case):
     print(name, check_o(o, o_ref), check_lse(lse, lse_ref))
 
 
+# Packs with one long sequence among many short ones (and empty ones): the
+# (sequence, head) x longest-block-count grid would be mostly empty, so the
+# library switches to the compact block order (one slot per real block).
+# The host rule (rows x blocks >= 4 x heads x (ceil(total_q / bm) + nseq))
+# holds for every case here with the default policy named in the comment.
+SKEWED_PACKS = [
+    ("d128_c", 128, True, [1500] + [20] * 60, 8, 2),         # 19, 256-query blocks
+    ("d128_n", 128, False, [20] * 30 + [1500] + [20] * 30, 8, 2),  # 19
+    ("d64_c_h12", 64, True, [1500] + [20] * 60 + [0, 0], 12, 4),   # 13, heads not a multiple of 8
+    ("d64_n_h12", 64, False, [0] + [20] * 60 + [1500], 12, 4),     # 13
+    ("d32_c", 32, True, [7] * 60 + [1500, 3], 8, 8),          # 19
+]
+
+
+@pytest.mark.parametrize("case", SKEWED_PACKS, ids=[c[0] for c in SKEWED_PACKS])
+def test_compact_block_order_skewed_pack(case):
+    name, d, causal, lens, hq, hkv = case
+    assert "ATTN_FWD_TILE" not in os.environ
+    w = gen.make_varlen("skew" + name, 1700 + d + hq, lens, hq, hkv, d, causal)
+    o, lse = run_varlen(w)
+    o_ref, lse_ref = oracle.attention_varlen(w.q, w.k, w.v, w.cu_seqlens_q, w.cu_seqlens_k,
+                                             w.scale, causal)
+    print(name, check_o(o, o_ref), check_lse(lse, lse_ref))
+
+
+def test_compact_block_order_fused_padded():
+    """The fused padded call on a skewed pack (compact order) equals the
+    three-call path bit for bit and matches the oracle."""
+    t = api()
+    r = np.random.Generator(np.random.PCG64(1750))
+    hq, hkv, d = 8, 2, 128
+    slots = [2048] + [32] * 60
+    lens = [1500] + [r.integers(0, 33) for _ in range(60)]
+    total = sum(slots)
+    mask = np.zeros(total, bool)
+    st = 0
+    for sl, L in zip(slots, lens):
+        mask[st:st + L] = True
+        st += sl
+    idx_h = np.flatnonzero(mask).astype(np.int32)
+    nz = [int(L) for L in lens if L > 0]
+    cu_h = gen.cu_seqlens_from_lengths(nz)
+    q = gen.normal_bf16(r, (1, total, hq, d))
+    k = gen.normal_bf16(r, (1, total, hkv, d))
+    v = gen.normal_bf16(r, (1, total, hkv, d))
+    scale = 1.0 / math.sqrt(d)
+    idx, cu = dev_i32(idx_h), dev_i32(cu_h)
+    qd, kd, vd = dev_bf16(q), dev_bf16(k), dev_bf16(v)
+    pf, lsef = t.attn_fwd_padded(qd, kd, vd, idx, cu, max(nz), scale=scale, causal=True)
+    (qc,) = t.attn_unpad_gather([qd], idx)  # q has more heads than k / v
+    kc, vc = t.attn_unpad_gather([kd, vd], idx)
+    o3, lse3 = t.attn_fwd_varlen(qc, kc, vc, cu, cu, max(nz), scale=scale, causal=True)
+    p3 = host(t.attn_pad_scatter(o3, idx, total, out_shape=(1, total, hq, d)))
+    pf = host(pf)
+    assert np.array_equal(pf.view(np.uint32), p3.view(np.uint32))
+    assert np.array_equal(host(lsef).view(np.uint32), host(lse3).view(np.uint32))
+    qg = [oracle.unpad_gather(x, idx_h, x.shape[2:]) for x in (q, k, v)]
+    o_ref, lse_ref = oracle.attention_varlen(qg[0], qg[1], qg[2], cu_h, cu_h, scale, True)
+    check_o(host(o3), o_ref)
+    check_lse(host(lse3), lse_ref)
+
+
 # ----------------------------------------------------------------------------- gather / scatter
 def test_gather_scatter_bit_exact_with_nan_bits_and_bad_index():
     import torch

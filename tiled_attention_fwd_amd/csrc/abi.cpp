@@ -140,6 +140,20 @@ attn_status_t launch(AttnArgs& a, int d, bool varlen, int max_q, void* ws, int64
     a.part_o = static_cast<float*>(ws);
     a.part_lse = a.part_o + rows * a.n_qb * sp.n_split * sp.bm * d;
   }
+  // A pack whose longest sequence is far above the rest (one long sequence
+  // with many short ones): the (sequence, head) x longest-block-count grid is
+  // then mostly workgroups with no block, each holding a CU slot while it
+  // reads cu_seqlens (1 x 8192 + 64 x 128, 16 heads: 383 us against 262 for
+  // the long sequence alone).  Compact order instead: sequence s owns block
+  // slots [cu_q[s] / bm + s, ...), at most ceil(total_q / bm) + nseq per head.
+  if (varlen && dma_kernel && a.nseq > 1 && a.n_split == 1) {
+    const int64_t bm = pol.bm();
+    const int64_t nv = (a.lse_hs + bm - 1) / bm + a.nseq;  // lse_hs: compact rows
+    if (rows * a.n_qb >= 4 * (int64_t)a.hq * nv && (int64_t)a.hq * nv <= 0x7fffffffLL) {
+      a.xcd_remap = 4;
+      a.n_vblk = (int32_t)nv;
+    }
+  }
   if (rows * a.n_qb * a.n_split > 0x7fffffffLL) return ATTN_ERR_SHAPE;
   hipError_t e = attnfwd::launch_attention(a, d, varlen, pid, stream);
   if (e == hipSuccess && a.n_split > 1) e = attnfwd::launch_merge(a, d, varlen, sp.bm, stream);

@@ -30,6 +30,7 @@ struct AttnArgs {
   int32_t nseq, hq, hkv, group;
   int32_t sq, sk;    // dense sequence lengths
   int32_t n_qb;      // query blocks per (sequence, head) in the grid
+  int32_t n_vblk;    // order 4: block slots per head, ceil(total_q / bm) + nseq
   float c;           // scale * log2(e): scores enter exp2 in base-2 units
   int32_t causal;
   int32_t xcd_remap; // 1: spread (sequence, head) rows so each XCD gets a contiguous slice;
@@ -38,6 +39,8 @@ struct AttnArgs {
                      // 3 (DMA-staged and pipelined kernels): (sequence, head) units
                      //   dealt to the XCDs, all blocks of a unit in a row (grid
                      //   padded to whole rounds of 8 units)
+                     // 4 (DMA-staged kernel, varlen): compact order, one workgroup
+                     //   slot per real query block (n_vblk slots per head)
   // Split key ranges (DMA-staged kernel only).  n_split == 1: off.  Otherwise
   // a query block whose key loop has more than split_tiles tiles of split_bn
   // keys is cut into up to n_split even parts; each part writes its

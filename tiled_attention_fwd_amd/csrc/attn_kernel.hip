@@ -878,6 +878,22 @@ __global__ __launch_bounds__(WAVES * 64, D == 256 ? 1 : 2) void attn_fwd_dma_ker
     part = r / a.hq;
     const int j = r - part * a.hq;
     h = (j & 7) * (a.hq >> 3) + (j >> 3);
+  } else if (VARLEN && a.xcd_remap == 4) {
+    // compact: sequence s owns block slots [cu_q[s] / BM + s, ...), disjoint and
+    // increasing in s; the workgroup finds its sequence by binary search.  The
+    // heads of one slot are consecutive, so each XCD keeps hq/8 fixed heads.
+    const int j = id % a.hq;
+    h = (a.hq % 8 == 0) ? (j & 7) * (a.hq >> 3) + (j >> 3) : j;
+    const int vb = id / a.hq;
+    int lo = 0, hi = a.nseq - 1;  // the last sequence whose first slot is <= vb
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (a.cu_q[mid] / BM + mid <= vb) lo = mid;
+      else hi = mid - 1;
+    }
+    seq = lo;
+    qb_rev = vb - (a.cu_q[seq] / BM + seq);  // block slot within the sequence
+    part = 0;
   } else if (a.xcd_remap == 3) {
     // (sequence, head) units dealt round-robin to the XCDs, all blocks of a
     // unit in a row on its XCD (no split parts in this order)
@@ -900,13 +916,19 @@ __global__ __launch_bounds__(WAVES * 64, D == 256 ? 1 : 2) void attn_fwd_dma_ker
     seq = p / a.hq;
     h = p - seq * a.hq;
   }
-  const int qb = a.causal ? (a.n_qb - 1 - qb_rev) : qb_rev;
+  int qb = a.causal ? (a.n_qb - 1 - qb_rev) : qb_rev;
   int lq, lk;
   int64_t qoff, koff, voff, ooff, lseoff;
   if constexpr (VARLEN) {
     const SeqRows sr = seq_rows(a, seq);
     lq = sr.lq;
     lk = sr.lk;
+    if (a.xcd_remap == 4) {
+      // slot qb_rev of this sequence's blocks, longest first when causal
+      const int nb = (lq + BM - 1) / BM;
+      if (qb_rev >= nb) return;
+      qb = a.causal ? nb - 1 - qb_rev : qb_rev;
+    }
     qoff = (int64_t)sr.q_row * a.q_ss;
     koff = (int64_t)sr.k_row * a.k_ss;
     voff = (int64_t)sr.k_row * a.v_ss;
@@ -1708,7 +1730,9 @@ template <int D, bool VARLEN>
 hipError_t launch_d(const AttnArgs& a, int policy_id, hipStream_t stream) {
   const int64_t rows = (int64_t)a.nseq * a.hq;
   // unit-major order deals (sequence, head) units to the 8 XCDs: whole rounds of 8
-  const int64_t grid = (a.xcd_remap == 3 ? (rows + 7) / 8 * 8 : rows) * a.n_qb * a.n_split;
+  const int64_t grid = a.xcd_remap == 4
+                           ? (int64_t)a.hq * a.n_vblk
+                           : (a.xcd_remap == 3 ? (rows + 7) / 8 * 8 : rows) * a.n_qb * a.n_split;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   const dim3 g((unsigned)grid);
