@@ -55,7 +55,7 @@ typedef enum {
   ATTN_OK = 0,
   ATTN_ERR_NULL = 1,        /* a required pointer is NULL */
   ATTN_ERR_SHAPE = 2,       /* a size is negative or sizes disagree */
-  ATTN_ERR_UNSUPPORTED = 3, /* head_dim not in {32,64,128,256}, scale <= 0 or not finite, ... */
+  ATTN_ERR_UNSUPPORTED = 3, /* head_dim not in {32,64,128,256}, scale not finite, ... */
   ATTN_ERR_ALIGN = 4,       /* a pointer or row size is not 16-byte aligned */
   ATTN_ERR_HIP = 5          /* the HIP runtime rejected the launch */
 } attn_status_t;
@@ -75,7 +75,10 @@ typedef enum {
  *      0, offsets never decrease, the last equals total_q (resp. total_k), and
  *      no query length exceeds max_seqlen.  Zero-length sequences are allowed.
  * max_seqlen: an upper bound on every query length (host value; sizes the grid).
- * scale: multiplies the raw scores q.k (use 1/sqrt(head_dim)); must be > 0 and finite.
+ * scale: multiplies the raw scores q.k (use 1/sqrt(head_dim)); any finite value.
+ *      A negative scale weights the smallest q.k highest; zero gives every
+ *      visible key the same weight (out = mean of the visible value rows,
+ *      lse = ln(number of visible keys)).
  * causal: nonzero => key j is visible to query i when j <= i + (Lk - Lq)
  *      (bottom-right alignment; with Lq == Lk this is j <= i).
  * out  (total_q, num_heads_q, head_dim) fp32, written once per element.
@@ -174,6 +177,39 @@ int64_t attn_fwd_workspace_bytes(int32_t num_seqs, int32_t max_seqlen, int32_t n
                                  int32_t head_dim, int32_t causal);
 
 /*
+ * attn_fwd_launch_plan -- how the library would launch a forward call.
+ *
+ * Passage: page "FlashAttention tuning: block_size and head_dim" (the block
+ * size is chosen per shape, from measurements; its checklist records the best
+ * configuration per sequence length).  This reports the choice for one shape
+ * so that sweeps and tests can see it.
+ *
+ * varlen: nonzero for attn_fwd_varlen (then total_q is the packed query count),
+ *      zero for attn_fwd_dense (num_seqs = batch, max_seqlen = seqlen_q).
+ * workspace_bytes: the workspace the _ws call would get (0: none).
+ * plan: host array of 4 int32 receiving {tile policy id, workgroup order, key-
+ *      range parts per query block (1 = no split), queries per block}.  Orders:
+ *      0 block-major, 1 block-major with (sequence, head) rows spread over the
+ *      XCDs, 2 sequence-major, 3 (sequence, head) units dealt to the XCDs, 4
+ *      compact (one workgroup slot per real query block of a varlen pack).
+ * The environment overrides ATTN_FWD_TILE (policy), ATTN_FWD_ORDER (order) and
+ * ATTN_FWD_SPLIT_TILES apply as they do to the calls.  Returns ATTN_ERR_SHAPE
+ * for non-positive sizes, ATTN_ERR_UNSUPPORTED for a head_dim, policy or
+ * order the library cannot use, ATTN_ERR_NULL when plan is NULL.  Pure host
+ * computation.
+ */
+attn_status_t attn_fwd_launch_plan(int32_t varlen, int32_t num_seqs, int32_t total_q,
+                                   int32_t max_seqlen, int32_t num_heads_q, int32_t head_dim,
+                                   int32_t causal, int64_t workspace_bytes, int32_t* plan);
+
+/*
+ * attn_fwd_tile_policy_compiled -- 1 if tile policy `policy` is compiled for
+ * head_dim (so ATTN_FWD_TILE=<policy> can force it), else 0.  Passage as for
+ * attn_fwd_launch_plan.  Pure host computation.
+ */
+int32_t attn_fwd_tile_policy_compiled(int32_t policy, int32_t head_dim);
+
+/*
  * attn_unpad_gather -- copy the rows named by `indices` into a compact tensor.
  *
  * Passage: page "Lesson 5: IAW model FA2 vs FA3 measured", section 1 (unpad:
@@ -212,6 +248,9 @@ attn_status_t attn_unpad_gather(const void* const* src, void* const* dst, int32_
  *      max_seqlen bound for the attention calls.
  * Three launches on `stream`; nothing is allocated.  batch * seqlen < 2^31.
  * The results equal those of the oracle's definition exactly (integer work).
+ * For attn_fwd_padded each slot's valid rows must be consecutive (a run at
+ * any position in the slot); a mask with holes inside a slot gives indices
+ * that the unpad/varlen/pad calls accept but the fused padded call does not.
  */
 attn_status_t attn_mask_to_varlen(const void* mask, int32_t batch, int32_t seqlen,
                                   int32_t* indices, int32_t* cu_seqlens, int32_t* stats,
@@ -253,7 +292,8 @@ attn_status_t attn_pad_scatter(const void* src, void* dst, const int32_t* indice
  * Precondition: the rows of one sequence are consecutive in the padded tensor,
  *      indices[cu_seqlens[s] + i] == indices[cu_seqlens[s]] + i (true of right-
  *      padded slots and of packed rows).  Violating it gives wrong values for
- *      that sequence but no out-of-range access.
+ *      that sequence but no out-of-range access; in debug mode (ATTN_FWD_DEBUG)
+ *      the call returns ATTN_ERR_SHAPE instead.
  * out  (n_rows, num_heads_q, head_dim) fp32: indexed rows get the attention
  *      output, every other row is written with +0.0 bytes.
  * lse  (num_heads_q, n_valid) fp32 over the COMPACT rows, or NULL.

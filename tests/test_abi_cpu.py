@@ -59,8 +59,11 @@ def varlen(lib, **kw):
 def test_varlen_validation(lib):
     assert varlen(lib, d=48) == UNSUP
     assert varlen(lib, d=16) == UNSUP
-    assert varlen(lib, scale=0.0) == UNSUP
-    assert varlen(lib, scale=-1.0) == UNSUP
+    # every finite scale is accepted (zero and negative included); checked
+    # with zero work so that nothing launches
+    assert varlen(lib, scale=0.0, nseq=0) == OK
+    assert varlen(lib, scale=-1.0, nseq=0) == OK
+    assert varlen(lib, scale=-0.0, tq=0) == OK
     assert varlen(lib, scale=float("inf")) == UNSUP
     assert varlen(lib, scale=float("nan")) == UNSUP
     assert varlen(lib, hq=6, hkv=4) == SHAPE
@@ -194,7 +197,8 @@ def test_backward_argument_checks(lib):
         return f(P, P, P, P, P, P, P, P, 1, 8, 8, a["hq"], a["hkv"], a["d"], a["mq"], 8,
                  a["scale"], 1, a["dq"], P, P, a["ws"], a["wsb"], None)
     assert call(d=32) == UNSUP and call(d=256) == UNSUP and call(d=96) == UNSUP
-    assert call(scale=0.0) == UNSUP
+    assert call(scale=float("inf")) == UNSUP
+    assert call(scale=float("nan")) == UNSUP
     assert call(hq=3) == SHAPE                       # hq % hkv
     assert call(wsb=8 * 2 * 4 - 4) == SHAPE          # workspace below 4 * tq * hq bytes
     assert call(wsb=-1) == SHAPE

@@ -79,6 +79,26 @@ def test_bad_indices_for_padded_path_and_scatter(debug):
         t.attn_pad_scatter(src, dev_i32(unsorted), 256)
 
 
+def test_padded_path_rejects_a_hole_inside_a_sequence(debug):
+    """A mask with a hole inside a slot: indices are sorted and in range, but
+    one sequence's rows are not consecutive, which the fused padded call needs."""
+    t = debug
+    w = gen.make_padded("dbg6", 7, 256, [128, 128], 2, 64, True, slot_lengths=[100, 50])
+    q, k, v = dev_bf16(w.q), dev_bf16(w.k), dev_bf16(w.v)
+    cu = dev_i32(w.cu_seqlens_q)
+    holed = w.indices.copy()
+    holed[60:100] += 5  # rows 60.. of slot 0 move past a 5-row hole (still < 128)
+    assert np.all(np.diff(holed) > 0) and holed[99] < 128
+    with pytest.raises(t.AttnError, match="SHAPE"):
+        t.attn_fwd_padded(q, k, v, dev_i32(holed), cu, w.max_seqlen)
+    # the same indices pass the gather, whose only precondition is order and range
+    (qc,) = t.attn_unpad_gather([q], dev_i32(holed))
+    assert qc.shape[0] == len(holed)
+    # and the consistent padded call runs
+    out, _ = t.attn_fwd_padded(q, k, v, dev_i32(w.indices), cu, w.max_seqlen)
+    assert not np.isnan(host(out)).any()
+
+
 def test_bad_paged_and_backward_metadata(debug):
     t = debug
     w = gen.make_paged("dbg4", 5, [1, 1], [40, 20], 4, 2, 64, 16, True)

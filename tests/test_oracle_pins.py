@@ -148,6 +148,65 @@ def test_varlen_matches_brute_force_with_empty_sequence():
                 assert_close(lse[h, cq[s]:cq[s + 1]], bl)
 
 
+NONPOS_CASES = [
+    # (lq, lk, d, hq, hkv, causal, scale)
+    (7, 7, 32, 2, 2, True, -0.25),
+    (5, 9, 64, 2, 1, True, -0.125),
+    (6, 6, 128, 4, 2, False, -1.0 / math.sqrt(128)),
+    (6, 10, 64, 2, 2, True, 0.0),
+    (4, 4, 32, 1, 1, False, 0.0),
+]
+
+
+@pytest.mark.parametrize("lq,lk,d,hq,hkv,causal,scale", NONPOS_CASES)
+def test_nonpositive_scale_matches_brute_force(lq, lk, d, hq, hkv, causal, scale):
+    """The definition holds for any finite scale: a negative one weights the
+    smallest dot products highest, a zero one weights every visible key alike."""
+    seed = 31 + lq * 5 + lk * 3 + d + causal
+    qb = rand_f64(seed, 1, lq, hq, d)
+    kb = rand_f64(seed + 1, 1, lk, hkv, d)
+    vb = rand_f64(seed + 2, 1, lk, hkv, d)
+    o, lse = oracle.attention_dense(qb, kb, vb, np.float32(scale), causal)
+    q, k, v = decode_bf16_struct(qb), decode_bf16_struct(kb), decode_bf16_struct(vb)
+    for h in range(hq):
+        g = h // (hq // hkv)
+        bo, bl = brute_attention(q[0, :, h], k[0, :, g], v[0, :, g], float(np.float32(scale)),
+                                 causal)
+        assert_close(o[0, :, h], bo)
+        assert_close(lse[0, h], bl)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_scale_gives_mean_of_visible_values(causal):
+    """Closed form: scale 0 makes every visible score 0 whatever Q and K hold."""
+    lq, lk = 9, 13
+    r = rng(61)
+    q = r.standard_normal((lq, 32)) * 5.0
+    k = r.standard_normal((lk, 32)) * 5.0
+    v = r.standard_normal((lk, 32))
+    o, lse = oracle.attention_one(q, k, v, 0.0, causal)
+    for i in range(lq):
+        n = i + 1 + (lk - lq) if causal else lk
+        np.testing.assert_allclose(o[i], v[:n].mean(axis=0), rtol=0, atol=1e-13)
+        assert abs(lse[i] - math.log(n)) < 1e-13
+
+
+def test_negative_scale_selects_most_negative_dot_product():
+    """Closed form: with Hadamard keys and q_i = -kappa H_t(i), a negative scale
+    gives the single score -scale kappa^2 D at key t(i) and 0 elsewhere."""
+    d, L, kappa = 64, 16, 3.0
+    scale = -1.0 / math.sqrt(d)
+    targets = [(5 * i + 2) % L for i in range(L)]
+    q, k = _onehot_case(d, L, kappa, targets)
+    q = -q
+    v = rng(62).standard_normal((L, d))
+    o, lse = oracle.attention_one(q, k, v, scale, False)
+    delta = -scale * kappa * kappa * d
+    for i in range(L):
+        np.testing.assert_allclose(o[i], v[targets[i]], rtol=0, atol=L * math.exp(-delta) * 10)
+        assert abs(lse[i] - (delta + math.log1p((L - 1) * math.exp(-delta)))) < 1e-12
+
+
 # --------------------------------------------------------------------------- invariants
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("lq,lk", [(16, 16), (8, 20), (20, 8)])

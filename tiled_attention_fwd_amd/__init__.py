@@ -71,6 +71,23 @@ def workspace(num_seqs: int, max_seqlen: int, num_heads_q: int, head_dim: int, c
     return _torch().empty(n, dtype=_torch().uint8, device=device)
 
 
+def attn_fwd_launch_plan(varlen: bool, num_seqs: int, total_q: int, max_seqlen: int,
+                         num_heads_q: int, head_dim: int, causal: bool,
+                         workspace_bytes: int = 0) -> dict:
+    """The library's launch choice for a forward shape: tile policy, workgroup
+    order, key-range parts per query block and queries per block."""
+    plan = (ctypes.c_int32 * 4)()
+    _lib.check("attn_fwd_launch_plan", _lib.load().attn_fwd_launch_plan(
+        int(bool(varlen)), int(num_seqs), int(total_q), int(max_seqlen), int(num_heads_q),
+        int(head_dim), int(bool(causal)), int(workspace_bytes), plan))
+    return {"policy": plan[0], "order": plan[1], "n_split": plan[2], "bm": plan[3]}
+
+
+def attn_fwd_tile_policy_compiled(policy: int, head_dim: int) -> bool:
+    """Whether ATTN_FWD_TILE=<policy> can force that tile policy at head_dim."""
+    return bool(_lib.load().attn_fwd_tile_policy_compiled(int(policy), int(head_dim)))
+
+
 def _ws_args(ws):
     if ws is None:
         return None, 0

@@ -69,6 +69,9 @@ SIGNATURES = {
     "attn_fwd_fp8_dense": (c_int32, [c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32,
                                      c_int32, c_int32, c_int32, c_float, c_float, c_float, c_float,
                                      c_int32, c_void_p, c_void_p, c_void_p]),
+    "attn_fwd_launch_plan": (c_int32, [c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,
+                                       c_int32, c_int64, c_void_p]),
+    "attn_fwd_tile_policy_compiled": (c_int32, [c_int32, c_int32]),
     "attn_status_str": (ctypes.c_char_p, [c_int32]),
     "attn_abi_version": (c_int32, []),
 }

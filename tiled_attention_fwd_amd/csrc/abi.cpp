@@ -97,10 +97,25 @@ int64_t split_workspace_bytes(const SplitPlan& sp, int64_t rows, int n_qb, int h
 // scale * log2(e), the factor that turns scores into base-2 exponents.
 float base2_factor(float scale) { return (float)((double)scale * 1.4426950408889634074); }
 
+// The forward kernels take the row maximum of the raw scores before
+// multiplying by c, so they need c > 0.  Any finite scale reaches that form
+// exactly: c = |scale| log2(e) (times the fp8 factors `extra`), and the sign
+// goes onto Q once per block -- a negative scale negates every Q element (a
+// sign-bit flip, exact in bf16 and E4M3), a zero scale clears Q (every score is
+// then exactly 0, the uniform weights a zero scale gives).  sign_bits holds the
+// sign bit of every element of a 32-bit word (0x80008000 for bf16, 0x80808080
+// for E4M3).
+void set_forward_scale(AttnArgs& a, float scale, double extra, uint32_t sign_bits) {
+  const double mag = scale == 0.f ? 1.0 : fabs((double)scale);
+  a.c = (float)(mag * extra * 1.4426950408889634074);
+  a.q_xor = scale < 0.f ? sign_bits : 0u;
+  a.q_clear = scale == 0.f ? 0xffffffffu : 0u;
+}
+
 attn_status_t check_common(int32_t hq, int32_t hkv, int32_t d, float scale) {
   if (hq < 0 || hkv < 0) return ATTN_ERR_SHAPE;
   if (!head_dim_ok(d)) return ATTN_ERR_UNSUPPORTED;
-  if (!(scale > 0.f) || !isfinite(scale)) return ATTN_ERR_UNSUPPORTED;
+  if (!isfinite(scale)) return ATTN_ERR_UNSUPPORTED;
   if (hq > 0 && (hkv <= 0 || hq % hkv != 0)) return ATTN_ERR_SHAPE;
   return ATTN_OK;
 }
@@ -110,8 +125,24 @@ bool span_fits(int64_t rows, int64_t row_stride_elems) {
   return rows * row_stride_elems * 2 < (1LL << 32);
 }
 
-attn_status_t launch(AttnArgs& a, int d, bool varlen, int max_q, void* ws, int64_t ws_bytes,
-                     hipStream_t stream) {
+// ATTN_FWD_ORDER=<n> forces the workgroup order of a launch (tests comparing
+// orders bit for bit): 1 head-remapped block-major, 2 sequence-major, 3
+// unit-major, 4 compact.  A launch the forced order cannot serve returns
+// ATTN_ERR_UNSUPPORTED.
+int order_override() {
+  const char* s = getenv("ATTN_FWD_ORDER");
+  if (s == nullptr || *s == '\0') return -1;
+  char* end = nullptr;
+  long v = strtol(s, &end, 10);
+  if (end == s || v < 0 || v > 4) return -1;
+  return (int)v;
+}
+
+// The launch plan of one forward call: tile policy, workgroup order, split
+// parts.  Fills the plan fields of `a` (n_qb, xcd_remap, n_vblk, n_split,
+// split_tiles, split_bn, part_o, part_lse).  Pure host computation.
+attn_status_t plan_launch(AttnArgs& a, int d, bool varlen, int max_q, void* ws, int64_t ws_bytes,
+                          int* pid_out, int* bm_out) {
   TilePolicy pol;
   int pid;
   const int64_t rows = (int64_t)a.nseq * a.hq;
@@ -132,13 +163,14 @@ attn_status_t launch(AttnArgs& a, int d, bool varlen, int max_q, void* ws, int64
   a.n_split = 1;
   const SplitPlan sp = plan_split(pol, pid, rows, a.n_qb, max_q, a.causal != 0);
   const int64_t need = split_workspace_bytes(sp, rows, a.n_qb, d);
-  if (unit_major && !(need > 0 && ws != nullptr && ws_bytes >= need)) a.xcd_remap = 3;
-  if (need > 0 && ws != nullptr && ws_bytes >= need) {
+  const bool split = need > 0 && ws_bytes >= need;
+  if (unit_major && !split) a.xcd_remap = 3;
+  if (split) {
     a.n_split = sp.n_split;
     a.split_tiles = sp.split_tiles;
     a.split_bn = sp.bn;
     a.part_o = static_cast<float*>(ws);
-    a.part_lse = a.part_o + rows * a.n_qb * sp.n_split * sp.bm * d;
+    a.part_lse = ws ? a.part_o + rows * a.n_qb * sp.n_split * sp.bm * d : nullptr;
   }
   // A pack whose longest sequence is far above the rest (one long sequence
   // with many short ones): the (sequence, head) x longest-block-count grid is
@@ -146,17 +178,38 @@ attn_status_t launch(AttnArgs& a, int d, bool varlen, int max_q, void* ws, int64
   // reads cu_seqlens (1 x 8192 + 64 x 128, 16 heads: 383 us against 262 for
   // the long sequence alone).  Compact order instead: sequence s owns block
   // slots [cu_q[s] / bm + s, ...), at most ceil(total_q / bm) + nseq per head.
-  if (varlen && dma_kernel && a.nseq > 1 && a.n_split == 1) {
-    const int64_t bm = pol.bm();
-    const int64_t nv = (a.lse_hs + bm - 1) / bm + a.nseq;  // lse_hs: compact rows
-    if (rows * a.n_qb >= 4 * (int64_t)a.hq * nv && (int64_t)a.hq * nv <= 0x7fffffffLL) {
-      a.xcd_remap = 4;
-      a.n_vblk = (int32_t)nv;
-    }
+  const int64_t bm = pol.bm();
+  const int64_t nv = (a.lse_hs + bm - 1) / bm + a.nseq;  // lse_hs: compact rows
+  const bool compact_ok = varlen && dma_kernel && a.n_split == 1 &&
+                          (int64_t)a.hq * nv <= 0x7fffffffLL;
+  if (compact_ok && a.nseq > 1 && rows * a.n_qb >= 4 * (int64_t)a.hq * nv) a.xcd_remap = 4;
+  const int forced = order_override();
+  if (forced >= 0) {
+    // 1 needs a bijective head remap (rows % 8 == 0); 2 and 3 exist in the
+    // DMA-staged kernel (3 also in the pipelined one) and 2 needs hq % 8 == 0;
+    // 3 and 4 take no split parts; 4 is varlen only.
+    const bool ok = forced == 0 || (forced == 1 && rows % 8 == 0) ||
+                    (forced == 2 && dma_kernel && a.hq % 8 == 0) ||
+                    (forced == 3 && (dma_kernel || pipe_kernel) && a.n_split == 1) ||
+                    (forced == 4 && compact_ok);
+    if (!ok) return ATTN_ERR_UNSUPPORTED;
+    a.xcd_remap = forced;
   }
+  if (a.xcd_remap == 4) a.n_vblk = (int32_t)nv;
   if (rows * a.n_qb * a.n_split > 0x7fffffffLL) return ATTN_ERR_SHAPE;
+  *pid_out = pid;
+  *bm_out = (int)bm;
+  return ATTN_OK;
+}
+
+attn_status_t launch(AttnArgs& a, int d, bool varlen, int max_q, void* ws, int64_t ws_bytes,
+                     hipStream_t stream) {
+  int pid = 0, bm = 0;
+  const attn_status_t st = plan_launch(a, d, varlen, max_q, ws, ws != nullptr ? ws_bytes : 0,
+                                       &pid, &bm);
+  if (st != ATTN_OK) return st;
   hipError_t e = attnfwd::launch_attention(a, d, varlen, pid, stream);
-  if (e == hipSuccess && a.n_split > 1) e = attnfwd::launch_merge(a, d, varlen, sp.bm, stream);
+  if (e == hipSuccess && a.n_split > 1) e = attnfwd::launch_merge(a, d, varlen, bm, stream);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
@@ -267,7 +320,7 @@ attn_status_t check_fp8(int32_t hq, int32_t hkv, int32_t d, float scale, float q
 
 attn_status_t launch_fp8(AttnArgs& a, int d, bool varlen, int max_q, float scale, float qs,
                          float ks, float vs, hipStream_t stream) {
-  a.c = (float)((double)scale * qs * ks * 1.4426950408889634074);
+  set_forward_scale(a, scale, (double)qs * ks, 0x80808080u);
   a.n_qb = (max_q + 127) / 128;
   const hipError_t e = attnfwd::launch_attention_fp8(a, d, varlen, vs, stream);
   return e == hipSuccess ? ATTN_OK : (e == hipErrorInvalidConfiguration ? ATTN_ERR_SHAPE : ATTN_ERR_HIP);
@@ -288,6 +341,8 @@ struct DebugCheck {
   int n_lens = 0, lens_max = 0;
   const int32_t* idx = nullptr;  // indices: n_idx entries
   int n_idx = 0, idx_rows = -1;
+  const int32_t* runs_cu = nullptr;  // with idx: idx consecutive within each of n_runs sequences
+  int n_runs = 0;
 };
 
 attn_status_t run_debug(std::initializer_list<DebugCheck> checks, hipStream_t s) {
@@ -299,6 +354,9 @@ attn_status_t run_debug(std::initializer_list<DebugCheck> checks, hipStream_t s)
     if (c.lens && attnfwd::debug_check_lens(c.lens, c.n_lens, c.lens_max, s) != hipSuccess)
       return ATTN_ERR_HIP;
     if (c.idx && attnfwd::debug_check_indices(c.idx, c.n_idx, c.idx_rows, s) != hipSuccess)
+      return ATTN_ERR_HIP;
+    if (c.idx && c.runs_cu &&
+        attnfwd::debug_check_runs(c.idx, c.n_idx, c.runs_cu, c.n_runs, s) != hipSuccess)
       return ATTN_ERR_HIP;
   }
   const int st = attnfwd::debug_status(s);
@@ -319,6 +377,15 @@ DebugCheck idx_check(const int32_t* idx, int n, int rows) {
   c.idx = idx;
   c.n_idx = n;
   c.idx_rows = rows;
+  return c;
+}
+
+DebugCheck runs_check(const int32_t* idx, int n_idx, const int32_t* cu, int n) {
+  DebugCheck c;
+  c.idx = idx;
+  c.n_idx = n_idx;
+  c.runs_cu = cu;
+  c.n_runs = n;
   return c;
 }
 
@@ -458,7 +525,7 @@ attn_status_t attn_fwd_varlen_ws(const void* q, const void* k, const void* v,
   a.hq = num_heads_q;
   a.hkv = num_heads_k;
   a.group = num_heads_q / num_heads_k;
-  a.c = base2_factor(scale);
+  set_forward_scale(a, scale, 1.0, 0x80008000u);
   a.causal = causal ? 1 : 0;
   if (!span_fits(total_q, a.q_ss) || !span_fits(total_k, a.k_ss)) return ATTN_ERR_SHAPE;
   st = run_debug({cu_check(cu_seqlens_q, num_seqs, total_q, max_seqlen),
@@ -537,7 +604,7 @@ attn_status_t attn_fwd_dense_ws(const void* q, const void* k, const void* v, int
   a.group = num_heads_q / num_heads_k;
   a.sq = seqlen_q;
   a.sk = seqlen_k;
-  a.c = base2_factor(scale);
+  set_forward_scale(a, scale, 1.0, 0x80008000u);
   a.causal = causal ? 1 : 0;
   if (!span_fits(seqlen_q, a.q_ss) || !span_fits(seqlen_k, a.k_ss) || !span_fits(seqlen_k, a.v_ss))
     return ATTN_ERR_SHAPE;
@@ -564,6 +631,37 @@ int64_t attn_fwd_workspace_bytes(int32_t num_seqs, int32_t max_seqlen, int32_t n
   const int n_qb = (max_seqlen + pol.bm() - 1) / pol.bm();
   const SplitPlan sp = plan_split(pol, pid, rows, n_qb, max_seqlen, causal != 0);
   return split_workspace_bytes(sp, rows, n_qb, head_dim);
+}
+
+attn_status_t attn_fwd_launch_plan(int32_t varlen, int32_t num_seqs, int32_t total_q,
+                                   int32_t max_seqlen, int32_t num_heads_q, int32_t head_dim,
+                                   int32_t causal, int64_t workspace_bytes, int32_t* plan) {
+  if (plan == nullptr) return ATTN_ERR_NULL;
+  if (num_seqs <= 0 || total_q <= 0 || max_seqlen <= 0 || num_heads_q <= 0 || workspace_bytes < 0)
+    return ATTN_ERR_SHAPE;
+  if (!head_dim_ok(head_dim)) return ATTN_ERR_UNSUPPORTED;
+  AttnArgs a{};
+  a.nseq = num_seqs;
+  a.hq = num_heads_q;
+  a.causal = causal ? 1 : 0;
+  a.lse_hs = varlen ? total_q : max_seqlen;
+  const int max_q = varlen ? std::min(max_seqlen, total_q) : max_seqlen;
+  int pid = 0, bm = 0;
+  const attn_status_t st = plan_launch(a, head_dim, varlen != 0, max_q, nullptr, workspace_bytes,
+                                       &pid, &bm);
+  if (st != ATTN_OK) return st;
+  plan[0] = pid;
+  plan[1] = a.xcd_remap;
+  plan[2] = a.n_split;
+  plan[3] = bm;
+  return ATTN_OK;
+}
+
+int32_t attn_fwd_tile_policy_compiled(int32_t policy, int32_t head_dim) {
+  if (policy < 0 || !head_dim_ok(head_dim)) return 0;
+  TilePolicy pol;
+  int pid;
+  return attnfwd::select_policy(head_dim, 1024, true, 1, policy, &pol, &pid) ? 1 : 0;
 }
 
 attn_status_t attn_fwd_padded(const void* q, const void* k, const void* v,
@@ -613,13 +711,14 @@ attn_status_t attn_fwd_padded(const void* q, const void* k, const void* v,
   a.hq = num_heads_q;
   a.hkv = num_heads_k;
   a.group = num_heads_k > 0 ? num_heads_q / num_heads_k : 1;
-  a.c = base2_factor(scale);
+  set_forward_scale(a, scale, 1.0, 0x80008000u);
   a.causal = causal ? 1 : 0;
   if (!span_fits(n_rows, a.q_ss) || !span_fits(n_rows, a.k_ss)) return ATTN_ERR_SHAPE;
   if (n_valid > 0) {
     const attn_status_t dst_ = run_debug(
         {idx_check(indices, n_valid, n_rows),
-         cu_check(cu_seqlens, work ? num_seqs : -1, n_valid, max_seqlen)},
+         cu_check(cu_seqlens, work ? num_seqs : -1, n_valid, max_seqlen),
+         runs_check(indices, n_valid, cu_seqlens, work ? num_seqs : 0)},
         static_cast<hipStream_t>(stream));
     if (dst_ != ATTN_OK) return dst_;
   }
@@ -934,7 +1033,7 @@ const char* attn_status_str(attn_status_t s) {
     case ATTN_OK: return "ok";
     case ATTN_ERR_NULL: return "a required pointer is NULL";
     case ATTN_ERR_SHAPE: return "invalid or inconsistent sizes";
-    case ATTN_ERR_UNSUPPORTED: return "unsupported argument (head_dim must be 32/64/128/256; scale > 0 and finite)";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported argument (head_dim must be 32/64/128/256; scale finite; or a policy/order this launch cannot use)";
     case ATTN_ERR_ALIGN: return "pointer, stride or row size not 16-byte aligned";
     case ATTN_ERR_HIP: return "HIP runtime rejected the launch";
     default: return "unknown status";

@@ -43,6 +43,12 @@ __device__ __forceinline__ uint32_t span_bytes(int rows, int64_t row_stride) {
   return b > 0xffffffffLL ? 0xffffffffu : (uint32_t)b;
 }
 
+// Sign of the score scale applied to a Q fragment word by word:
+// (x ^ xr) & ~clr (negation: xr = the element sign bits; zero: clr = ~0).
+__device__ __forceinline__ u32x4 q_sign(u32x4 x, uint32_t xr, uint32_t clr) {
+  return (x ^ xr) & ~clr;
+}
+
 // Key held by accumulator row i of a 32-key block (see the header comment).
 __device__ __forceinline__ int key_of_row(int i) {
   return ((i >> 4) << 4) + (((i >> 2) & 1) << 3) + (((i >> 3) & 1) << 2) + (i & 3);

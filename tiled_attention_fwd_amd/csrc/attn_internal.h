@@ -31,7 +31,16 @@ struct AttnArgs {
   int32_t sq, sk;    // dense sequence lengths
   int32_t n_qb;      // query blocks per (sequence, head) in the grid
   int32_t n_vblk;    // order 4: block slots per head, ceil(total_q / bm) + nseq
-  float c;           // scale * log2(e): scores enter exp2 in base-2 units
+  float c;           // |scale| * log2(e): scores enter exp2 in base-2 units
+  // Sign of the scale, applied to the Q fragments once per block:
+  // q' = (q ^ q_xor) & ~q_clear on each 32-bit word.  scale < 0: q_xor holds
+  // the sign bit of every element (exact negation, so c * (-q).k = scale * q.k
+  // with c = |scale| log2 e); scale == 0: q_clear = all ones (every score is
+  // exactly 0, the same weights as a zero scale); otherwise both 0.  The
+  // kernels take the row maximum of the raw scores and multiply it by c, which
+  // needs c > 0.  Zero-initialised arguments mean "unchanged".
+  uint32_t q_xor;
+  uint32_t q_clear;
   int32_t causal;
   int32_t xcd_remap; // 1: spread (sequence, head) rows so each XCD gets a contiguous slice;
                      // 2 (DMA-staged kernel, hq % 8 == 0): sequence-major order, each
@@ -134,6 +143,10 @@ hipError_t debug_reset(hipStream_t s);
 hipError_t debug_check_cu(const int32_t* cu, int n, int total, int max_len, hipStream_t s);
 hipError_t debug_check_lens(const int32_t* lens, int n, int max_len, hipStream_t s);
 hipError_t debug_check_indices(const int32_t* idx, int n, int n_rows, hipStream_t s);
+// idx (n_idx entries) holds consecutive rows within each sequence of cu (n + 1
+// offsets): the precondition of the fused padded call.
+hipError_t debug_check_runs(const int32_t* idx, int n_idx, const int32_t* cu, int n,
+                            hipStream_t s);
 int debug_status(hipStream_t s);
 
 // Padding mask (B slots x L rows, nonzero = valid) -> indices of the valid

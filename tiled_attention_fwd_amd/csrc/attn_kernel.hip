@@ -199,7 +199,7 @@ __global__ __launch_bounds__(WAVES * 64, MINW) void attn_fwd_kernel(const AttnAr
 #pragma unroll
     for (int s = 0; s < NDS; ++s) {
       asm volatile("" : "+v"(qraw[c][s]));
-      qf[c][s] = __builtin_bit_cast(bf16x8, qraw[c][s]);
+      qf[c][s] = __builtin_bit_cast(bf16x8, q_sign(qraw[c][s], a.q_xor, a.q_clear));
     }
 
   f32x16 oacc[QC][NDB];
@@ -578,7 +578,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_pingpong_kernel(const AttnArg
 #pragma unroll
   for (int s = 0; s < NDS; ++s) {
     asm volatile("" : "+v"(qraw[s]));
-    qf[s] = __builtin_bit_cast(bf16x8, qraw[s]);
+    qf[s] = __builtin_bit_cast(bf16x8, q_sign(qraw[s], a.q_xor, a.q_clear));
   }
 
   f32x16 oacc[NDB];
@@ -985,7 +985,7 @@ __global__ __launch_bounds__(WAVES * 64, D == 256 ? 1 : 2) void attn_fwd_dma_ker
 #pragma unroll
   for (int s = 0; s < NDS; ++s) {
     asm volatile("" : "+v"(qraw[s]));
-    qf[s] = __builtin_bit_cast(bf16x8, qraw[s]);
+    qf[s] = __builtin_bit_cast(bf16x8, q_sign(qraw[s], a.q_xor, a.q_clear));
   }
 
   f32x16 oacc[NDB];
@@ -1458,7 +1458,7 @@ __global__ __launch_bounds__(WAVES * 64, MINW) void attn_fwd_pipe_kernel(const A
 #pragma unroll
   for (int s = 0; s < NDS; ++s) {
     asm volatile("" : "+v"(qraw[s]));
-    qf[s] = __builtin_bit_cast(bf16x8, qraw[s]);
+    qf[s] = __builtin_bit_cast(bf16x8, q_sign(qraw[s], a.q_xor, a.q_clear));
   }
 
   f32x16 oacc[NDB];

@@ -13,7 +13,7 @@ namespace {
 
 // Status bits (OR-ed by the checks; 0 = consistent).
 constexpr int kCuFirst = 1, kCuOrder = 2, kCuLast = 4, kCuTooLong = 8, kIdxRange = 16,
-              kIdxOrder = 32;
+              kIdxOrder = 32, kIdxRuns = 64;
 
 __device__ int g_status;
 
@@ -58,6 +58,25 @@ __global__ __launch_bounds__(256) void check_indices_kernel(const int32_t* idx, 
   if (bad) atomicOr(&g_status, bad);
 }
 
+// The rows of each sequence are consecutive in the padded tensor: for every
+// i in (cu[s], cu[s+1]), idx[i] == idx[i-1] + 1.  The sequence of entry i is
+// found by binary search over cu (n + 1 entries, n >= 1); the search stays
+// within cu whatever its contents, and only idx[0..n_idx) is read.
+__global__ __launch_bounds__(256) void check_runs_kernel(const int32_t* idx, int n_idx,
+                                                         const int32_t* cu, int n) {
+  int bad = 0;
+  for (int i = blockIdx.x * 256 + threadIdx.x + 1; i < n_idx; i += gridDim.x * 256) {
+    int lo = 0, hi = n - 1;  // the last sequence whose start is <= i
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (cu[mid] <= i) lo = mid;
+      else hi = mid - 1;
+    }
+    if (cu[lo] < i && idx[i] != idx[i - 1] + 1) bad |= kIdxRuns;
+  }
+  if (bad) atomicOr(&g_status, bad);
+}
+
 }  // namespace
 
 hipError_t debug_reset(hipStream_t s) {
@@ -81,6 +100,14 @@ hipError_t debug_check_indices(const int32_t* idx, int n, int n_rows, hipStream_
   if (n <= 0) return hipSuccess;
   const int blocks = (n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024;
   hipLaunchKernelGGL(check_indices_kernel, dim3(blocks), dim3(256), 0, s, idx, n, n_rows);
+  return hipGetLastError();
+}
+
+hipError_t debug_check_runs(const int32_t* idx, int n_idx, const int32_t* cu, int n,
+                            hipStream_t s) {
+  if (n_idx <= 1 || n <= 0) return hipSuccess;
+  const int blocks = (n_idx + 255) / 256 < 1024 ? (n_idx + 255) / 256 : 1024;
+  hipLaunchKernelGGL(check_runs_kernel, dim3(blocks), dim3(256), 0, s, idx, n_idx, cu, n);
   return hipGetLastError();
 }
 

@@ -119,6 +119,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_fp8_kernel(const AttnArgs a, 
       u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(qrs, (int)(ob + 64 * s), 0, 0);
       u32x4 y = __builtin_amdgcn_raw_buffer_load_b128(qrs, (int)(ob + 64 * s + 16), 0, 0);
       asm volatile("" : "+v"(x), "+v"(y));
+      x = q_sign(x, a.q_xor, a.q_clear);
+      y = q_sign(y, a.q_xor, a.q_clear);
       qf[s] = i32x8{(int)x[0], (int)x[1], (int)x[2], (int)x[3], (int)y[0], (int)y[1], (int)y[2], (int)y[3]};
     }
   }
@@ -195,7 +197,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_fp8_kernel(const AttnArgs a, 
       }
       // register r of block kb holds key kbeg + 32 kb + 16 (r / 8) + 8 hh + r % 8
       const bool edge = (kbeg + 64 > lk) || (a.causal && kbeg + 63 > qw0 + off);
-      float mt = -INFINITY;  // raw score maximum (scale > 0)
+      float mt = -INFINITY;  // raw score maximum (c > 0: a negative scale negates Q)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
