@@ -176,7 +176,9 @@ def time_calls(torch, fn, iters, warmup, flush=None):
     return times
 
 
-def run_configs(torch, t, names, flush):
+def run_configs(torch, t, names, flush, oracle_budget_s=0.0):
+    """Per-workload cold and warm call times; with oracle_budget_s > 0 each row
+    also gets the fp64 oracle's time for the same workload on the host."""
     import numpy as np
     from synth import gen
     rows = []
@@ -230,6 +232,10 @@ def run_configs(torch, t, names, flush):
             "bound": "mfma" if t_mfma >= t_hbm else "hbm",
             "pct_of_bound": round(100 * max(t_mfma, t_hbm) / med, 1),
         })
+        if oracle_budget_s > 0:
+            orc = oracle_config_time(w, oracle_budget_s)
+            orc["gpu_speedup"] = round(orc["s"] / (med * 1e-6), 1)
+            rows[-1]["oracle"] = orc
         del q, k, v, o, lse
         torch.cuda.empty_cache()
     return rows
@@ -353,16 +359,84 @@ def run_fp8(torch, t, names, flush):
 
 
 # ------------------------------------------------------------------------- CPU baseline
+def host_threads():
+    """(host cores this process may use, BLAS threads NumPy's library runs)."""
+    cores = len(os.sched_getaffinity(0))
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        blas = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        blas = cores
+    return cores, blas
+
+
+def oracle_config_time(w, budget_s=2.5):
+    """Wall time of the fp64 oracle for one workload, from a bounded sample.
+
+    The oracle works one (sequence, head) at a time (oracle.attention_one on
+    that unit's decoded rows, the per-unit step of attention_varlen and
+    attention_dense), materialising the full Lq x Lk score matrix.  Units are
+    taken in a seeded random order until the budget is spent; the total is
+    the sample's time scaled by (all units' Lq * Lk * (D + 1)) / (the sample's).
+    Padded workloads add the oracle's gather and scatter of the whole input."""
+    import numpy as np
+    import oracle
+    units = []
+    if w.kind == "dense":
+        for b in range(w.q.shape[0]):
+            for h in range(w.hq):
+                units.append((b, h))
+    else:
+        for s in range(len(w.lengths_q)):
+            if w.lengths_q[s] > 0:
+                for h in range(w.hq):
+                    units.append((s, h))
+    group = w.hq // w.hkv
+    cost = lambda u: w.lengths_q[u[0]] * w.lengths_k[u[0]] * (w.d + 1)
+    total_cost = sum(cost(u) for u in units)
+    order = np.random.Generator(np.random.PCG64(99)).permutation(len(units))
+    t_extra = 0.0
+    if w.kind == "padded":
+        t0 = time.perf_counter()
+        hd = w.q.shape[2:]
+        q, k, v = (oracle.unpad_gather(x, w.indices, hd) for x in (w.q, w.k, w.v))
+        oracle.pad_scatter(np.zeros((len(w.indices),) + tuple(hd)), w.indices, w.q.shape[1])
+        t_extra = time.perf_counter() - t0
+    else:
+        q, k, v = w.q, w.k, w.v
+    cq, ck = w.cu_seqlens_q, w.cu_seqlens_k
+    scale = np.float32(w.scale)
+    done_cost, t_units, n = 0, 0.0, 0
+    for i in order:
+        s, h = units[i]
+        g = h // group
+        t0 = time.perf_counter()
+        if w.kind == "dense":
+            qs, ks, vs = q[s, :, h], k[s, :, g], v[s, :, g]
+        else:
+            qs, ks, vs = q[cq[s]:cq[s + 1], h], k[ck[s]:ck[s + 1], g], v[ck[s]:ck[s + 1], g]
+        oracle.attention_one(oracle.bf16_bits_to_f64(qs), oracle.bf16_bits_to_f64(ks),
+                             oracle.bf16_bits_to_f64(vs), scale, w.causal)
+        t_units += time.perf_counter() - t0
+        done_cost += cost(units[i])
+        n += 1
+        if t_units >= budget_s:
+            break
+    est = t_extra + t_units * total_cost / max(1, done_cost)
+    full = n == len(units)
+    return {"s": round(est, 3), "kind": "oracle",
+            "sample": (f"all {n} (sequence, head) units" if full else
+                       f"{n} of {len(units)} (sequence, head) units in {t_units:.2f} s, scaled by "
+                       f"Lq*Lk*(D+1) to the whole workload (extrapolated)")
+            + (", plus gather and scatter of the padded input" if w.kind == "padded" else "")}
+
+
 def cpu_baseline(step_workloads, budget_s=20.0):
     """The fp64 oracle on the host, for the same padded-path step."""
     import numpy as np
     import oracle
-    try:
-        import threadpoolctl
-        info = threadpoolctl.threadpool_info()
-        threads = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
-    except Exception:  # pragma: no cover
-        threads = len(os.sched_getaffinity(0))
+    cores, threads = host_threads()
     flops = sum(attn_flops(w) for w in step_workloads)
     t0 = time.perf_counter()
     steps = 0
@@ -378,7 +452,7 @@ def cpu_baseline(step_workloads, budget_s=20.0):
             break
     per_step = el / steps
     return {"value": round(flops / per_step / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle",
+            "host_cores": cores, "blas_threads": threads, "kind": "oracle",
             "sample": f"{steps} full step(s) of the same padded-path workload ((a) and (b)): NumPy fp64 "
                       f"gather, attention_varlen, scatter; {per_step * 1e3:.0f} ms per step"}
 
@@ -481,6 +555,23 @@ def main():
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     value = flops_step / (ms_per_step * 1e-3) / 1e12
+
+    # The same replays cold: before each one a 1 GiB write evicts L2 and MALL
+    # (outside the span); HIP events on the replay stream bracket the step.
+    flush_buf = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    s_rep = torch.cuda.current_stream()
+    cold_us = []
+    for _ in range(max(5, min(args.steps, 50))):
+        flush_buf.zero_()
+        ea = torch.cuda.Event(enable_timing=True)
+        eb = torch.cuda.Event(enable_timing=True)
+        ea.record(s_rep)
+        graph.replay()
+        eb.record(s_rep)
+        eb.synchronize()
+        cold_us.append(ea.elapsed_time(eb) * 1e3)
+    del flush_buf
+    step_cold_us = statistics.median(cold_us)
 
     # The fused padded path (attn_fwd_padded: zero fill + attention reading and
     # writing the padded rows) on the same inputs, captured and replayed alike.
@@ -607,7 +698,7 @@ def main():
         flush = lambda: flush_buf.zero_()
         cfg_names = list(gen.WORKLOADS) if args.configs == "all" else args.configs.split(",")
         print(f"[bench] timing {len(cfg_names)} workloads", file=sys.stderr, flush=True)
-        cfg_rows = run_configs(torch, t, cfg_names, flush)
+        cfg_rows = run_configs(torch, t, cfg_names, flush, 0.0 if args.no_cpu else 2.5)
         del flush_buf
     bwd_rows = []
     if args.bwd_configs != "none":
@@ -646,6 +737,12 @@ def main():
                    "global_batch": 2, "seq_len": 4096, "parallelism": "none (1 GPU)",
                    "per_launch_us": {f"{names[pi]}:{k}": round(v, 2) for (pi, k), v in avg_us.items()},
                    "pct_bf16_peak_step": round(100 * value / PEAK_BF16_TFLOPS, 2),
+                   "step_cold": {"timing": "one graph replay per sample, L2 and MALL flushed "
+                                           "(1 GiB write) before each, HIP events around it",
+                                 "us_median": round(step_cold_us, 2),
+                                 "us_p10": round(sorted(cold_us)[len(cold_us) // 10], 2),
+                                 "us_p90": round(sorted(cold_us)[(len(cold_us) * 9) // 10], 2),
+                                 "tflops": round(flops_step / (step_cold_us * 1e-6) / 1e12, 2)},
                    "fused_path": {"call": "attn_fwd_padded (zero fill + attention in place on "
                                           "the padded rows), same inputs and outputs",
                                   "ms_per_step": round(ms_fused, 4),
