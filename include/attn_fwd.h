@@ -57,7 +57,8 @@ typedef enum {
   ATTN_ERR_SHAPE = 2,       /* a size is negative or sizes disagree */
   ATTN_ERR_UNSUPPORTED = 3, /* head_dim not in {32,64,128,256}, scale not finite, ... */
   ATTN_ERR_ALIGN = 4,       /* a pointer or row size is not 16-byte aligned */
-  ATTN_ERR_HIP = 5          /* the HIP runtime rejected the launch */
+  ATTN_ERR_HIP = 5,         /* the HIP runtime rejected the launch */
+  ATTN_ERR_SCRATCH = 6      /* the call needs more than the library's static scratch */
 } attn_status_t;
 
 /*
@@ -378,6 +379,37 @@ attn_status_t attn_fwd_paged_fp8kv(const void* q, const void* k_cache, const voi
                                    float k_scale, float v_scale, int32_t causal, float* out,
                                    float* lse, void* workspace, int64_t workspace_bytes,
                                    void* stream);
+
+/*
+ * attn_fwd_paged_noalloc -- attn_fwd_paged for callers that cannot allocate.
+ *
+ * For code that must not call hipMalloc: work under HIP graph capture, tight
+ * serving (decode) loops, harnesses that forbid allocation.  The same
+ * computation, kernels and results as attn_fwd_paged with a workspace of
+ * attn_fwd_paged_workspace_bytes; the scratch memory of the key-range split
+ * is instead a static device array inside the library, of
+ * ATTN_NOALLOC_SCRATCH_BYTES bytes per GPU, held from the first call on a GPU
+ * until the process ends.  Nothing is allocated or freed.
+ * Arguments, layouts, preconditions and errors are those of attn_fwd_paged
+ * without the workspace.  `stream` must belong to the current HIP device
+ * (the array's copy on that device is used).
+ * Limit: a shape whose split needs more than ATTN_NOALLOC_SCRATCH_BYTES (only
+ * possible under the ATTN_PAGED_CHUNK_TILES test override; every default plan
+ * needs at most 33.8 MB) returns ATTN_ERR_SCRATCH before anything is launched.
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents (each call writes every slot it reads, so nothing needs clearing):
+ * calls that overlap in time on one GPU (different streams, or host threads)
+ * race and give wrong results; serialise them.
+ */
+#define ATTN_NOALLOC_SCRATCH_BYTES (40ll << 20)
+attn_status_t attn_fwd_paged_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                     const int32_t* cu_seqlens_q, const int32_t* seqlens_k,
+                                     const int32_t* block_table, int32_t num_seqs,
+                                     int32_t total_q, int32_t num_pages, int32_t page_size,
+                                     int32_t max_pages_per_seq, int32_t num_heads_q,
+                                     int32_t num_heads_k, int32_t head_dim, int32_t max_seqlen_q,
+                                     int32_t max_seqlen_k, float scale, int32_t causal,
+                                     float* out, float* lse, void* stream);
 
 /*
  * attn_fwd_paged_workspace_bytes -- workspace that lets attn_fwd_paged split

@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_abi_version_and_status_strings(lib):
     assert lib.attn_abi_version() == 1
-    for s in range(6):
+    for s in range(7):
         assert lib.attn_status_str(s)
     assert b"unknown" in lib.attn_status_str(99)
 
@@ -254,3 +254,18 @@ def test_paged_fp8_and_mask_argument_checks(lib):
     assert m(P, 2, 4, P, None, P, None) == NULL
     assert m(None, 2, 4, P, P, P, None) == NULL
     assert m(P, 2, 4, P, ctypes.c_void_p(18), P, None) == ALIGN
+
+
+def test_paged_noalloc_refuses_a_split_beyond_its_scratch_without_launching(lib, monkeypatch):
+    """The no-allocation paged call checks its static scratch limit on the host:
+    a forced one-tile-per-part split of 8000 keys needs ~63 MiB, above the
+    40 MiB array, and is refused before anything touches a device."""
+    P = ctypes.c_void_p(16)
+    monkeypatch.setenv("ATTN_PAGED_CHUNK_TILES", "1")
+    assert lib.attn_fwd_paged_workspace_bytes(4, 1, 8000, 16, 4, 128) > (40 << 20)
+    # q, k, v, cu_q, seqlens_k, table, nseq, tq, num_pages, page_size, max_pages, hq, hkv, d,
+    # max_q, max_k, scale, causal, out, lse, stream
+    st = lib.attn_fwd_paged_noalloc(P, P, P, P, P, P, 4, 4, 200, 64, 125, 16, 4, 128, 1, 8000,
+                                    0.125, 1, P, None, None)
+    assert st == 6
+    assert b"scratch" in lib.attn_status_str(6)

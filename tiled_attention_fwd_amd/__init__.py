@@ -420,6 +420,44 @@ def attn_fwd_paged(q, k_cache, v_cache, cu_seqlens_q, seqlens_k, block_table,
     return out, lse
 
 
+def attn_fwd_paged_noalloc(q, k_cache, v_cache, cu_seqlens_q, seqlens_k, block_table,
+                           max_seqlen_q: int, max_seqlen_k: int, out, lse=None,
+                           scale: Optional[float] = None, causal: bool = True, stream=None):
+    """attn_fwd_paged with the library's own static scratch instead of a
+    workspace; `out` (Tq, Hq, D) fp32 and `lse` (Hq, Tq) fp32 or None are
+    passed in, so this call allocates nothing."""
+    torch = _torch()
+    lib = _lib.load()
+    for n, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _check_bf16(n, t)
+    if q.dim() != 3 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
+        raise ValueError("q must be (Tq, Hq, D) and the caches (num_pages, page_size, Hkv, D)")
+    for n, t in (("cu_seqlens_q", cu_seqlens_q), ("seqlens_k", seqlens_k),
+                 ("block_table", block_table)):
+        if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{n} must be a contiguous int32 GPU tensor")
+    tq, hq, d = q.shape
+    num_pages, page_size, hkv, dk = k_cache.shape
+    if dk != d:
+        raise ValueError("head_dim of q and the caches differ")
+    nseq = cu_seqlens_q.numel() - 1
+    if seqlens_k.numel() != nseq or block_table.dim() != 2 or block_table.shape[0] != nseq:
+        raise ValueError("seqlens_k must be (num_seqs,) and block_table (num_seqs, max_pages)")
+    _check_fp32("out", out, (tq, hq, d))
+    if lse is not None:
+        _check_fp32("lse", lse, (hq, tq))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib.attn_fwd_paged_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cu_seqlens_q),
+                                    _ptr(seqlens_k), _ptr(block_table), nseq, tq, num_pages,
+                                    page_size, block_table.shape[1], hq, hkv, d,
+                                    int(max_seqlen_q), int(max_seqlen_k), float(scale),
+                                    int(bool(causal)), _ptr(out), _ptr(lse),
+                                    _stream_ptr(q.device, stream))
+    _lib.check("attn_fwd_paged_noalloc", st)
+    return out, lse
+
+
 def attn_mask_to_varlen(mask, stream=None):
     """mask (B, L) bool/uint8/int8 GPU tensor, nonzero = valid row.  Returns
     (indices (B*L,) int32 whose first n_valid entries are the valid rows,

@@ -58,6 +58,10 @@ SIGNATURES = {
                                        c_int32, c_int32, c_int32, c_int32, c_int32, c_float,
                                        c_float, c_float, c_int32, c_void_p, c_void_p, c_void_p,
                                        c_int64, c_void_p]),
+    "attn_fwd_paged_noalloc": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                         c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32,
+                                         c_int32, c_int32, c_int32, c_int32, c_int32, c_float,
+                                         c_int32, c_void_p, c_void_p, c_void_p]),
     "attn_fwd_paged_workspace_bytes": (c_int64, [c_int32, c_int32, c_int32, c_int32, c_int32,
                                                  c_int32]),
     "attn_mask_to_varlen": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p,
@@ -77,7 +81,7 @@ SIGNATURES = {
 }
 
 STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_UNSUPPORTED",
-          4: "ATTN_ERR_ALIGN", 5: "ATTN_ERR_HIP"}
+          4: "ATTN_ERR_ALIGN", 5: "ATTN_ERR_HIP", 6: "ATTN_ERR_SCRATCH"}
 
 _lib = None
 

@@ -405,7 +405,8 @@ attn_status_t paged_impl(const void* q, const void* k_cache, const void* v_cache
                          int32_t num_heads_q, int32_t num_heads_k, int32_t head_dim,
                          int32_t max_seqlen_q, int32_t max_seqlen_k, float scale, int32_t causal,
                          float* out, float* lse, void* workspace, int64_t workspace_bytes,
-                         bool kv_fp8, float k_scale, float v_scale, void* stream) {
+                         bool kv_fp8, float k_scale, float v_scale, void* stream,
+                         bool no_alloc = false) {
   if (num_seqs < 0 || total_q < 0 || num_pages < 0 || max_pages_per_seq < 0 ||
       max_seqlen_q < 0 || max_seqlen_k < 0)
     return ATTN_ERR_SHAPE;
@@ -467,6 +468,12 @@ attn_status_t paged_impl(const void* q, const void* k_cache, const void* v_cache
   a.n_split = 1;
   a.chunk_tiles = 0;
   const int64_t need = paged_workspace_bytes(p, num_seqs, num_heads_k, head_dim);
+  if (no_alloc) {
+    // the library's own scratch array instead of a caller workspace
+    if (need > attnfwd::noalloc_scratch_bytes()) return ATTN_ERR_SCRATCH;
+    if (attnfwd::noalloc_scratch(&workspace) != hipSuccess) return ATTN_ERR_HIP;
+    workspace_bytes = attnfwd::noalloc_scratch_bytes();
+  }
   if (need > 0 && workspace != nullptr && workspace_bytes >= need) {
     a.n_split = p.n_split;
     a.chunk_tiles = p.chunk_tiles;
@@ -877,6 +884,20 @@ attn_status_t attn_fwd_paged_fp8kv(const void* q, const void* k_cache, const voi
                     workspace_bytes, true, k_scale, v_scale, stream);
 }
 
+attn_status_t attn_fwd_paged_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                     const int32_t* cu_seqlens_q, const int32_t* seqlens_k,
+                                     const int32_t* block_table, int32_t num_seqs,
+                                     int32_t total_q, int32_t num_pages, int32_t page_size,
+                                     int32_t max_pages_per_seq, int32_t num_heads_q,
+                                     int32_t num_heads_k, int32_t head_dim, int32_t max_seqlen_q,
+                                     int32_t max_seqlen_k, float scale, int32_t causal,
+                                     float* out, float* lse, void* stream) {
+  return paged_impl(q, k_cache, v_cache, cu_seqlens_q, seqlens_k, block_table, num_seqs, total_q,
+                    num_pages, page_size, max_pages_per_seq, num_heads_q, num_heads_k, head_dim,
+                    max_seqlen_q, max_seqlen_k, scale, causal, out, lse, nullptr, 0, false, 1.f,
+                    1.f, stream, true);
+}
+
 attn_status_t attn_mask_to_varlen(const void* mask, int32_t batch, int32_t seqlen,
                                   int32_t* indices, int32_t* cu_seqlens, int32_t* stats,
                                   void* stream) {
@@ -1033,6 +1054,7 @@ const char* attn_status_str(attn_status_t s) {
     case ATTN_OK: return "ok";
     case ATTN_ERR_NULL: return "a required pointer is NULL";
     case ATTN_ERR_SHAPE: return "invalid or inconsistent sizes";
+    case ATTN_ERR_SCRATCH: return "the call needs more scratch memory than the library's static buffer holds";
     case ATTN_ERR_UNSUPPORTED: return "unsupported argument (head_dim must be 32/64/128/256; scale finite; or a policy/order this launch cannot use)";
     case ATTN_ERR_ALIGN: return "pointer, stride or row size not 16-byte aligned";
     case ATTN_ERR_HIP: return "HIP runtime rejected the launch";

@@ -136,6 +136,11 @@ hipError_t launch_scatter(const void* src, void* dst, const int32_t* indices, in
 hipError_t launch_attention_fp8(const AttnArgs& a, int head_dim, bool varlen, float o_mul,
                                 hipStream_t stream);
 
+// Library-owned scratch memory (noalloc.hip): its size, and the current
+// device's copy of it (looked up once per device, then cached).
+int64_t noalloc_scratch_bytes();
+hipError_t noalloc_scratch(void** ptr);
+
 // Debug-mode checks of device-resident preconditions (debug_checks.hip).  The
 // checks OR bits into one device status word; debug_status synchronises the
 // stream and reads it (0 = consistent, -1 = HIP error).
