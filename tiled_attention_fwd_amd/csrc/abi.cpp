@@ -539,6 +539,11 @@ attn_status_t attn_fwd_varlen_ws(const void* q, const void* k, const void* v,
                   cu_check(cu_seqlens_k, num_seqs, total_k, -1)},
                  static_cast<hipStream_t>(stream));
   if (st != ATTN_OK) return st;
+  if (num_seqs == 1) {  // offsets 0, lengths total_q / total_k by the cu_seqlens contract
+    a.single_seq = 1;
+    a.sq = total_q;
+    a.sk = total_k;
+  }
   const int max_q = max_seqlen < total_q ? max_seqlen : total_q;
   return launch(a, head_dim, true, max_q, workspace, workspace_bytes,
                 static_cast<hipStream_t>(stream));

@@ -28,7 +28,12 @@ struct AttnArgs {
   int64_t o_bs, o_ss, o_hs;
   int64_t lse_bs, lse_hs;  // dense: (B, Hq, Sq); varlen: (Hq, Tq) with hs = Tq
   int32_t nseq, hq, hkv, group;
-  int32_t sq, sk;    // dense sequence lengths
+  int32_t sq, sk;    // dense sequence lengths; varlen with single_seq: total_q, total_k
+  // Varlen with one sequence and no row map: its offsets are 0 and its lengths
+  // total_q / total_k (the cu_seqlens contract), so the kernels take them from
+  // sq / sk instead of loading cu_seqlens (one dependent memory round trip
+  // less before the first tile).
+  int32_t single_seq;
   int32_t n_qb;      // query blocks per (sequence, head) in the grid
   int32_t n_vblk;    // order 4: block slots per head, ceil(total_q / bm) + nseq
   float c;           // |scale| * log2(e): scores enter exp2 in base-2 units
@@ -69,6 +74,12 @@ struct SeqRows {
 };
 __device__ __forceinline__ SeqRows seq_rows(const AttnArgs& a, int seq) {
   SeqRows r;
+  if (a.single_seq) {
+    r.qs = r.ks = r.q_row = r.k_row = 0;
+    r.lq = a.sq;
+    r.lk = a.sk;
+    return r;
+  }
   r.qs = a.cu_q[seq];
   r.ks = a.cu_k[seq];
   r.lq = a.cu_q[seq + 1] - r.qs;

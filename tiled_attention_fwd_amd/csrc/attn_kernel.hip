@@ -994,27 +994,55 @@ __global__ __launch_bounds__(WAVES * 64, D == 256 ? 1 : 2) void attn_fwd_dma_ker
   float m_run = -INFINITY, l_run = 0.f;
 
   // ---- DMA of one step (KG tiles of K and of V) into buffer B ----------------
-  auto dma = [&](auto Bc, int step) {
+  // Byte offsets of this wave's DMA instructions within a step's tiles (the
+  // same every step): pair i is the wave's i-th K and V instruction.  The
+  // step's first key moves the buffer base instead (scalar arithmetic), so an
+  // instruction is one M0 write and one load, with no vector work.
+  constexpr int NP = NK / WAVES;
+  uint32_t koffp[NP], voffp[NP];
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const int ins = wave * NP + i;  // 0 .. NK-1, wave-uniform
+    const int g = ins / IPT;
+    const int cgi = ins - g * IPT;
+    const int slot = cgi * 64 + lane;
+    const int row = slot / CPR;      // row within the tile
+    const int phys = slot - row * CPR;
+    koffp[i] = (uint32_t)(g * BN + row) * k_row_bytes + (uint32_t)((phys ^ swz_k<D>(row)) * 16);
+    voffp[i] = (uint32_t)(g * BN + row) * v_row_bytes + (uint32_t)((phys ^ swz_v<D>(row)) * 16);
+  }
+  // the buffer of rows [first row of the step, end of sequence)
+  auto step_desc = [](u32x4 d, uint32_t ofs) __attribute__((always_inline)) {
+    const uint64_t base = (((uint64_t)(d[1] & 0xffffu)) << 32 | d[0]) + ofs;
+    u32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((uint32_t)base);
+    r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32) & 0xffffu);
+    r[2] = __builtin_amdgcn_readfirstlane(d[2] > ofs ? d[2] - ofs : 0u);
+    r[3] = d[3];
+    return r;
+  };
+  struct StepDesc {
+    u32x4 k, v;
+  };
+  auto descs_of = [&](int step) __attribute__((always_inline)) {
+    const uint32_t kbeg = __builtin_amdgcn_readfirstlane((t_begin + step * KG) * BN);
+    return StepDesc{step_desc(kdesc, kbeg * k_row_bytes), step_desc(vdesc, kbeg * v_row_bytes)};
+  };
+  auto dma_pair = [&](auto Bc, const StepDesc& sd, int i) __attribute__((always_inline)) {
     constexpr int B = decltype(Bc)::value;
     uint16_t* kd = B == 0 ? ks0 : B == 1 ? ks1 : ks2;
     uint16_t* vd = B == 0 ? vs0 : B == 1 ? vs1 : vs2;
-    const uint32_t kbeg = (t_begin + step * KG) * BN;
-#pragma unroll
-    for (int i = 0; i < NK / WAVES; ++i) {
-      const int ins = wave * (NK / WAVES) + i;  // 0 .. NK-1, wave-uniform
-      const int g = ins / IPT;
-      const int cgi = ins - g * IPT;
-      const int slot = cgi * 64 + lane;
-      const int row = slot / CPR;                 // row within the tile
-      const int phys = slot - row * CPR;
-      const uint32_t grow = kbeg + g * BN + row;  // key index within the sequence
-      dma16(kdesc, grow * k_row_bytes + (uint32_t)((phys ^ swz_k<D>(row)) * 16),
-            __builtin_amdgcn_readfirstlane(lds_addr(kd + g * TILE + cgi * 512)));
-      dma16(vdesc, grow * v_row_bytes + (uint32_t)((phys ^ swz_v<D>(row)) * 16),
-            __builtin_amdgcn_readfirstlane(lds_addr(vd + g * TILE + cgi * 512)));
-    }
+    const int ins = wave * NP + i;
+    const int g = ins / IPT;
+    const int cgi = ins - g * IPT;
+    dma16(sd.k, koffp[i], __builtin_amdgcn_readfirstlane(lds_addr(kd + g * TILE + cgi * 512)));
+    dma16(sd.v, voffp[i], __builtin_amdgcn_readfirstlane(lds_addr(vd + g * TILE + cgi * 512)));
   };
-
+  auto dma = [&](auto Bc, int step) {
+    const StepDesc sd = descs_of(step);
+#pragma unroll
+    for (int i = 0; i < NP; ++i) dma_pair(Bc, sd, i);
+  };
   // lane-constant parts of the fragment addresses
   int krow[NKB];
 #pragma unroll
@@ -1151,7 +1179,91 @@ __global__ __launch_bounds__(WAVES * 64, D == 256 ? 1 : 2) void attn_fwd_dma_ker
   }
 
   // ---- key-group merge (KG > 1): partial (m, l, O) through LDS ------------------
-  if constexpr (KG > 1) {
+  // Sliced merge (the 32-dim blocks divide evenly over the groups): every
+  // wave publishes its (m, l) and the O blocks of the other groups' dim
+  // slices, one barrier, then each wave combines its own slice of the output
+  // dims from all KG groups and stores just that slice.  The merge and the
+  // stores of a block are then spread over all of its waves, behind a single
+  // barrier.  The groups are combined in group order in every wave, so the
+  // row sum (and thus the normaliser of every slice) is the same in all.
+  constexpr bool SLICED = KG > 1 && NDB % KG == 0;
+  constexpr int DSL = SLICED ? NDB / KG : NDB;  // 32-dim blocks this wave stores
+  const int db0 = SLICED ? kg * DSL : 0;
+  if constexpr (SLICED) {
+    constexpr int NOUT = (NDB - DSL) * 16;  // O values a wave hands to the other groups, per lane
+    constexpr int SLOT = NOUT + 2;          // plus m and l
+    static_assert(2 * SLOT * 64 * 4 <= KG * TILE * 2, "two waves' partials per tile array");
+    static_assert(WAVES == 8, "slots: two waves per tile array");
+    auto slot_of = [&](int w) {
+      uint16_t* s16 = (w >> 1) == 0 ? ks0 : (w >> 1) == 1 ? vs0 : (w >> 1) == 2 ? ks1 : vs1;
+      return reinterpret_cast<float*>(s16) + (w & 1) * SLOT * 64 + lane;  // [reg][lane]
+    };
+    {
+      float* my = slot_of(wave);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        if (db >= db0 && db < db0 + DSL) continue;
+        const int j = db < db0 ? db : db - DSL;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) my[(j * 16 + r) * 64] = oacc[db][r];
+      }
+      my[NOUT * 64] = m_run;
+      my[(NOUT + 1) * 64] = l_run;
+    }
+    __syncthreads();
+    float m_g[KG], l_g[KG];
+#pragma unroll
+    for (int g = 0; g < KG; ++g) {
+      if (g == kg) {
+        m_g[g] = m_run;
+        l_g[g] = l_run;
+      } else {
+        const float* o = slot_of(g * QW + qw);
+        m_g[g] = o[NOUT * 64];
+        l_g[g] = o[(NOUT + 1) * 64];
+      }
+    }
+    float m_all = m_g[0];
+#pragma unroll
+    for (int g = 1; g < KG; ++g) m_all = fmaxf(m_all, m_g[g]);
+    const float m_ref = m_all == -INFINITY ? 0.f : m_all;
+    float al[KG];
+    float l_tot = 0.f;
+#pragma unroll
+    for (int g = 0; g < KG; ++g) {
+      al[g] = __builtin_amdgcn_exp2f(m_g[g] - m_ref);
+      l_tot += l_g[g] * al[g];
+    }
+    f32x16 acc[DSL];
+#pragma unroll
+    for (int d = 0; d < DSL; ++d) acc[d] = f32x16{};
+#pragma unroll
+    for (int g = 0; g < KG; ++g) {
+      const float* o = slot_of(g * QW + qw);
+      const int gdb0 = g * DSL;  // group g's slice; where our blocks sit in its slot
+#pragma unroll
+      for (int d = 0; d < DSL; ++d) {
+        if (g == kg) {
+          // own blocks db0 + d: still in registers (db0 is wave-uniform)
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+            if (db == db0 + d) acc[d] += oacc[db] * al[g];
+        } else {
+          const int db = db0 + d;
+          const int j = db < gdb0 ? db : db - DSL;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[d][r] += o[(j * 16 + r) * 64] * al[g];
+        }
+      }
+    }
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int d = 0; d < DSL; ++d)
+        if (db == d) oacc[db] = acc[d];  // this wave's slice now sits in oacc[0..DSL)
+    m_run = m_all;
+    l_run = l_tot;
+  } else if constexpr (KG > 1) {
     static_assert(KG == 2 || KG == 4, "merge written for two or four key groups");
     constexpr int NREG = NDB * 16 + 2;
     static_assert(NREG * 64 * 4 <= KG * TILE * 2, "one wave's partial must fit one tile array");
@@ -1210,9 +1322,9 @@ __global__ __launch_bounds__(WAVES * 64, D == 256 ? 1 : 2) void attn_fwd_dma_ker
     if (qrow < lq) {
       const int64_t slot = (((int64_t)(seq * a.hq + h) * a.n_qb + qb) * a.n_split + part) * BM +
                            (qrow - q0);
-      float* op = a.part_o + slot * D + hh * 4;
+      float* op = a.part_o + slot * D + hh * 4 + db0 * 32;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+      for (int db = 0; db < DSL; ++db)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           float4 w;
@@ -1222,14 +1334,14 @@ __global__ __launch_bounds__(WAVES * 64, D == 256 ? 1 : 2) void attn_fwd_dma_ker
           w.w = oacc[db][4 * g + 3] * inv;
           *reinterpret_cast<float4*>(op + db * 32 + 8 * g) = w;
         }
-      if (hh == 0) a.part_lse[slot] = lt > 0.f ? m_run + __log2f(lt) : -INFINITY;
+      if (hh == 0 && kg == 0) a.part_lse[slot] = lt > 0.f ? m_run + __log2f(lt) : -INFINITY;
     }
     return;
   }
   if (qrow < lq) {
-    float* op = obase + (int64_t)qrow * a.o_ss + hh * 4;
+    float* op = obase + (int64_t)qrow * a.o_ss + hh * 4 + db0 * 32;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+    for (int db = 0; db < DSL; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         float4 w;
@@ -1239,7 +1351,7 @@ __global__ __launch_bounds__(WAVES * 64, D == 256 ? 1 : 2) void attn_fwd_dma_ker
         w.w = oacc[db][4 * g + 3] * inv;
         *reinterpret_cast<float4*>(op + db * 32 + 8 * g) = w;
       }
-    if (a.lse != nullptr && hh == 0)
+    if (a.lse != nullptr && hh == 0 && kg == 0)
       a.lse[lseoff + (int64_t)h * a.lse_hs + qrow] =
           lt > 0.f ? (m_run + __log2f(lt)) * kLn2 : -INFINITY;
   }
