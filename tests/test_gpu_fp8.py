@@ -13,6 +13,8 @@ for bf16.
 
 from __future__ import annotations
 
+import os
+
 import numpy as np
 import pytest
 
@@ -63,31 +65,40 @@ def check_fp8(w, o, lse, causal):
             "sum_rel": rel}
 
 
+# Query blocks of the fp8 kernel: 128 (4 waves, 64-key tiles) and 256 (8
+# waves, 128-key tiles); the library picks one per shape, ATTN_FP8_TILE forces it.
+@pytest.fixture(params=["128", "256"])
+def fp8_tile(request, monkeypatch):
+    monkeypatch.setenv("ATTN_FP8_TILE", request.param)
+    return request.param
+
+
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [True, False])
-def test_fp8_varlen_ragged_gqa(d, causal):
-    w = gen.make_fp8_varlen(f"f8v{d}", 2000 + d, [1, 7, 64, 100, 129, 300, 33], 4, 2, d, causal)
+def test_fp8_varlen_ragged_gqa(d, causal, fp8_tile):
+    w = gen.make_fp8_varlen(f"f8v{d}", 2000 + d, [1, 7, 64, 100, 129, 300, 33, 700], 4, 2, d,
+                            causal)
     o, lse = run_varlen(w)
     print(check_fp8(w, o, lse, causal))
 
 
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [True, False])
-def test_fp8_lq_ne_lk_and_empty(d, causal):
-    w = gen.make_fp8_varlen("f8ne", 2100 + d, [5, 130, 0, 64, 3, 0], 2, 2, d, causal,
-                            lengths_k=[9, 70, 12, 200, 0, 0])
+def test_fp8_lq_ne_lk_and_empty(d, causal, fp8_tile):
+    w = gen.make_fp8_varlen("f8ne", 2100 + d, [5, 130, 0, 64, 3, 0, 300], 2, 2, d, causal,
+                            lengths_k=[9, 70, 12, 200, 0, 0, 190])
     o, lse = run_varlen(w)
     print(check_fp8(w, o, lse, causal))
 
 
-def test_fp8_factors():
+def test_fp8_factors(fp8_tile):
     w = gen.make_fp8_varlen("f8fac", 2200, [77, 300], 4, 1, 128, True, factors=(0.5, 4.0, 0.125))
     o, lse = run_varlen(w)
     print(check_fp8(w, o, lse, True))
 
 
 @pytest.mark.parametrize("causal", [True, False])
-def test_fp8_dense_matches_varlen(causal):
+def test_fp8_dense_matches_varlen(causal, fp8_tile):
     t = api()
     w = gen.make_fp8_varlen("f8d", 2300, [200, 200], 4, 2, 128, causal)
     o_v, l_v = run_varlen(w)
@@ -99,18 +110,36 @@ def test_fp8_dense_matches_varlen(causal):
     assert np.array_equal(host(l_d).transpose(1, 0, 2).reshape(l_v.shape), l_v)
 
 
-def test_fp8_full_size_1x8192_sampled():
-    """1 x 8192 causal, 16 heads, d=128: 64 sampled (query, head) rows against the oracle."""
+def test_fp8_full_size_1x8192_whole_output():
+    """1 x 8192 causal, 16 heads, d=128 (the fp8 benchmark shape, default query
+    block): every output element within its bound, every LSE within 1e-3.  The
+    oracle runs per head and per 1024-row block with the key prefix those rows
+    see (the causal prefix property)."""
     w = gen.make_fp8_varlen("f8big", 2400, [8192], 16, 16, 128, True)
+    assert "ATTN_FP8_TILE" not in os.environ
     o, lse = run_varlen(w)
-    r = np.random.Generator(np.random.PCG64(5))
+    assert np.isfinite(o).all()
     qd = oracle.e4m3_to_f64(w.q)
     kd = oracle.e4m3_to_f64(w.k)
     vd = oracle.e4m3_to_f64(w.v)
-    for _ in range(64):
-        i, h = int(r.integers(0, 8192)), int(r.integers(0, 16))
-        o_ref, l_ref = oracle.attention_query(qd[i, h], kd[:, h], vd[:, h], w.scale, True, i, 8192)
-        o_abs, _ = oracle.attention_query(qd[i, h], kd[:, h], np.abs(vd[:, h]), w.scale, True, i, 8192)
-        bound = 2.0 ** -4 * o_abs + 2.0 ** -17 * 8192 * float(np.abs(vd).max()) + 1e-6
-        assert (np.abs(o[i, h] - o_ref) <= bound).all(), (i, h)
-        assert abs(lse[h, i] - l_ref) <= 1e-3
+    vmax = float(np.abs(vd).max())
+    scale = np.float32(w.scale)
+
+    def one(h):
+        worst, lerr = 0.0, 0.0
+        for r0 in range(0, 8192, 1024):
+            r1 = r0 + 1024
+            o_ref, l_ref = oracle.attention_one(qd[r0:r1, h], kd[:r1, h], vd[:r1, h], scale, True)
+            o_abs, _ = oracle.attention_one(qd[r0:r1, h], kd[:r1, h], np.abs(vd[:r1, h]), scale, True)
+            bound = 2.0 ** -4 * o_abs + 2.0 ** -17 * 8192 * vmax + 1e-6
+            worst = max(worst, float((np.abs(o[r0:r1, h] - o_ref) / bound).max()))
+            lerr = max(lerr, float(np.abs(lse[h, r0:r1] - l_ref).max()))
+        return worst, lerr
+
+    import concurrent.futures
+    with concurrent.futures.ThreadPoolExecutor(8) as ex:
+        res = list(ex.map(one, range(16)))
+    worst = max(r[0] for r in res)
+    lerr = max(r[1] for r in res)
+    print("fp8 1x8192: worst error / bound", worst, "max |dLSE|", lerr)
+    assert worst <= 1.0 and lerr <= 1e-3

@@ -318,11 +318,28 @@ attn_status_t check_fp8(int32_t hq, int32_t hkv, int32_t d, float scale, float q
   return ATTN_OK;
 }
 
+// ATTN_FP8_TILE=128|256 forces the fp8 query block (sweeps and tests).
+int fp8_tile_override() {
+  const char* s = getenv("ATTN_FP8_TILE");
+  if (s == nullptr || *s == '\0') return -1;
+  const long v = strtol(s, nullptr, 10);
+  return (v == 128 || v == 256) ? (int)v : -1;
+}
+
 attn_status_t launch_fp8(AttnArgs& a, int d, bool varlen, int max_q, float scale, float qs,
                          float ks, float vs, hipStream_t stream) {
   set_forward_scale(a, scale, (double)qs * ks, 0x80808080u);
-  a.n_qb = (max_q + 127) / 128;
-  const hipError_t e = attnfwd::launch_attention_fp8(a, d, varlen, vs, stream);
+  // 256-query blocks (8 waves, 128-key tiles: K/V tiles shared by twice the
+  // queries, half the barriers and row-maximum passes per key) once they fill
+  // the CUs twice (causal: the longest blocks must not run alone at the end)
+  // or once (non-causal); 128-query blocks otherwise.
+  const int64_t rows = (int64_t)a.nseq * a.hq;
+  const int64_t n256 = rows * ((max_q + 255) / 256);
+  int bm = n256 >= (a.causal ? 512 : 256) ? 256 : 128;
+  if (fp8_tile_override() > 0) bm = fp8_tile_override();
+  a.n_qb = (max_q + bm - 1) / bm;
+  a.xcd_remap = (rows % 8 == 0) ? 1 : 0;
+  const hipError_t e = attnfwd::launch_attention_fp8(a, d, varlen, vs, bm, stream);
   return e == hipSuccess ? ATTN_OK : (e == hipErrorInvalidConfiguration ? ATTN_ERR_SHAPE : ATTN_ERR_HIP);
 }
 

@@ -143,8 +143,10 @@ hipError_t launch_scatter(const void* src, void* dst, const int32_t* indices, in
                           int n_rows_total, int64_t row_bytes, hipStream_t stream);
 
 // fp8 (E4M3) attention: q/k/v hold bytes (strides in bytes), a.c includes the
-// q and k factors, o_mul = the v factor.  head_dim 64 or 128; BM 128.
-hipError_t launch_attention_fp8(const AttnArgs& a, int head_dim, bool varlen, float o_mul,
+// q and k factors, o_mul = the v factor.  head_dim 64 or 128; bm = queries per
+// block, 128 (4 waves, 64-key tiles) or 256 (8 waves, 128-key tiles), with
+// a.n_qb counted in blocks of bm.
+hipError_t launch_attention_fp8(const AttnArgs& a, int head_dim, bool varlen, float o_mul, int bm,
                                 hipStream_t stream);
 
 // Library-owned scratch memory (noalloc.hip): its size, and the current

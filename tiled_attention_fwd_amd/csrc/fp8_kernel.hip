@@ -41,12 +41,12 @@ __device__ __forceinline__ f32x16 mfma_f8(i32x8 a, i32x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, kScaleOne, 0, kScaleOne);
 }
 
-template <int D>
+template <int D, int TK>
 struct F8Tile {
   static constexpr int CPR = D / 16;    // 16-byte chunks per row
   static constexpr int R = 1024 / D;    // rows per DMA instruction
-  static constexpr int NI = 64 / R;     // DMA instructions per 64-row tile
-  static constexpr int BYTES = 64 * D;
+  static constexpr int NI = TK / R;     // DMA instructions per TK-row tile
+  static constexpr int BYTES = TK * D;
   static __device__ __forceinline__ int swz_k(int r) { return D == 128 ? ((r >> 1) & 7) : ((r >> 2) & 3); }
   static __device__ __forceinline__ int swz_v(int r) { return D == 128 ? (r & 7) : (((r >> 2) & 1) << 1); }
 };
@@ -59,18 +59,26 @@ __device__ __forceinline__ int pack_fp8x4(float a, float b, float c, float d) {
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
 }
 
-template <int D, bool VARLEN>
-__global__ __launch_bounds__(256, 2) void attn_fwd_fp8_kernel(const AttnArgs a, float o_mul) {
-  using T = F8Tile<D>;
+// WAVES x 32 queries per workgroup, TK keys per tile (64 or 128: one barrier,
+// one row-maximum pass and one DMA wait per tile).
+template <int D, bool VARLEN, int WAVES, int TK>
+__global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_fp8_kernel(const AttnArgs a, float o_mul) {
+  using T = F8Tile<D, TK>;
+  constexpr int BM = WAVES * 32;
   constexpr int NS = D / 64;   // fp8 MFMAs per 32x32 score block
   constexpr int NDB = D / 32;  // 32-dim output blocks
+  constexpr int NKB = TK / 32; // 32-key score blocks per tile
+  constexpr int NH = TK / 64;  // 64-key halves (one P operand each)
   __shared__ __attribute__((aligned(16))) unsigned char lds[2][2][T::BYTES];  // [buf][K|V]
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
   const int rows = a.nseq * a.hq;
   const int qb_rev = blockIdx.x / rows;
-  const int p = blockIdx.x - qb_rev * rows;
+  int p = blockIdx.x - qb_rev * rows;
+  // (sequence, head) rows spread so each XCD (workgroups are dealt round-robin
+  // over 8) takes a contiguous range of heads: grouped heads share one L2
+  if (a.xcd_remap) p = (p & 7) * (rows >> 3) + (p >> 3);
   const int seq = p / a.hq, h = p - seq * a.hq;
   const int qb = a.causal ? (a.n_qb - 1 - qb_rev) : qb_rev;
   const uint8_t* qp = reinterpret_cast<const uint8_t*>(a.q);
@@ -92,13 +100,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_fp8_kernel(const AttnArgs a, 
     obase = (int64_t)seq * a.o_bs;
     lbase = (int64_t)seq * a.lse_bs + (int64_t)h * a.lse_hs;
   }
-  const int q0 = qb * 128;
+  const int q0 = qb * BM;
   if (q0 >= lq) return;
   const int kvh = h / a.group;
   const int off = lk - lq;
   int kend = lk;
-  if (a.causal) kend = min(lk, q0 + 128 + off);
-  const int n_kt = kend > 0 ? (kend + 63) / 64 : 0;
+  if (a.causal) kend = min(lk, q0 + BM + off);
+  const int n_kt = kend > 0 ? (kend + TK - 1) / TK : 0;
   const int qw0 = q0 + wave * 32;
   int kend_w = lk;
   if (a.causal) kend_w = min(lk, qw0 + 32 + off);
@@ -135,29 +143,28 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_fp8_kernel(const AttnArgs a, 
   const int dma_p = lane % T::CPR;
   auto dma = [&](int t) {
     const uint32_t b = lds0 + (uint32_t)(t & 1) * 2 * T::BYTES;
-    for (int q = wave; q < T::NI; q += 4) {
+    for (int q = wave; q < T::NI; q += WAVES) {
       const int r = q * T::R + lane / T::CPR;
-      const uint32_t ko = (uint32_t)(t * 64 + tile_key_of_row(r)) * (uint32_t)a.k_ss +
+      const uint32_t ko = (uint32_t)(t * TK + tile_key_of_row(r)) * (uint32_t)a.k_ss +
                           16 * (uint32_t)(dma_p ^ T::swz_k(r));
       dma16(kdesc, ko, __builtin_amdgcn_readfirstlane(b + q * 1024));
-      const uint32_t vo = (uint32_t)(t * 64 + r) * (uint32_t)a.v_ss +
+      const uint32_t vo = (uint32_t)(t * TK + r) * (uint32_t)a.v_ss +
                           16 * (uint32_t)(dma_p ^ T::swz_v(r));
       dma16(vdesc, vo, __builtin_amdgcn_readfirstlane(b + T::BYTES + q * 1024));
     }
   };
 
-  // per-lane fragment offsets
-  int k_off[2][2 * NS];  // [kb][2 s + half]
+  // per-lane fragment offsets of the first 32-key block; block kb adds
+  // 32 kb rows (the chunk swizzle depends on the row modulo 16 only)
+  int k_off[2 * NS];  // [2 s + half]
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+  for (int s = 0; s < NS; ++s)
 #pragma unroll
-    for (int s = 0; s < NS; ++s)
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int r = 32 * kb + l32;
-        const int c = 4 * s + 2 * hh + half;
-        k_off[kb][2 * s + half] = r * D + 16 * (c ^ T::swz_k(r));
-      }
+    for (int half = 0; half < 2; ++half) {
+      const int r = l32;
+      const int c = 4 * s + 2 * hh + half;
+      k_off[2 * s + half] = r * D + 16 * (c ^ T::swz_k(r));
+    }
   const int vg = (lane >> 4) & 1, vi = lane & 15;
   int v_off[NDB][4];
 #pragma unroll
@@ -179,36 +186,42 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_fp8_kernel(const AttnArgs a, 
   __syncthreads();
   for (int t = 0; t < n_kt; ++t) {
     if (t + 1 < n_kt) dma(t + 1);
-    const int kbeg = t * 64;
+    const int kbeg = t * TK;
     if (kbeg < kend_w) {
       const unsigned char* kt = &lds[t & 1][0][0];
       const unsigned char* vt = &lds[t & 1][1][0];
-      f32x16 st[2];
+      f32x16 st[NKB];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < NKB; ++kb) {
         st[kb] = f32x16{};
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
-          const uint4 x = *reinterpret_cast<const uint4*>(kt + k_off[kb][2 * s]);
-          const uint4 y = *reinterpret_cast<const uint4*>(kt + k_off[kb][2 * s + 1]);
+          const uint4 x = *reinterpret_cast<const uint4*>(kt + k_off[2 * s] + kb * 32 * D);
+          const uint4 y = *reinterpret_cast<const uint4*>(kt + k_off[2 * s + 1] + kb * 32 * D);
           const i32x8 af = {(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
           st[kb] = mfma_f8(af, qf[s], st[kb]);
         }
       }
       // register r of block kb holds key kbeg + 32 kb + 16 (r / 8) + 8 hh + r % 8
-      const bool edge = (kbeg + 64 > lk) || (a.causal && kbeg + 63 > qw0 + off);
-      float mt = -INFINITY;  // raw score maximum (c > 0: a negative scale negates Q)
+      const bool edge = (kbeg + TK > lk) || (a.causal && kbeg + TK - 1 > qw0 + off);
+      if (edge) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          if (edge) {
+          for (int r = 0; r < 16; ++r) {
             const int key = kbeg + 32 * kb + ((r >> 3) << 4) + 8 * hh + (r & 7);
             if (key > lim) st[kb][r] = -INFINITY;
           }
-          mt = fmaxf(mt, st[kb][r]);
+      }
+      float mt0 = -INFINITY, mt1 = -INFINITY;  // raw score maximum (c > 0: a negative scale negates Q)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          mt0 = fmaxf(mt0, st[kb][r]);
+          mt1 = fmaxf(mt1, st[kb][r + 1]);
         }
-      mt = half_max(mt) * a.c;
+      float mt = half_max(fmaxf(mt0, mt1)) * a.c;
       // lazy rescale: the reference m moves only when the row maximum passes
       // it by more than a factor 2, so 2^7 p <= 2^8 stays inside E4M3 (448)
       if (mt > m + 1.f) {
@@ -222,34 +235,37 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_fp8_kernel(const AttnArgs a, 
       }
       // 2^7 p = exp2(c s - m + 7); the row sum keeps the same factor
       const float nb = m == -INFINITY ? 0.f : 7.f - m;
-      float rs = 0.f;
+      float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float pv = __builtin_amdgcn_exp2f(fmaf(st[kb][r], a.c, nb));
-          rs += pv;
+          if (r & 1) rs1 += pv; else rs0 += pv;
           st[kb][r] = pv;
         }
-      l += rs;
-      // P bytes: byte 16 kb + r <-> key 32 kb + 16 (r / 8) + 8 hh + r % 8
-      i32x8 pf;
+      l += rs0 + rs1;
+      // per 64 keys: P bytes 16 kb' + r <-> key 32 kb' + 16 (r / 8) + 8 hh + r % 8
 #pragma unroll
-      for (int w = 0; w < 8; ++w) {
-        const int kb = w >> 2, r0 = 4 * (w & 3);
-        pf[w] = pack_fp8x4(st[kb][r0], st[kb][r0 + 1], st[kb][r0 + 2], st[kb][r0 + 3]);
-      }
+      for (int hf = 0; hf < NH; ++hf) {
+        i32x8 pf;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        i32x8 vf;
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-          const i32x2 x = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-              (__attribute__((address_space(3))) i32x2*)(vt + v_off[db][tt]));
-          vf[2 * tt] = x[0];
-          vf[2 * tt + 1] = x[1];
+        for (int w = 0; w < 8; ++w) {
+          const int kb = 2 * hf + (w >> 2), r0 = 4 * (w & 3);
+          pf[w] = pack_fp8x4(st[kb][r0], st[kb][r0 + 1], st[kb][r0 + 2], st[kb][r0 + 3]);
         }
-        oacc[db] = mfma_f8(vf, pf, oacc[db]);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          i32x8 vf;
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt) {
+            const i32x2 x = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                (__attribute__((address_space(3))) i32x2*)(vt + v_off[db][tt] + hf * 64 * D));
+            vf[2 * tt] = x[0];
+            vf[2 * tt + 1] = x[1];
+          }
+          oacc[db] = mfma_f8(vf, pf, oacc[db]);
+        }
       }
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -274,24 +290,29 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_fp8_kernel(const AttnArgs a, 
 
 }  // namespace
 
-hipError_t launch_attention_fp8(const AttnArgs& a, int head_dim, bool varlen, float o_mul,
+hipError_t launch_attention_fp8(const AttnArgs& a, int head_dim, bool varlen, float o_mul, int bm,
                                 hipStream_t stream) {
   const int64_t grid = (int64_t)a.nseq * a.hq * a.n_qb;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   if (grid == 0) return hipSuccess;
-  const dim3 g((unsigned)grid), b(256);
+  const bool wide = bm == 256;  // a.n_qb counts blocks of bm queries
+  const dim3 g((unsigned)grid), b(wide ? 512 : 256);
+#define ATTN_FP8_LAUNCH(D_, V_)                                                                  \
+  if (wide)                                                                                     \
+    hipLaunchKernelGGL((attn_fwd_fp8_kernel<D_, V_, 8, 128>), g, b, 0, stream, a, o_mul);       \
+  else                                                                                          \
+    hipLaunchKernelGGL((attn_fwd_fp8_kernel<D_, V_, 4, 64>), g, b, 0, stream, a, o_mul);
   switch (head_dim) {
     case 64:
-      if (varlen) hipLaunchKernelGGL((attn_fwd_fp8_kernel<64, true>), g, b, 0, stream, a, o_mul);
-      else hipLaunchKernelGGL((attn_fwd_fp8_kernel<64, false>), g, b, 0, stream, a, o_mul);
+      if (varlen) { ATTN_FP8_LAUNCH(64, true) } else { ATTN_FP8_LAUNCH(64, false) }
       break;
     case 128:
-      if (varlen) hipLaunchKernelGGL((attn_fwd_fp8_kernel<128, true>), g, b, 0, stream, a, o_mul);
-      else hipLaunchKernelGGL((attn_fwd_fp8_kernel<128, false>), g, b, 0, stream, a, o_mul);
+      if (varlen) { ATTN_FP8_LAUNCH(128, true) } else { ATTN_FP8_LAUNCH(128, false) }
       break;
     default:
       return hipErrorInvalidValue;
   }
+#undef ATTN_FP8_LAUNCH
   return hipGetLastError();
 }
 
