@@ -54,6 +54,22 @@ __device__ __forceinline__ int key_of_row(int i) {
   return ((i >> 4) << 4) + (((i >> 2) & 1) << 3) + (((i >> 3) & 1) << 2) + (i & 3);
 }
 
+// Called first inside a branch on a wave-uniform condition that is rarely
+// true (a tile crossing the causal diagonal or the sequence end): an empty
+// volatile asm cannot be speculated, so the compiler keeps the branch instead
+// of turning the masked path into selects that every tile then executes.
+__device__ __forceinline__ void keep_branch() { asm volatile(""); }
+
+// Scores of one 32-key block of the transposed score tile: register r of lane
+// half hh holds key kb0 + 16 (r / 8) + 8 hh + r % 8.  Keys after `lim` (the
+// lane's last visible key) get -inf.  thr = lim - kb0 - 8 hh, computed once,
+// so each register costs one compare and one select.
+__device__ __forceinline__ void mask_block(f32x16& s, int thr) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r)
+    if (((r >> 3) << 4) + (r & 7) > thr) s[r] = -INFINITY;
+}
+
 // Value of x in the other half of the wave (lane ^ 32) combined with x.
 __device__ __forceinline__ float half_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);

@@ -319,18 +319,13 @@ __global__ __launch_bounds__(WAVES * 64, MINW) void attn_fwd_kernel(const AttnAr
       // ---- mask (only sub-blocks crossing the diagonal or the sequence end) --
       const bool need_mask = (kbeg + SUB > lk) || (a.causal && kbeg + SUB - 1 > qw0 + off);
       if (need_mask) {
+        keep_branch();
 #pragma unroll
         for (int c = 0; c < QC; ++c) {
           const int qi = qw0 + c * 32 + l32;
           const int lim = a.causal ? min(lk - 1, qi + off) : lk - 1;  // last visible key
 #pragma unroll
-          for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int key = kbeg + kb * 32 + ((r >> 3) << 4) + hh * 8 + (r & 7);
-              if (key > lim) sacc[c][kb][r] = -INFINITY;
-            }
-          }
+          for (int kb = 0; kb < NKB; ++kb) mask_block(sacc[c][kb], lim - kbeg - kb * 32 - hh * 8);
         }
       }
 
@@ -713,14 +708,10 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_pingpong_kernel(const AttnArg
         if (j < nw) {
           const int kbeg = j * BN;
           if ((kbeg + BN > lk) || (a.causal && kbeg + BN - 1 > qw0 + off)) {
+            keep_branch();
             const int lim = a.causal ? min(lk - 1, qw0 + l32 + off) : lk - 1;
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-              for (int r = 0; r < 16; ++r) {
-                const int key = kbeg + kb * 32 + ((r >> 3) << 4) + hh * 8 + (r & 7);
-                if (key > lim) sacc[kb][r] = -INFINITY;
-              }
+            for (int kb = 0; kb < NKB; ++kb) mask_block(sacc[kb], lim - kbeg - kb * 32 - hh * 8);
           }
           float mx0 = -INFINITY, mx1 = -INFINITY;
 #pragma unroll
@@ -1067,14 +1058,10 @@ __global__ __launch_bounds__(WAVES * 64, D == 256 ? 1 : 2) void attn_fwd_dma_ker
       }
     lds_pipeline_hint<NKB * NDS>();
     if ((kbeg + BN0 > lk) || (a.causal && kbeg + BN0 - 1 > qw0 + off)) {
+      keep_branch();
       const int lim = a.causal ? min(lk - 1, qw0 + l32 + off) : lk - 1;
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kbeg + kb * 32 + ((r >> 3) << 4) + hh * 8 + (r & 7);
-          if (key > lim) sacc[kb][r] = -INFINITY;
-        }
+      for (int kb = 0; kb < NKB; ++kb) mask_block(sacc[kb], lim - kbeg - kb * 32 - hh * 8);
     }
     float mx0 = -INFINITY, mx1 = -INFINITY;
 #pragma unroll
@@ -1635,15 +1622,11 @@ __global__ __launch_bounds__(WAVES * 64, MINW) void attn_fwd_pipe_kernel(const A
   };
 
   auto mask = [&](f32x16 (&S)[NKB], int t) {
+    keep_branch();
     const int kbeg = t * BN;
     const int lim = a.causal ? min(lk - 1, qw0 + l32 + off) : lk - 1;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = kbeg + kb * 32 + ((r >> 3) << 4) + hh * 8 + (r & 7);
-        if (key > lim) S[kb][r] = -INFINITY;
-      }
+    for (int kb = 0; kb < NKB; ++kb) mask_block(S[kb], lim - kbeg - kb * 32 - hh * 8);
   };
 
   // row maximum in base-2 units; mx0/mx1 hold the running partial maxima

@@ -205,13 +205,9 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_fp8_kernel(const AttnA
       // register r of block kb holds key kbeg + 32 kb + 16 (r / 8) + 8 hh + r % 8
       const bool edge = (kbeg + TK > lk) || (a.causal && kbeg + TK - 1 > qw0 + off);
       if (edge) {
+        keep_branch();
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kbeg + 32 * kb + ((r >> 3) << 4) + 8 * hh + (r & 7);
-            if (key > lim) st[kb][r] = -INFINITY;
-          }
+        for (int kb = 0; kb < NKB; ++kb) mask_block(st[kb], lim - kbeg - 32 * kb - 8 * hh);
       }
       float mt0 = -INFINITY, mt1 = -INFINITY;  // raw score maximum (c > 0: a negative scale negates Q)
 #pragma unroll
