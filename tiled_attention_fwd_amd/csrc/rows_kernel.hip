@@ -117,13 +117,29 @@ __global__ __launch_bounds__(kThreads) void scatter_rows_kernel(
   __syncthreads();
   const int nrows = min(kRows, n_rows_total - r0);
   const int total = nrows * cpr;
-  for (int g = tid; g < total; g += kThreads) {
-    const int row = g / cpr;
-    const int col = g - row * cpr;
-    const int sp = srcpos[row];
-    if (sp >= 0 && src == nullptr) continue;  // fill only: indexed rows stay as they are
-    const uint4 v = sp >= 0 ? src[(int64_t)sp * cpr + col] : make_uint4(0, 0, 0, 0);
-    store_stream(&dst[(int64_t)(r0 + row) * cpr + col], v);
+  // batches of kScatterBatch chunks per thread: every load of a batch is
+  // issued before its stores, so each thread keeps several rows in flight
+  constexpr int kScatterBatch = 8;
+  for (int g0 = 0; g0 < total; g0 += kThreads * kScatterBatch) {
+    uint4 v[kScatterBatch];
+    int64_t at[kScatterBatch];
+#pragma unroll
+    for (int i = 0; i < kScatterBatch; ++i) {
+      const int g = g0 + i * kThreads + tid;
+      at[i] = -1;
+      v[i] = make_uint4(0, 0, 0, 0);
+      if (g < total) {
+        const int row = g / cpr;
+        const int col = g - row * cpr;
+        const int sp = srcpos[row];
+        if (sp >= 0 && src == nullptr) continue;  // fill only: indexed rows stay as they are
+        if (sp >= 0) v[i] = src[(int64_t)sp * cpr + col];
+        at[i] = (int64_t)(r0 + row) * cpr + col;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kScatterBatch; ++i)
+      if (at[i] >= 0) store_stream(&dst[at[i]], v[i]);
   }
 }
 
