@@ -65,8 +65,8 @@ def check_fp8(w, o, lse, causal):
             "sum_rel": rel}
 
 
-# Query blocks of the fp8 kernel: 128 (4 waves, 64-key tiles) and 256 (8
-# waves, 128-key tiles); the library picks one per shape, ATTN_FP8_TILE forces it.
+# Query blocks of the fp8 kernel: 128 (4 waves, 64-key tiles; the default) and
+# 256 (8 waves, 128-key tiles); ATTN_FP8_TILE forces one.
 @pytest.fixture(params=["128", "256"])
 def fp8_tile(request, monkeypatch):
     monkeypatch.setenv("ATTN_FP8_TILE", request.param)
@@ -110,13 +110,17 @@ def test_fp8_dense_matches_varlen(causal, fp8_tile):
     assert np.array_equal(host(l_d).transpose(1, 0, 2).reshape(l_v.shape), l_v)
 
 
-def test_fp8_full_size_1x8192_whole_output():
-    """1 x 8192 causal, 16 heads, d=128 (the fp8 benchmark shape, default query
-    block): every output element within its bound, every LSE within 1e-3.  The
-    oracle runs per head and per 1024-row block with the key prefix those rows
-    see (the causal prefix property)."""
+@pytest.mark.parametrize("tile", [None, "256"])
+def test_fp8_full_size_1x8192_whole_output(tile, monkeypatch):
+    """1 x 8192 causal, 16 heads, d=128 (the fp8 benchmark shape; the default
+    query block and the 256-query one): every output element within its bound,
+    every LSE within 1e-3.  The oracle runs per head and per 1024-row block
+    with the key prefix those rows see (the causal prefix property)."""
     w = gen.make_fp8_varlen("f8big", 2400, [8192], 16, 16, 128, True)
-    assert "ATTN_FP8_TILE" not in os.environ
+    if tile is None:
+        assert "ATTN_FP8_TILE" not in os.environ
+    else:
+        monkeypatch.setenv("ATTN_FP8_TILE", tile)
     o, lse = run_varlen(w)
     assert np.isfinite(o).all()
     qd = oracle.e4m3_to_f64(w.q)

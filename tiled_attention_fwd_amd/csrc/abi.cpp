@@ -329,13 +329,14 @@ int fp8_tile_override() {
 attn_status_t launch_fp8(AttnArgs& a, int d, bool varlen, int max_q, float scale, float qs,
                          float ks, float vs, hipStream_t stream) {
   set_forward_scale(a, scale, (double)qs * ks, 0x80808080u);
-  // 256-query blocks (8 waves, 128-key tiles: K/V tiles shared by twice the
-  // queries, half the barriers and row-maximum passes per key) once they fill
-  // the CUs twice (causal: the longest blocks must not run alone at the end)
-  // or once (non-causal); 128-query blocks otherwise.
+  // 128-query blocks (4 waves, 64-key tiles, 150 VGPRs: three workgroups per
+  // CU).  256-query blocks (8 waves, 128-key tiles: K/V tiles shared by twice
+  // the queries, half the barriers and row-maximum passes per key, but 187
+  // VGPRs and one workgroup per CU) measured 10-11 % slower on 1x4096 causal
+  // and 4x4096 non-causal, and from 2 % faster to 9 % slower on 1x8192 causal
+  // depending on the box; they stay selectable with ATTN_FP8_TILE=256.
   const int64_t rows = (int64_t)a.nseq * a.hq;
-  const int64_t n256 = rows * ((max_q + 255) / 256);
-  int bm = n256 >= (a.causal ? 512 : 256) ? 256 : 128;
+  int bm = 128;
   if (fp8_tile_override() > 0) bm = fp8_tile_override();
   a.n_qb = (max_q + bm - 1) / bm;
   a.xcd_remap = (rows % 8 == 0) ? 1 : 0;

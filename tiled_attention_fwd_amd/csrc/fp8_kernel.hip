@@ -141,6 +141,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_fp8_kernel(const AttnA
   const u32x4 vdesc = make_desc(vp + krow0 * a.v_ss + (int64_t)kvh * a.v_hs, vbytes);
   const uint32_t lds0 = lds_addr(lds);
   const int dma_p = lane % T::CPR;
+  // K rows of tile t into lds[t & 1][0], V rows into lds[t & 1][1]
   auto dma = [&](int t) {
     const uint32_t b = lds0 + (uint32_t)(t & 1) * 2 * T::BYTES;
     for (int q = wave; q < T::NI; q += WAVES) {
@@ -181,88 +182,98 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_fp8_kernel(const AttnA
 #pragma unroll
   for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
 
+  // S^T of 32-key block kb of tile t (K in lds[t & 1][0])
+  auto score_block = [&](int t, int kb, f32x16& sb) __attribute__((always_inline)) {
+    const unsigned char* kt = &lds[t & 1][0][0] + kb * 32 * D;
+    sb = f32x16{};
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const uint4 x = *reinterpret_cast<const uint4*>(kt + k_off[2 * s]);
+      const uint4 y = *reinterpret_cast<const uint4*>(kt + k_off[2 * s + 1]);
+      const i32x8 af = {(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+      sb = mfma_f8(af, qf[s], sb);
+    }
+  };
+  // Masks, row maximum, rescale, and the E4M3 P operands of NB 32-key score
+  // blocks starting at key kbeg (register r of block b holds key
+  // kbeg + 32 b + 16 (r / 8) + 8 hh + r % 8).  2^7 p = exp2(c s - m + 7) is
+  // rounded four values at a time into pf[b / 2] (byte 16 (b % 2) + r of a P
+  // operand <-> key 32 (b % 2) + 16 (r / 8) + 8 hh + r % 8 of its 64 keys);
+  // the row sum keeps the same factor and the unrounded values.
+  auto softmax = [&](int kbeg, auto& sb, auto& pf) __attribute__((always_inline)) {
+    constexpr int NB = sizeof(sb) / sizeof(sb[0]);
+    const bool edge = (kbeg + 32 * NB > lk) || (a.causal && kbeg + 32 * NB - 1 > qw0 + off);
+    if (edge) {
+      keep_branch();
+#pragma unroll
+      for (int b = 0; b < NB; ++b) mask_block(sb[b], lim - kbeg - 32 * b - 8 * hh);
+    }
+    float mt0 = -INFINITY, mt1 = -INFINITY;  // raw score maximum (c > 0: a negative scale negates Q)
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        mt0 = fmaxf(mt0, sb[b][r]);
+        mt1 = fmaxf(mt1, sb[b][r + 1]);
+      }
+    float mt = half_max(fmaxf(mt0, mt1)) * a.c;
+    // lazy rescale: the reference m moves only when the row maximum passes
+    // it by more than a factor 2, so 2^7 p <= 2^8 stays inside E4M3 (448)
+    if (mt > m + 1.f) {
+      const float alpha = __builtin_amdgcn_exp2f(m - mt);  // 0 while m = -inf
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      m = mt;
+    }
+    const float nb = m == -INFINITY ? 0.f : 7.f - m;
+    float rs0 = 0.f, rs1 = 0.f;
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int r0 = 0; r0 < 16; r0 += 4) {
+        float p4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p4[e] = __builtin_amdgcn_exp2f(fmaf(sb[b][r0 + e], a.c, nb));
+        rs0 += p4[0] + p4[2];
+        rs1 += p4[1] + p4[3];
+        pf[b >> 1][4 * (b & 1) + (r0 >> 2)] = pack_fp8x4(p4[0], p4[1], p4[2], p4[3]);
+      }
+    l += rs0 + rs1;
+  };
+  // O^T += V^T P^T for the 64-key half hf of tile t (V in lds[t & 1][1])
+  auto pv = [&](int t, int hf, const i32x8& pf) __attribute__((always_inline)) {
+    const unsigned char* vt = &lds[t & 1][1][0] + hf * 64 * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      i32x8 vf;
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        const i32x2 x = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (__attribute__((address_space(3))) i32x2*)(vt + v_off[db][tt]));
+        vf[2 * tt] = x[0];
+        vf[2 * tt + 1] = x[1];
+      }
+      oacc[db] = mfma_f8(vf, pf, oacc[db]);
+    }
+  };
+
+  // one barrier per tile; K and V of tile t + 1 load while tile t is processed
   if (n_kt > 0) dma(0);
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   __syncthreads();
   for (int t = 0; t < n_kt; ++t) {
     if (t + 1 < n_kt) dma(t + 1);
-    const int kbeg = t * TK;
-    if (kbeg < kend_w) {
-      const unsigned char* kt = &lds[t & 1][0][0];
-      const unsigned char* vt = &lds[t & 1][1][0];
+    if (t * TK < kend_w) {
       f32x16 st[NKB];
+      i32x8 pf[NH];
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        st[kb] = f32x16{};
+      for (int kb = 0; kb < NKB; ++kb) score_block(t, kb, st[kb]);
+      softmax(t * TK, st, pf);
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-          const uint4 x = *reinterpret_cast<const uint4*>(kt + k_off[2 * s] + kb * 32 * D);
-          const uint4 y = *reinterpret_cast<const uint4*>(kt + k_off[2 * s + 1] + kb * 32 * D);
-          const i32x8 af = {(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
-          st[kb] = mfma_f8(af, qf[s], st[kb]);
-        }
-      }
-      // register r of block kb holds key kbeg + 32 kb + 16 (r / 8) + 8 hh + r % 8
-      const bool edge = (kbeg + TK > lk) || (a.causal && kbeg + TK - 1 > qw0 + off);
-      if (edge) {
-        keep_branch();
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) mask_block(st[kb], lim - kbeg - 32 * kb - 8 * hh);
-      }
-      float mt0 = -INFINITY, mt1 = -INFINITY;  // raw score maximum (c > 0: a negative scale negates Q)
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          mt0 = fmaxf(mt0, st[kb][r]);
-          mt1 = fmaxf(mt1, st[kb][r + 1]);
-        }
-      float mt = half_max(fmaxf(mt0, mt1)) * a.c;
-      // lazy rescale: the reference m moves only when the row maximum passes
-      // it by more than a factor 2, so 2^7 p <= 2^8 stays inside E4M3 (448)
-      if (mt > m + 1.f) {
-        const float alpha = __builtin_amdgcn_exp2f(m - mt);  // 0 while m = -inf
-        l *= alpha;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-        m = mt;
-      }
-      // 2^7 p = exp2(c s - m + 7); the row sum keeps the same factor
-      const float nb = m == -INFINITY ? 0.f : 7.f - m;
-      float rs0 = 0.f, rs1 = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float pv = __builtin_amdgcn_exp2f(fmaf(st[kb][r], a.c, nb));
-          if (r & 1) rs1 += pv; else rs0 += pv;
-          st[kb][r] = pv;
-        }
-      l += rs0 + rs1;
-      // per 64 keys: P bytes 16 kb' + r <-> key 32 kb' + 16 (r / 8) + 8 hh + r % 8
-#pragma unroll
-      for (int hf = 0; hf < NH; ++hf) {
-        i32x8 pf;
-#pragma unroll
-        for (int w = 0; w < 8; ++w) {
-          const int kb = 2 * hf + (w >> 2), r0 = 4 * (w & 3);
-          pf[w] = pack_fp8x4(st[kb][r0], st[kb][r0 + 1], st[kb][r0 + 2], st[kb][r0 + 3]);
-        }
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          i32x8 vf;
-#pragma unroll
-          for (int tt = 0; tt < 4; ++tt) {
-            const i32x2 x = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                (__attribute__((address_space(3))) i32x2*)(vt + v_off[db][tt] + hf * 64 * D));
-            vf[2 * tt] = x[0];
-            vf[2 * tt + 1] = x[1];
-          }
-          oacc[db] = mfma_f8(vf, pf, oacc[db]);
-        }
-      }
+      for (int hf = 0; hf < NH; ++hf) pv(t, hf, pf[hf]);
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();
