@@ -38,6 +38,7 @@ PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["tiled_attention_fwd_amd/csrc/attn_device.h",
                   "tiled_attention_fwd_amd/csrc/attn_kernel.hip",
+                  "tiled_attention_fwd_amd/csrc/attn_kernel_d256.hip",
                   "tiled_attention_fwd_amd/csrc/rows_kernel.hip"]
 
 

@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libattnfwd.so")
 MICROBENCH = os.path.join(PKG, "microbench")  # bench-only executable (unit rates, copy bandwidth)
-SOURCES = ["attn_kernel.hip", "attn_bwd.hip", "decode_kernel.hip", "fp8_kernel.hip", "rows_kernel.hip", "debug_checks.hip", "noalloc.hip", "abi.cpp"]
+SOURCES = ["attn_kernel.hip", "attn_kernel_d256.hip", "attn_bwd.hip", "decode_kernel.hip", "fp8_kernel.hip", "rows_kernel.hip", "debug_checks.hip", "noalloc.hip", "abi.cpp"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 VALU ops.
@@ -37,7 +37,16 @@ COMMON_FLAGS = [
 # operands (head_dim 256 DMA kernel: ~900 -> ~50 AGPR copies per two tiles).
 # Not for the backward: its dK/dV accumulators are touched by MFMAs only, and
 # keeping them in AGPRs measured faster (1x8192: 1357 vs 1468 us).
-EXTRA_FLAGS = {"attn_kernel.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# The iterative ILP scheduler places LDS reads further ahead of the MFMAs
+# that use them, which pays where one wave per SIMD has to hide its own
+# latencies: the head_dim 256 forward kernels (their own unit, 1 x 4096
+# causal 212 -> 183 us) and the backward (dK/dV pass at one wave per SIMD;
+# 1x8192 causal 1353 -> 1250 us).  The other forward kernels, fp8 and the
+# paged decode measured within +-2 % with it and keep the default.
+_VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+_ILP = ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]
+EXTRA_FLAGS = {"attn_kernel.hip": _VGPR_FORM, "attn_kernel_d256.hip": _VGPR_FORM + _ILP,
+               "attn_bwd.hip": _ILP}
 
 
 def hipcc() -> str:

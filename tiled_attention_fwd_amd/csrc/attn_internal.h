@@ -119,6 +119,10 @@ bool select_policy(int head_dim, int max_seqlen_q, bool causal, int64_t rows, in
 hipError_t launch_attention(const AttnArgs& a, int head_dim, bool varlen, int policy_id,
                             hipStream_t stream);
 
+// The head_dim 256 part of launch_attention, compiled in its own translation
+// unit (attn_kernel_d256.hip) with a different instruction scheduler.
+hipError_t launch_attention_d256(const AttnArgs& a, bool varlen, int policy_id, hipStream_t stream);
+
 // Combines the partial outputs of split query blocks (after launch_attention
 // with n_split > 1).  bm is the query block of the policy used.
 hipError_t launch_merge(const AttnArgs& a, int head_dim, bool varlen, int bm, hipStream_t stream);

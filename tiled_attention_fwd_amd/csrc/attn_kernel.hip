@@ -1964,6 +1964,7 @@ hipError_t launch_v(const AttnArgs& a, bool varlen, int policy_id, hipStream_t s
 
 }  // namespace
 
+#ifndef ATTNFWD_D256_UNIT
 bool select_policy(int head_dim, int max_seqlen_q, bool causal, int64_t rows, int override_id,
                    TilePolicy* out, int* policy_id) {
   static const TilePolicy kTable[kNumPolicies] = {{4, 1, 64}, {2, 1, 64}, {4, 2, 64}, {8, 1, 64},
@@ -2073,9 +2074,18 @@ hipError_t launch_attention(const AttnArgs& a, int head_dim, bool varlen, int po
     case 32: return launch_v<32>(a, varlen, policy_id, stream);
     case 64: return launch_v<64>(a, varlen, policy_id, stream);
     case 128: return launch_v<128>(a, varlen, policy_id, stream);
-    case 256: return launch_v<256>(a, varlen, policy_id, stream);
+    case 256: return launch_attention_d256(a, varlen, policy_id, stream);
     default: return hipErrorInvalidValue;
   }
 }
+
+#else
+
+// Built from attn_kernel_d256.hip: the head_dim 256 instances only.
+hipError_t launch_attention_d256(const AttnArgs& a, bool varlen, int policy_id, hipStream_t stream) {
+  return launch_v<256>(a, varlen, policy_id, stream);
+}
+
+#endif  // ATTNFWD_D256_UNIT
 
 }  // namespace attnfwd
