@@ -269,3 +269,30 @@ def test_paged_noalloc_refuses_a_split_beyond_its_scratch_without_launching(lib,
                                     0.125, 1, P, None, None)
     assert st == 6
     assert b"scratch" in lib.attn_status_str(6)
+
+
+# The host plan for each configured workload (computed without a GPU): the
+# tile policy and block order the default call launches.  A change to the
+# selection shows up here first; the GPU tests then check each policy's
+# results against the oracle.
+PLANS = [
+    # (varlen, nseq, total_q, max_seqlen, heads_q, head_dim, causal) -> policy, order, bm
+    ((True, 1, 2048, 2048, 16, 128, True), (18, 1, 64)),       # bench step (b), 1 x 2048
+    ((True, 32, 2048, 64, 16, 128, True), (13, 2, 128)),       # 32 x 64 packed
+    ((True, 1, 8192, 8192, 16, 128, True), (19, 1, 256)),      # varlen 1 x 8192
+    ((False, 1, 8192, 8192, 64, 128, True), (19, 1, 256)),     # GQA S8192, 64 query heads
+    ((False, 149, 149 * 1024, 1024, 12, 64, False), (13, 3, 128)),  # ViT B149
+    ((True, 1, 4096, 4096, 128, 32, True), (19, 1, 256)),      # head_dim sweep
+    ((True, 1, 4096, 4096, 64, 64, True), (13, 1, 128)),
+    ((True, 1, 4096, 4096, 32, 128, True), (19, 1, 256)),
+    ((True, 1, 4096, 4096, 16, 256, True), (13, 1, 128)),
+    ((True, 8, 8192, 1024, 16, 256, True), (13, 2, 128)),      # head_dim 256: policy 13 throughout
+    ((True, 2, 590, 300, 4, 256, False), (13, 3, 128)),
+]
+
+
+@pytest.mark.parametrize("shape,want", PLANS)
+def test_launch_plan_of_configured_shapes(shape, want):
+    import tiled_attention_fwd_amd as t
+    plan = t.attn_fwd_launch_plan(*shape)
+    assert (plan["policy"], plan["order"], plan["bm"]) == want, plan

@@ -303,9 +303,9 @@ DEFAULT_BRANCHES = [
     ("d128_n_kg4", 128, False, [600], 4, 2, "18"),
     ("d128_n_split", 128, False, [1024] * 4, 8, 2, "12"),
     ("d128_c_1k", 128, True, [1024] * 4, 16, 4, "13"),
-    ("d256_c_many", 256, True, [256] * 64, 8, 2, "3"),
-    ("d256_c_round", 256, True, [256] * 16, 8, 2, "0"),
-    ("d256_n_few", 256, False, [300, 290], 4, 2, "0"),
+    ("d256_c_many", 256, True, [256] * 64, 8, 2, "13"),
+    ("d256_c_round", 256, True, [256] * 16, 8, 2, "13"),
+    ("d256_n_few", 256, False, [300, 290], 4, 2, "13"),
 ]
 
 

@@ -2027,15 +2027,13 @@ bool select_policy(int head_dim, int max_seqlen_q, bool causal, int64_t rows, in
       // S1024 x 16 heads causal: 12 us vs 17 on 13; S8192 x 64 heads 402 vs 449
       id = wg256 >= (causal ? 1024 : 256) ? 19 : 20;
     } else {
-      // head_dim 256: eight waves (3) once the blocks fill the CUs several
-      // times; four-wave staged blocks (0) when they fill about one round
-      // (S1024 x 32 heads causal 57 us vs 87 on 13)
-      if (wg128 >= (causal ? 1024 : 512))
-        id = 3;
-      else if (!causal || (wg128 > 128 && wg128 <= 256))
-        id = 0;
-      else
-        id = 13;
+      // head_dim 256 (one wave per SIMD, built with the iterative ILP
+      // scheduler): the DMA-staged 128-query block beat the staged kernels
+      // (0, 3) on 10 of 11 shapes from 2 x 300 to 1 x 8192 x 32 heads, causal
+      // and not (1 x 4096 x 16 heads causal 186 us vs 207 on 0 and 465 on 3;
+      // 4 x 2048 non-causal 348 vs 381 and 491); 8 x 1024 x 16 heads causal
+      // is the exception at 172 vs 165 on 0
+      id = 13;
     }
   }
   *out = kTable[id];
