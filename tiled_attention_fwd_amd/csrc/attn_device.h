@@ -119,6 +119,19 @@ __device__ __forceinline__ u32x4 make_desc(const void* base, uint32_t bytes) {
   return d;
 }
 
+// The descriptor d (from make_desc) advanced by ofs bytes: base + ofs, and the
+// range shortened by ofs (to 0 past its end), so loads relative to the new
+// base still read zero beyond the original end.  Scalar arithmetic only.
+__device__ __forceinline__ u32x4 desc_advance(u32x4 d, uint32_t ofs) {
+  const uint64_t base = (((uint64_t)(d[1] & 0xffffu)) << 32 | d[0]) + ofs;
+  u32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((uint32_t)base);
+  r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32) & 0xffffu);
+  r[2] = __builtin_amdgcn_readfirstlane(d[2] > ofs ? d[2] - ofs : 0u);
+  r[3] = d[3];
+  return r;
+}
+
 // 32-bit LDS byte address of a pointer into a __shared__ array.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) char*)p);

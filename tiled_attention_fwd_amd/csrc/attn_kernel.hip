@@ -1003,21 +1003,12 @@ __global__ __launch_bounds__(WAVES * 64, D == 256 ? 1 : 2) void attn_fwd_dma_ker
     voffp[i] = (uint32_t)(g * BN + row) * v_row_bytes + (uint32_t)((phys ^ swz_v<D>(row)) * 16);
   }
   // the buffer of rows [first row of the step, end of sequence)
-  auto step_desc = [](u32x4 d, uint32_t ofs) __attribute__((always_inline)) {
-    const uint64_t base = (((uint64_t)(d[1] & 0xffffu)) << 32 | d[0]) + ofs;
-    u32x4 r;
-    r[0] = __builtin_amdgcn_readfirstlane((uint32_t)base);
-    r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32) & 0xffffu);
-    r[2] = __builtin_amdgcn_readfirstlane(d[2] > ofs ? d[2] - ofs : 0u);
-    r[3] = d[3];
-    return r;
-  };
   struct StepDesc {
     u32x4 k, v;
   };
   auto descs_of = [&](int step) __attribute__((always_inline)) {
     const uint32_t kbeg = __builtin_amdgcn_readfirstlane((t_begin + step * KG) * BN);
-    return StepDesc{step_desc(kdesc, kbeg * k_row_bytes), step_desc(vdesc, kbeg * v_row_bytes)};
+    return StepDesc{desc_advance(kdesc, kbeg * k_row_bytes), desc_advance(vdesc, kbeg * v_row_bytes)};
   };
   auto dma_pair = [&](auto Bc, const StepDesc& sd, int i) __attribute__((always_inline)) {
     constexpr int B = decltype(Bc)::value;

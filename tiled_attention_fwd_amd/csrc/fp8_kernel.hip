@@ -140,18 +140,35 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_fp8_kernel(const AttnA
   const uint32_t vbytes = vspan > 0xffffffffLL ? 0xffffffffu : (uint32_t)vspan;
   const u32x4 vdesc = make_desc(vp + krow0 * a.v_ss + (int64_t)kvh * a.v_hs, vbytes);
   const uint32_t lds0 = lds_addr(lds);
-  const int dma_p = lane % T::CPR;
+  // This wave's DMA instructions of a tile are q = wave + WAVES i; their lane
+  // byte offsets inside the tile's rows are the same every tile, so they are
+  // computed once, and tile t moves the buffer base by t TK rows instead
+  // (scalar arithmetic): an instruction is then one M0 write and one load.
+  // K rows land permuted by tile_key_of_row (the score registers then come
+  // out in the order the P operand needs).
+  constexpr int NP = T::NI / WAVES;
+  static_assert(T::NI % WAVES == 0, "every wave issues the same number of loads");
+  uint32_t koffp[NP], voffp[NP];
+  {
+    const int dma_p = lane % T::CPR;
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int r = (wave + WAVES * i) * T::R + lane / T::CPR;
+      koffp[i] = (uint32_t)tile_key_of_row(r) * (uint32_t)a.k_ss + 16 * (uint32_t)(dma_p ^ T::swz_k(r));
+      voffp[i] = (uint32_t)r * (uint32_t)a.v_ss + 16 * (uint32_t)(dma_p ^ T::swz_v(r));
+    }
+  }
   // K rows of tile t into lds[t & 1][0], V rows into lds[t & 1][1]
-  auto dma = [&](int t) {
+  auto dma = [&](int t) __attribute__((always_inline)) {
     const uint32_t b = lds0 + (uint32_t)(t & 1) * 2 * T::BYTES;
-    for (int q = wave; q < T::NI; q += WAVES) {
-      const int r = q * T::R + lane / T::CPR;
-      const uint32_t ko = (uint32_t)(t * TK + tile_key_of_row(r)) * (uint32_t)a.k_ss +
-                          16 * (uint32_t)(dma_p ^ T::swz_k(r));
-      dma16(kdesc, ko, __builtin_amdgcn_readfirstlane(b + q * 1024));
-      const uint32_t vo = (uint32_t)(t * TK + r) * (uint32_t)a.v_ss +
-                          16 * (uint32_t)(dma_p ^ T::swz_v(r));
-      dma16(vdesc, vo, __builtin_amdgcn_readfirstlane(b + T::BYTES + q * 1024));
+    const uint32_t row0 = __builtin_amdgcn_readfirstlane(t * TK);
+    const u32x4 kd = desc_advance(kdesc, row0 * (uint32_t)a.k_ss);
+    const u32x4 vd = desc_advance(vdesc, row0 * (uint32_t)a.v_ss);
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int q = wave + WAVES * i;
+      dma16(kd, koffp[i], __builtin_amdgcn_readfirstlane(b + q * 1024));
+      dma16(vd, voffp[i], __builtin_amdgcn_readfirstlane(b + T::BYTES + q * 1024));
     }
   };
 
