@@ -22,7 +22,9 @@
  * Conventions shared by every entry point:
  *  - Every tensor pointer is a DEVICE pointer owned by the caller.  The library
  *    allocates nothing, frees nothing and never synchronises the stream; the
- *    only scratch memory it uses is a workspace the caller passes (_ws calls).
+ *    only scratch memory it uses is a workspace the caller passes (_ws calls,
+ *    attn_fwd_paged), except attn_fwd_paged_noalloc, which uses a fixed array
+ *    of the library's own in device memory (declared with it below).
  *  - bfloat16 tensors are passed as raw 16-bit storage (const void*).
  *  - `stream` is a hipStream_t cast to void*; NULL means the default stream.
  *    Work is enqueued asynchronously on it.
@@ -30,6 +32,20 @@
  *    error nothing is launched and the status says why.  Device-side faults (for
  *    example cu_seqlens that do not match the tensors) surface at the caller's
  *    next synchronisation; the preconditions below say what must hold.
+ *  - Tuning and test overrides (environment variables read at each call; unset
+ *    means the library's own choice, which is what the results are measured
+ *    with): ATTN_FWD_TILE=<policy> forces a compiled forward tile policy
+ *    (sweeps; an uncompiled one returns ATTN_ERR_UNSUPPORTED),
+ *    ATTN_FWD_SPLIT_TILES=<n> forces key-range parts of at most n tiles on the
+ *    split-capable policies when a workspace is given, ATTN_FWD_ORDER=<1..4>
+ *    forces the workgroup order (head-remapped block-major, sequence-major,
+ *    unit-major, compact), ATTN_FP8_TILE=128|256 forces the fp8 query block,
+ *    ATTN_PAGED_VARIANT=<0..2>, ATTN_PAGED_ORDER=0|1 and
+ *    ATTN_PAGED_CHUNK_TILES=<n> force the paged kernel's layout, grid order
+ *    and key-range parts, and ATTN_BWD_SPLIT=1 runs the backward's dV and dK
+ *    as two passes.  Every forced choice computes the same attention; the
+ *    GPU tests compare them with the oracle and, where the arithmetic is the
+ *    same, bit for bit with the default.
  *  - Debug mode: with the environment variable ATTN_FWD_DEBUG set (to anything
  *    but "0"), every call that takes device-resident metadata first checks it
  *    on the device (cu_seqlens start at 0, never decrease, end at the total,
