@@ -253,7 +253,7 @@ def run_backward(torch, t, names, flush):
     rows = []
     for name in names:
         w = gen.build_workload(name)
-        if w.d not in (64, 128) or w.kind == "padded":
+        if w.d not in (32, 64, 128) or w.kind == "padded":
             continue
         dev = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to("cuda").view(torch.bfloat16)
         q, k, v = dev(w.q), dev(w.k), dev(w.v)
@@ -467,7 +467,7 @@ def main():
     ap.add_argument("--configs", default="all",
                     help="comma list of extra workloads to time per call, 'all' or 'none'")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
-    ap.add_argument("--bwd-configs", default="varlen_1x8192,hdim_sweep_d128,hdim_sweep_d64",
+    ap.add_argument("--bwd-configs", default="varlen_1x8192,hdim_sweep_d128,hdim_sweep_d64,hdim_sweep_d32",
                     help="comma list of workloads whose backward is timed, or 'none'")
     ap.add_argument("--paged-configs", default="all",
                     help="comma list of paged KV-cache workloads, 'all' or 'none'")

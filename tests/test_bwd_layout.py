@@ -28,13 +28,13 @@ def key_of_row(i):
 def layout(d):
     cpr = d // 8
     r = 64 // cpr
-    g = 1024 + (64 if r == 4 else 128)
-    rot = (lambda c: 4 * ((c ^ (c >> 1)) & 1)) if r == 8 else (lambda c: 0)
+    g = 1024 + {4: 64, 8: 128, 16: 0}[r]
+    rot = {8: lambda c: 4 * ((c ^ (c >> 1)) & 1), 16: lambda c: 4 * c}.get(r, lambda c: 0)
     at = lambda row, c: (row // r) * g + 16 * (c * r + ((row % r) ^ rot(c)))
     return r, g, rot, at
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [32, 64, 128])
 def test_dma_placement_and_fragment_reads(d):
     r, g, rot, at = layout(d)
     ni = 64 // r

@@ -550,6 +550,8 @@ hipError_t launch_attention_bwd(const AttnArgs& a, int head_dim, bool varlen, co
                                 float* dq, float* dk, float* dv, int64_t n_pairs, int n_kb,
                                 hipStream_t stream) {
   switch (head_dim) {
+    case 32: return varlen ? bwd_d<32, true>(a, dout, dq, dk, dv, n_pairs, n_kb, stream)
+                           : bwd_d<32, false>(a, dout, dq, dk, dv, n_pairs, n_kb, stream);
     case 64: return varlen ? bwd_d<64, true>(a, dout, dq, dk, dv, n_pairs, n_kb, stream)
                            : bwd_d<64, false>(a, dout, dq, dk, dv, n_pairs, n_kb, stream);
     case 128: return varlen ? bwd_d<128, true>(a, dout, dq, dk, dv, n_pairs, n_kb, stream)

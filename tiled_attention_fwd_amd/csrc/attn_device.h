@@ -146,16 +146,19 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) |
 // and consecutive instructions are G bytes apart (G_K for tiles read as rows,
 // G_V for tiles read transposed).  Fragment addresses are then (lane base) +
 // (constant), and both read patterns are free of bank conflicts (see the
-// software-pipelined forward kernel for the argument).
+// software-pipelined forward kernel for the argument).  At head_dim 32 an
+// instruction moves 16 rows; there the blocks need no padding and chunk c is
+// rotated by 4 c, which keeps both read patterns of the backward's tiles free
+// of bank conflicts (checked by a host model of the placement and reads).
 template <int D>
 struct PipeLayout {
   static constexpr int CPR = D / 8;
   static constexpr int R = 64 / CPR;
-  static_assert(R == 4 || R == 8, "layout defined for head_dim 128 and 64");
-  static constexpr int GK = 1024 + (R == 4 ? 64 : 128);
+  static_assert(R == 4 || R == 8 || R == 16, "layout defined for head_dim 128, 64 and 32");
+  static constexpr int GK = 1024 + (R == 4 ? 64 : (R == 8 ? 128 : 0));
   static constexpr int GV = 1024;
   static __device__ __forceinline__ int rot(int c) {
-    return R == 8 ? 4 * ((c ^ (c >> 1)) & 1) : 0;
+    return R == 8 ? 4 * ((c ^ (c >> 1)) & 1) : (R == 16 ? 4 * c : 0);
   }
   // byte offset of (row, chunk) inside a tile with instruction stride G
   static __device__ __forceinline__ int at(int row, int c, int G) {
