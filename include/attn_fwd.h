@@ -357,7 +357,7 @@ attn_status_t attn_fwd_padded(const void* q, const void* k, const void* v,
  *          attn_fwd_paged_workspace_bytes(...) bytes: lets long key ranges be
  *          split over several workgroups (one more launch merges them).  Too
  *          small or NULL: no split.
- * head_dim 64 or 128; page_size a positive multiple of 16; one page of one
+ * head_dim 32, 64 or 128; page_size a positive multiple of 16; one page of one
  * tensor (page_size * num_heads_k * head_dim * 2 bytes) under 4 GiB.
  * GQA: the query heads of one KV head are processed together, so each K/V
  * byte is read once per (sequence, KV head).  One or two launches on `stream`.
@@ -381,7 +381,8 @@ attn_status_t attn_fwd_paged(const void* q, const void* k_cache, const void* v_c
  * k_cache, v_cache (num_pages, page_size, num_heads_k, head_dim): E4M3 bytes;
  * the keys and values are k_scale * K and v_scale * V (factors > 0, finite).
  * q stays bf16.  Every other argument, the workspace and the size rules are
- * those of attn_fwd_paged (the page-size limit counts one byte per element).
+ * those of attn_fwd_paged (the page-size limit counts one byte per element),
+ * except that head_dim must be 64 or 128 (else ATTN_ERR_UNSUPPORTED).
  * The cache bytes are dequantised to bf16 in registers (E4M3 values are exact
  * in bf16) and the products are the bf16 MFMAs of attn_fwd_paged, so the
  * results carry the same rounding as the bf16 path on the dequantised values.

@@ -226,7 +226,7 @@ def test_paged_fp8_and_mask_argument_checks(lib):
         return f(P, P, P, P, P, P, 2, 2, 8, a["ps"], a["maxp"], a["hq"], a["hkv"], a["d"], a["mq"],
                  a["mk"], 0.125, 1, a["out"], None, a["ws"], a["wsb"], None)
     assert paged(ps=8) == UNSUP and paged(ps=24) == UNSUP      # page size: a multiple of 16
-    assert paged(d=32) == UNSUP and paged(d=256) == UNSUP
+    assert paged(d=48) == UNSUP and paged(d=256) == UNSUP
     assert paged(mk=33) == SHAPE                                # > max_pages * page_size
     assert paged(mq=0) == SHAPE
     assert paged(hq=6, hkv=4) == SHAPE
@@ -236,6 +236,8 @@ def test_paged_fp8_and_mask_argument_checks(lib):
     base = (P, P, P, P, P, P, 2, 2, 8, 16, 2, 8, 2, 128, 1, 32, 0.125)
     assert g(*base, 0.0, 1.0, 1, P, None, None, 0, None) == UNSUP   # k factor
     assert g(*base, 1.0, float("inf"), 1, P, None, None, 0, None) == UNSUP
+    base32 = base[:13] + (32,) + base[14:]                       # E4M3 tiles: head_dim 64 and 128
+    assert g(*base32, 1.0, 1.0, 1, P, None, None, 0, None) == UNSUP
     ws = lib.attn_fwd_paged_workspace_bytes
     assert ws(32, 1, 8192, 64, 8, 128) > 0                      # few workgroups: splits
     assert ws(32, 1, 8192, 64, 8, 96) == 0 and ws(0, 1, 8, 8, 8, 128) == 0

@@ -45,19 +45,20 @@ constexpr int kTileKeys = 32;
 // position p of row r holds chunk p ^ swz(r).  K rows hold key key_of_row(r)
 // (the accumulator order the P operand needs), V rows their own key.  The
 // swizzles make the K row fragments and the V transposed fragments free of
-// bank conflicts.
+// bank conflicts (at d=32 a row is one 64-byte segment: K rotates by (r / 4)
+// mod 4 chunks, V needs none).
 template <int D>
 struct RowTile {
   static constexpr int CPR = D / 8;        // 16-byte chunks per row
   static constexpr int R = 64 / CPR;       // rows per DMA instruction
   static constexpr int PITCH = 2 * D;      // bytes per row
   static constexpr int BYTES = kTileKeys * PITCH;
-  static_assert(D == 64 || D == 128, "tile layout defined for head_dim 64 and 128");
+  static_assert(D == 32 || D == 64 || D == 128, "tile layout defined for head_dim 32, 64 and 128");
   static __device__ __forceinline__ int swz_k(int row) {
-    return D == 128 ? (row & 15) : ((row >> 1) & 7);
+    return D == 128 ? (row & 15) : (D == 64 ? ((row >> 1) & 7) : ((row >> 2) & 3));
   }
   static __device__ __forceinline__ int swz_v(int row) {
-    return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
+    return D == 128 ? ((row & 3) << 2) : (D == 64 ? (((row >> 1) & 1) << 2) : 0);
   }
 };
 
@@ -535,8 +536,8 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeArgs a) {
 // CU's LDS, so the product of the two is bounded by the tile size; the
 // variants trade waves (latency hiding of the softmax/MFMA work) for stages
 // (tiles in flight per wave).  d=128 (16 KiB per stage): 0 = 4 waves x 2
-// stages, 1 = 3 x 3, 2 = 5 x 2; d=64 (8 KiB per stage): 0 = 4 x 4, 1 = 8 x 2,
-// 2 = 5 x 4.
+// stages, 1 = 3 x 3, 2 = 5 x 2; d=64 (8 KiB per stage) and d=32 (4 KiB):
+// 0 = 4 x 4, 1 = 8 x 2, 2 = 5 x 4.
 template <int D, int W, int NB, int ES>
 hipError_t launch_v(const DecodeArgs& a, int64_t grid, hipStream_t stream) {
   hipLaunchKernelGGL((attn_decode_kernel<D, W, NB, ES>), dim3((unsigned)grid), dim3(W * 64), 0,
@@ -552,7 +553,13 @@ hipError_t launch_d(const DecodeArgs& a, int variant, hipStream_t stream) {
   // Defaults (variant < 0) from measured sweeps: more waves beat more stages
   // for bf16 caches (d=128 decode: 4x2 3.8, 3x3 3.6, 5x2 4.5 TB/s; d=64: 4x4
   // 3.4, 8x2 4.5, 5x4 4.2 TB/s).  E4M3 caches halve the stage size.
-  if (a.kv_fp8) {
+  if constexpr (D == 32) {
+    // bf16 caches only (E4M3 tiles are laid out for head_dim 64 and 128)
+    if (a.kv_fp8) return hipErrorInvalidValue;
+    if (variant == 0) launch_v<D, 4, 4, 2>(a, grid, stream);
+    else if (variant == 2) launch_v<D, 5, 4, 2>(a, grid, stream);
+    else launch_v<D, 8, 2, 2>(a, grid, stream);
+  } else if (a.kv_fp8) {
     // E4M3 caches, d=128 decode b32 GQA-8 (cold): 4x4 195, 8x2 173, 5x4 184 us
     if constexpr (D == 128) {
       if (variant == 0) launch_v<D, 4, 4, 1>(a, grid, stream);
@@ -583,6 +590,7 @@ hipError_t launch_d(const DecodeArgs& a, int variant, hipStream_t stream) {
 
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, int variant, hipStream_t stream) {
   switch (head_dim) {
+    case 32: return launch_d<32>(a, variant, stream);
     case 64: return launch_d<64>(a, variant, stream);
     case 128: return launch_d<128>(a, variant, stream);
     default: return hipErrorInvalidValue;
