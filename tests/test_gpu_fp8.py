@@ -73,7 +73,7 @@ def fp8_tile(request, monkeypatch):
     return request.param
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [32, 64, 128])
 @pytest.mark.parametrize("causal", [True, False])
 def test_fp8_varlen_ragged_gqa(d, causal, fp8_tile):
     w = gen.make_fp8_varlen(f"f8v{d}", 2000 + d, [1, 7, 64, 100, 129, 300, 33, 700], 4, 2, d,
@@ -82,7 +82,7 @@ def test_fp8_varlen_ragged_gqa(d, causal, fp8_tile):
     print(check_fp8(w, o, lse, causal))
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [32, 64, 128])
 @pytest.mark.parametrize("causal", [True, False])
 def test_fp8_lq_ne_lk_and_empty(d, causal, fp8_tile):
     w = gen.make_fp8_varlen("f8ne", 2100 + d, [5, 130, 0, 64, 3, 0, 300], 2, 2, d, causal,

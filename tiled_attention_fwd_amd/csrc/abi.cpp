@@ -312,7 +312,7 @@ attn_status_t check_fp8(int32_t hq, int32_t hkv, int32_t d, float scale, float q
                         float vs) {
   attn_status_t st = check_common(hq, hkv, d, scale);
   if (st != ATTN_OK) return st;
-  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  if (d != 32 && d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
   for (float f : {qs, ks, vs})
     if (!(f > 0.f) || !isfinite(f)) return ATTN_ERR_UNSUPPORTED;
   return ATTN_OK;

@@ -47,8 +47,12 @@ struct F8Tile {
   static constexpr int R = 1024 / D;    // rows per DMA instruction
   static constexpr int NI = TK / R;     // DMA instructions per TK-row tile
   static constexpr int BYTES = TK * D;
-  static __device__ __forceinline__ int swz_k(int r) { return D == 128 ? ((r >> 1) & 7) : ((r >> 2) & 3); }
-  static __device__ __forceinline__ int swz_v(int r) { return D == 128 ? (r & 7) : (((r >> 2) & 1) << 1); }
+  static __device__ __forceinline__ int swz_k(int r) {
+    return D == 128 ? ((r >> 1) & 7) : (D == 64 ? ((r >> 2) & 3) : ((r ^ (r >> 3)) & 1));
+  }
+  static __device__ __forceinline__ int swz_v(int r) {
+    return D == 128 ? (r & 7) : (D == 64 ? (((r >> 2) & 1) << 1) : ((r ^ (r >> 1)) & 1));
+  }
 };
 
 __device__ __forceinline__ int tile_key_of_row(int r) { return (r & ~31) + key_of_row(r & 31); }
@@ -65,7 +69,10 @@ template <int D, bool VARLEN, int WAVES, int TK>
 __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_fp8_kernel(const AttnArgs a, float o_mul) {
   using T = F8Tile<D, TK>;
   constexpr int BM = WAVES * 32;
-  constexpr int NS = D / 64;   // fp8 MFMAs per 32x32 score block
+  // fp8 MFMAs per 32x32 score block (64 dims each).  At head_dim 32 the one
+  // product takes dims 0..31 from lane half 0 and zeros from lane half 1 (its
+  // Q operand is 0, and its K operand repeats half 0's bytes).
+  constexpr int NS = (D + 63) / 64;
   constexpr int NDB = D / 32;  // 32-dim output blocks
   constexpr int NKB = TK / 32; // 32-key score blocks per tile
   constexpr int NH = TK / 64;  // 64-key halves (one P operand each)
@@ -121,14 +128,16 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_fp8_kernel(const AttnA
     const int64_t span = (int64_t)lq * a.q_ss;
     const __amdgpu_buffer_rsrc_t qrs =
         make_rsrc(qbase, span > 0xffffffffLL ? 0xffffffffu : (uint32_t)span);
-    const uint32_t ob = (uint32_t)qrow * (uint32_t)a.q_ss + 32 * hh;
+    const uint32_t ob = (uint32_t)qrow * (uint32_t)a.q_ss + (D == 32 ? 0 : 32 * hh);
+    // head_dim 32: lane half 1 carries dims 32..63, which do not exist
+    const uint32_t zero_half = (D == 32 && hh == 1) ? ~0u : 0u;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(qrs, (int)(ob + 64 * s), 0, 0);
       u32x4 y = __builtin_amdgcn_raw_buffer_load_b128(qrs, (int)(ob + 64 * s + 16), 0, 0);
       asm volatile("" : "+v"(x), "+v"(y));
-      x = q_sign(x, a.q_xor, a.q_clear);
-      y = q_sign(y, a.q_xor, a.q_clear);
+      x = q_sign(x, a.q_xor, a.q_clear | zero_half);
+      y = q_sign(y, a.q_xor, a.q_clear | zero_half);
       qf[s] = i32x8{(int)x[0], (int)x[1], (int)x[2], (int)x[3], (int)y[0], (int)y[1], (int)y[2], (int)y[3]};
     }
   }
@@ -146,8 +155,9 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_fp8_kernel(const AttnA
   // (scalar arithmetic): an instruction is then one M0 write and one load.
   // K rows land permuted by tile_key_of_row (the score registers then come
   // out in the order the P operand needs).
-  constexpr int NP = T::NI / WAVES;
-  static_assert(T::NI % WAVES == 0, "every wave issues the same number of loads");
+  // (head_dim 32: a tile is fewer instructions than waves; the rest issue none)
+  constexpr int NP = (T::NI + WAVES - 1) / WAVES;
+  static_assert(T::NI % WAVES == 0 || T::NI < WAVES, "every wave issues the same number of loads");
   uint32_t koffp[NP], voffp[NP];
   {
     const int dma_p = lane % T::CPR;
@@ -167,8 +177,10 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_fp8_kernel(const AttnA
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
       const int q = wave + WAVES * i;
-      dma16(kd, koffp[i], __builtin_amdgcn_readfirstlane(b + q * 1024));
-      dma16(vd, voffp[i], __builtin_amdgcn_readfirstlane(b + T::BYTES + q * 1024));
+      if (T::NI >= WAVES || q < T::NI) {
+        dma16(kd, koffp[i], __builtin_amdgcn_readfirstlane(b + q * 1024));
+        dma16(vd, voffp[i], __builtin_amdgcn_readfirstlane(b + T::BYTES + q * 1024));
+      }
     }
   };
 
@@ -180,7 +192,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_fp8_kernel(const AttnA
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const int r = l32;
-      const int c = 4 * s + 2 * hh + half;
+      const int c = D == 32 ? half : 4 * s + 2 * hh + half;
       k_off[2 * s + half] = r * D + 16 * (c ^ T::swz_k(r));
     }
   const int vg = (lane >> 4) & 1, vi = lane & 15;
@@ -327,6 +339,9 @@ hipError_t launch_attention_fp8(const AttnArgs& a, int head_dim, bool varlen, fl
   else                                                                                          \
     hipLaunchKernelGGL((attn_fwd_fp8_kernel<D_, V_, 4, 64>), g, b, 0, stream, a, o_mul);
   switch (head_dim) {
+    case 32:
+      if (varlen) { ATTN_FP8_LAUNCH(32, true) } else { ATTN_FP8_LAUNCH(32, false) }
+      break;
     case 64:
       if (varlen) { ATTN_FP8_LAUNCH(64, true) } else { ATTN_FP8_LAUNCH(64, false) }
       break;
