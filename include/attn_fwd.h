@@ -455,8 +455,9 @@ int64_t attn_fwd_paged_workspace_bytes(int32_t num_seqs, int32_t max_seqlen_q,
  * Precision: the scores and the row sums are exact products in fp32; the
  * probabilities enter the P*V product as E4M3 (after scaling by 2^8), so the
  * output carries their rounding (at most 2^-4 relative per probability).
- * head_dim 32, 64 or 128 (else ATTN_ERR_UNSUPPORTED; at 32 the fp8 MFMA's
- * 64-element reduction runs half empty).  One launch.
+ * head_dim 32, 64, 128 or 256 (else ATTN_ERR_UNSUPPORTED; at 32 the fp8
+ * MFMA's 64-element reduction runs half empty; at 256 the query block is 128
+ * and forcing ATTN_FP8_TILE=256 returns ATTN_ERR_UNSUPPORTED).  One launch.
  */
 attn_status_t attn_fwd_fp8_varlen(const void* q, const void* k, const void* v,
                                   const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,

@@ -243,12 +243,12 @@ def test_paged_fp8_and_mask_argument_checks(lib):
     assert ws(32, 1, 8192, 64, 8, 96) == 0 and ws(0, 1, 8, 8, 8, 128) == 0
     h = lib.attn_fwd_fp8_varlen
     # q, k, v, cu_q, cu_k, nseq, tq, tk, hq, hkv, d, max, scale, qs, ks, vs, causal, out, lse, s
-    assert h(P, P, P, P, P, 1, 8, 8, 2, 2, 256, 8, 0.125, 1.0, 1.0, 1.0, 1, P, None, None) == UNSUP
+    assert h(P, P, P, P, P, 1, 8, 8, 2, 2, 96, 8, 0.125, 1.0, 1.0, 1.0, 1, P, None, None) == UNSUP
     assert h(P, P, P, P, P, 1, 8, 8, 2, 2, 64, 8, 0.125, -1.0, 1.0, 1.0, 1, P, None, None) == UNSUP
     assert h(P, P, P, P, P, 1, 8, 8, 2, 2, 64, 0, 0.125, 1.0, 1.0, 1.0, 1, P, None, None) == SHAPE
     assert h(None, P, P, P, P, 1, 8, 8, 2, 2, 64, 8, 0.125, 1.0, 1.0, 1.0, 1, P, None, None) == NULL
     d = lib.attn_fwd_fp8_dense
-    assert d(P, P, P, 1, 8, 8, 2, 2, 256, 0.125, 1.0, 1.0, 1.0, 1, P, None, None) == UNSUP
+    assert d(P, P, P, 1, 8, 8, 2, 2, 48, 0.125, 1.0, 1.0, 1.0, 1, P, None, None) == UNSUP
     assert d(P, P, P, 0, 8, 8, 2, 2, 128, 0.125, 1.0, 1.0, 1.0, 1, None, None, None) == OK
     m = lib.attn_mask_to_varlen
     assert m(P, -1, 4, P, P, P, None) == SHAPE

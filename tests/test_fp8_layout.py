@@ -25,18 +25,18 @@ def key_of_row(i):
 
 
 def swz_k(d, r):
-    return {128: (r >> 1) & 7, 64: (r >> 2) & 3, 32: (r ^ (r >> 3)) & 1}[d]
+    return {256: r & 15, 128: (r >> 1) & 7, 64: (r >> 2) & 3, 32: (r ^ (r >> 3)) & 1}[d]
 
 
 def swz_v(d, r):
-    return {128: r & 7, 64: ((r >> 2) & 1) << 1, 32: (r ^ (r >> 1)) & 1}[d]
+    return {256: (r & 7) << 1, 128: r & 7, 64: ((r >> 2) & 1) << 1, 32: (r ^ (r >> 1)) & 1}[d]
 
 
 def krow(r):
     return 32 * (r // 32) + key_of_row(r % 32)
 
 
-@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("d", [32, 64, 128, 256])
 def test_fp8_tiles(d):
     cpr = d // 16
     rows_per = 1024 // d

@@ -73,22 +73,31 @@ def fp8_tile(request, monkeypatch):
     return request.param
 
 
-@pytest.mark.parametrize("d", [32, 64, 128])
+def run_checked(w, fp8_tile, causal):
+    """run_varlen, except that head_dim 256 has 128-query blocks only: a forced
+    256-query block must be refused before anything is launched."""
+    if w.d == 256 and fp8_tile == "256":
+        with pytest.raises(api().AttnError, match="UNSUPPORTED"):
+            run_varlen(w)
+        return None
+    o, lse = run_varlen(w)
+    return check_fp8(w, o, lse, causal)
+
+
+@pytest.mark.parametrize("d", [32, 64, 128, 256])
 @pytest.mark.parametrize("causal", [True, False])
 def test_fp8_varlen_ragged_gqa(d, causal, fp8_tile):
     w = gen.make_fp8_varlen(f"f8v{d}", 2000 + d, [1, 7, 64, 100, 129, 300, 33, 700], 4, 2, d,
                             causal)
-    o, lse = run_varlen(w)
-    print(check_fp8(w, o, lse, causal))
+    print(run_checked(w, fp8_tile, causal))
 
 
-@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("d", [32, 64, 128, 256])
 @pytest.mark.parametrize("causal", [True, False])
 def test_fp8_lq_ne_lk_and_empty(d, causal, fp8_tile):
     w = gen.make_fp8_varlen("f8ne", 2100 + d, [5, 130, 0, 64, 3, 0, 300], 2, 2, d, causal,
                             lengths_k=[9, 70, 12, 200, 0, 0, 190])
-    o, lse = run_varlen(w)
-    print(check_fp8(w, o, lse, causal))
+    print(run_checked(w, fp8_tile, causal))
 
 
 def test_fp8_factors(fp8_tile):
@@ -97,14 +106,17 @@ def test_fp8_factors(fp8_tile):
     print(check_fp8(w, o, lse, True))
 
 
+@pytest.mark.parametrize("d", [128, 256])
 @pytest.mark.parametrize("causal", [True, False])
-def test_fp8_dense_matches_varlen(causal, fp8_tile):
+def test_fp8_dense_matches_varlen(d, causal, fp8_tile):
     t = api()
-    w = gen.make_fp8_varlen("f8d", 2300, [200, 200], 4, 2, 128, causal)
+    if d == 256 and fp8_tile == "256":
+        pytest.skip("head_dim 256 has 128-query blocks only (the refusal is tested above)")
+    w = gen.make_fp8_varlen("f8d", 2300 + d, [200, 200], 4, 2, d, causal)
     o_v, l_v = run_varlen(w)
-    q = dev_u8(w.q.reshape(2, 200, 4, 128))
-    k = dev_u8(w.k.reshape(2, 200, 2, 128))
-    v = dev_u8(w.v.reshape(2, 200, 2, 128))
+    q = dev_u8(w.q.reshape(2, 200, 4, d))
+    k = dev_u8(w.k.reshape(2, 200, 2, d))
+    v = dev_u8(w.v.reshape(2, 200, 2, d))
     o_d, l_d = t.attn_fwd_fp8_dense(q, k, v, scale=float(w.scale), causal=causal)
     assert np.array_equal(host(o_d).reshape(o_v.shape), o_v)
     assert np.array_equal(host(l_d).transpose(1, 0, 2).reshape(l_v.shape), l_v)

@@ -312,7 +312,7 @@ attn_status_t check_fp8(int32_t hq, int32_t hkv, int32_t d, float scale, float q
                         float vs) {
   attn_status_t st = check_common(hq, hkv, d, scale);
   if (st != ATTN_OK) return st;
-  if (d != 32 && d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  if (d != 32 && d != 64 && d != 128 && d != 256) return ATTN_ERR_UNSUPPORTED;
   for (float f : {qs, ks, vs})
     if (!(f > 0.f) || !isfinite(f)) return ATTN_ERR_UNSUPPORTED;
   return ATTN_OK;
@@ -338,6 +338,7 @@ attn_status_t launch_fp8(AttnArgs& a, int d, bool varlen, int max_q, float scale
   const int64_t rows = (int64_t)a.nseq * a.hq;
   int bm = 128;
   if (fp8_tile_override() > 0) bm = fp8_tile_override();
+  if (d == 256 && bm != 128) return ATTN_ERR_UNSUPPORTED;  // 256-query blocks: head_dim <= 128
   a.n_qb = (max_q + bm - 1) / bm;
   a.xcd_remap = (rows % 8 == 0) ? 1 : 0;
   const hipError_t e = attnfwd::launch_attention_fp8(a, d, varlen, vs, bm, stream);

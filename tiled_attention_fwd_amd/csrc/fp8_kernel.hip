@@ -48,10 +48,12 @@ struct F8Tile {
   static constexpr int NI = TK / R;     // DMA instructions per TK-row tile
   static constexpr int BYTES = TK * D;
   static __device__ __forceinline__ int swz_k(int r) {
-    return D == 128 ? ((r >> 1) & 7) : (D == 64 ? ((r >> 2) & 3) : ((r ^ (r >> 3)) & 1));
+    return D == 256 ? (r & 15)
+                    : (D == 128 ? ((r >> 1) & 7) : (D == 64 ? ((r >> 2) & 3) : ((r ^ (r >> 3)) & 1)));
   }
   static __device__ __forceinline__ int swz_v(int r) {
-    return D == 128 ? (r & 7) : (D == 64 ? (((r >> 2) & 1) << 1) : ((r ^ (r >> 1)) & 1));
+    return D == 256 ? ((r & 7) << 1)
+                    : (D == 128 ? (r & 7) : (D == 64 ? (((r >> 2) & 1) << 1) : ((r ^ (r >> 1)) & 1)));
   }
 };
 
@@ -65,8 +67,9 @@ __device__ __forceinline__ int pack_fp8x4(float a, float b, float c, float d) {
 
 // WAVES x 32 queries per workgroup, TK keys per tile (64 or 128: one barrier,
 // one row-maximum pass and one DMA wait per tile).
+// head_dim 256 (4 waves, 64-key tiles) needs ~270 registers: one wave per SIMD.
 template <int D, bool VARLEN, int WAVES, int TK>
-__global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_fp8_kernel(const AttnArgs a, float o_mul) {
+__global__ __launch_bounds__(WAVES * 64, D == 256 ? 1 : 2) void attn_fwd_fp8_kernel(const AttnArgs a, float o_mul) {
   using T = F8Tile<D, TK>;
   constexpr int BM = WAVES * 32;
   // fp8 MFMAs per 32x32 score block (64 dims each).  At head_dim 32 the one
@@ -347,6 +350,13 @@ hipError_t launch_attention_fp8(const AttnArgs& a, int head_dim, bool varlen, fl
       break;
     case 128:
       if (varlen) { ATTN_FP8_LAUNCH(128, true) } else { ATTN_FP8_LAUNCH(128, false) }
+      break;
+    case 256:  // 128-query blocks only
+      if (wide) return hipErrorInvalidValue;
+      if (varlen)
+        hipLaunchKernelGGL((attn_fwd_fp8_kernel<256, true, 4, 64>), g, b, 0, stream, a, o_mul);
+      else
+        hipLaunchKernelGGL((attn_fwd_fp8_kernel<256, false, 4, 64>), g, b, 0, stream, a, o_mul);
       break;
     default:
       return hipErrorInvalidValue;
