@@ -357,7 +357,7 @@ attn_status_t attn_fwd_padded(const void* q, const void* k, const void* v,
  *          attn_fwd_paged_workspace_bytes(...) bytes: lets long key ranges be
  *          split over several workgroups (one more launch merges them).  Too
  *          small or NULL: no split.
- * head_dim 32, 64 or 128; page_size a positive multiple of 16; one page of one
+ * head_dim 32, 64, 128 or 256; page_size a positive multiple of 16; one page of one
  * tensor (page_size * num_heads_k * head_dim * 2 bytes) under 4 GiB.
  * GQA: the query heads of one KV head are processed together, so each K/V
  * byte is read once per (sequence, KV head).  One or two launches on `stream`.
@@ -412,13 +412,14 @@ attn_status_t attn_fwd_paged_fp8kv(const void* q, const void* k_cache, const voi
  * (the array's copy on that device is used).
  * Limit: a shape whose split needs more than ATTN_NOALLOC_SCRATCH_BYTES (only
  * possible under the ATTN_PAGED_CHUNK_TILES test override; every default plan
- * needs at most 33.8 MB) returns ATTN_ERR_SCRATCH before anything is launched.
+ * needs at most 67.3 MB at head_dim 256, 33.8 MB at 128) returns
+ * ATTN_ERR_SCRATCH before anything is launched.
  * Every call on one GPU shares that GPU's array, which keeps the last call's
  * contents (each call writes every slot it reads, so nothing needs clearing):
  * calls that overlap in time on one GPU (different streams, or host threads)
  * race and give wrong results; serialise them.
  */
-#define ATTN_NOALLOC_SCRATCH_BYTES (40ll << 20)
+#define ATTN_NOALLOC_SCRATCH_BYTES (68ll << 20)
 attn_status_t attn_fwd_paged_noalloc(const void* q, const void* k_cache, const void* v_cache,
                                      const int32_t* cu_seqlens_q, const int32_t* seqlens_k,
                                      const int32_t* block_table, int32_t num_seqs,

@@ -226,7 +226,7 @@ def test_paged_fp8_and_mask_argument_checks(lib):
         return f(P, P, P, P, P, P, 2, 2, 8, a["ps"], a["maxp"], a["hq"], a["hkv"], a["d"], a["mq"],
                  a["mk"], 0.125, 1, a["out"], None, a["ws"], a["wsb"], None)
     assert paged(ps=8) == UNSUP and paged(ps=24) == UNSUP      # page size: a multiple of 16
-    assert paged(d=48) == UNSUP and paged(d=256) == UNSUP
+    assert paged(d=48) == UNSUP and paged(d=96) == UNSUP
     assert paged(mk=33) == SHAPE                                # > max_pages * page_size
     assert paged(mq=0) == SHAPE
     assert paged(hq=6, hkv=4) == SHAPE
@@ -260,14 +260,15 @@ def test_paged_fp8_and_mask_argument_checks(lib):
 
 def test_paged_noalloc_refuses_a_split_beyond_its_scratch_without_launching(lib, monkeypatch):
     """The no-allocation paged call checks its static scratch limit on the host:
-    a forced one-tile-per-part split of 8000 keys needs ~63 MiB, above the
-    40 MiB array, and is refused before anything touches a device."""
+    a forced one-tile-per-part split of 8000 keys over 8 KV heads needs ~126
+    MiB, above the 68 MiB array, and is refused before anything touches a
+    device."""
     P = ctypes.c_void_p(16)
     monkeypatch.setenv("ATTN_PAGED_CHUNK_TILES", "1")
-    assert lib.attn_fwd_paged_workspace_bytes(4, 1, 8000, 16, 4, 128) > (40 << 20)
+    assert lib.attn_fwd_paged_workspace_bytes(4, 1, 8000, 32, 8, 128) > (68 << 20)
     # q, k, v, cu_q, seqlens_k, table, nseq, tq, num_pages, page_size, max_pages, hq, hkv, d,
     # max_q, max_k, scale, causal, out, lse, stream
-    st = lib.attn_fwd_paged_noalloc(P, P, P, P, P, P, 4, 4, 200, 64, 125, 16, 4, 128, 1, 8000,
+    st = lib.attn_fwd_paged_noalloc(P, P, P, P, P, P, 4, 4, 200, 64, 125, 32, 8, 128, 1, 8000,
                                     0.125, 1, P, None, None)
     assert st == 6
     assert b"scratch" in lib.attn_status_str(6)

@@ -23,14 +23,14 @@ def key_of_row(i):
 
 
 def swz_k(d, row):
-    return {128: row & 15, 64: (row >> 1) & 7, 32: (row >> 2) & 3}[d]
+    return {256: row & 15, 128: row & 15, 64: (row >> 1) & 7, 32: (row >> 2) & 3}[d]
 
 
 def swz_v(d, row):
-    return {128: (row & 3) << 2, 64: ((row >> 1) & 1) << 2, 32: 0}[d]
+    return {256: (row & 3) << 2, 128: (row & 3) << 2, 64: ((row >> 1) & 1) << 2, 32: 0}[d]
 
 
-@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("d", [32, 64, 128, 256])
 def test_row_major_swizzled_tiles(d):
     cpr = d // 8
     r = 64 // cpr

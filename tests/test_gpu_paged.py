@@ -53,7 +53,7 @@ def check(w, **kw):
     return check_o(o, o_ref), check_lse(lse, lse_ref)
 
 
-@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("d", [32, 64, 128, 256])
 @pytest.mark.parametrize("page", [16, 48, 64])
 def test_decode_gqa_ragged(d, page):
     w = gen.make_paged(f"dec{d}_{page}", 1000 + d + page, [1] * 6, [1, 17, 300, 1000, 64, 33],
@@ -70,7 +70,7 @@ def test_speculative_decode_causal(group):
 
 
 @pytest.mark.parametrize("causal", [True, False])
-@pytest.mark.parametrize("d", [32, 64])
+@pytest.mark.parametrize("d", [32, 64, 256])
 def test_chunked_prefill_several_row_blocks(causal, d):
     w = gen.make_paged("chunk", 1200 + d, [70, 5, 0, 33], [200, 40, 9, 33], 8, 2, d, 16, causal,
                        fill=float("nan"))
@@ -90,7 +90,7 @@ def test_lq_gt_lk_and_empty():
 
 
 @pytest.mark.parametrize("chunk", ["1", "3"])
-@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("d", [32, 64, 128, 256])
 def test_forced_split_matches_oracle(monkeypatch, chunk, d):
     monkeypatch.setenv("ATTN_PAGED_CHUNK_TILES", chunk)
     w = gen.make_paged(f"split{chunk}", 1400 + d, [1, 3, 2, 1], [500, 70, 0, 31], 8, 2, d, 32,
@@ -162,7 +162,7 @@ def test_full_size_decode_batch_sampled():
         check_lse(lse[:, s:s + 1], lse_ref, f"seq {s}")
 
 
-@pytest.mark.parametrize("d,lk", [(128, 6000), (64, 9500), (32, 7000)])
+@pytest.mark.parametrize("d,lk", [(128, 6000), (64, 9500), (32, 7000), (256, 3000)])
 def test_long_sequence_without_split(d, lk):
     # no workspace: one workgroup walks the whole key range, more than 32 tiles
     # per wave (the page numbers are fetched in batches of 32 tiles)

@@ -60,7 +60,7 @@ def test_noalloc_two_calls_second_smaller():
 def test_noalloc_refuses_a_split_beyond_its_scratch():
     import torch
     t = api()
-    w = gen.make_paged("na3", 8103, [1] * 4, [8000, 100, 3000, 50], 16, 4, 128, 64, True)
+    w = gen.make_paged("na3", 8103, [1] * 4, [8000, 100, 3000, 50], 32, 8, 128, 64, True)
     out = torch.zeros((w.q.shape[0], w.hq, w.d), dtype=torch.float32, device="cuda")
     args = (dev_bf16(w.q), dev_bf16(w.k_cache), dev_bf16(w.v_cache), dev_i32(w.cu_seqlens_q),
             dev_i32(w.seqlens_k), dev_i32(w.block_table), w.max_seqlen_q, w.max_seqlen_k)
@@ -68,7 +68,7 @@ def test_noalloc_refuses_a_split_beyond_its_scratch():
     try:
         nseq = len(w.lengths_q)
         assert t.attn_fwd_paged_workspace_bytes(nseq, 1, w.max_seqlen_k, w.hq, w.hkv,
-                                                w.d) > (40 << 20)
+                                                w.d) > (68 << 20)
         with pytest.raises(t.AttnError, match="SCRATCH"):
             t.attn_fwd_paged_noalloc(*args, out=out, scale=float(w.scale), causal=True)
     finally:

@@ -431,8 +431,8 @@ attn_status_t paged_impl(const void* q, const void* k_cache, const void* v_cache
     return ATTN_ERR_SHAPE;
   attn_status_t st = check_common(num_heads_q, num_heads_k, head_dim, scale);
   if (st != ATTN_OK) return st;
-  if (head_dim != 32 && head_dim != 64 && head_dim != 128) return ATTN_ERR_UNSUPPORTED;
-  if (kv_fp8 && head_dim == 32) return ATTN_ERR_UNSUPPORTED;  // E4M3 tiles: head_dim 64 and 128
+  if (!head_dim_ok(head_dim)) return ATTN_ERR_UNSUPPORTED;
+  if (kv_fp8 && head_dim != 64 && head_dim != 128) return ATTN_ERR_UNSUPPORTED;  // E4M3 tiles
   if (page_size < 16 || page_size % 16 != 0) return ATTN_ERR_UNSUPPORTED;
   if (kv_fp8)
     for (float f : {k_scale, v_scale})
@@ -873,8 +873,7 @@ int64_t attn_fwd_paged_workspace_bytes(int32_t num_seqs, int32_t max_seqlen_q,
                                        int32_t max_seqlen_k, int32_t num_heads_q,
                                        int32_t num_heads_k, int32_t head_dim) {
   if (num_seqs <= 0 || max_seqlen_q <= 0 || max_seqlen_k <= 0 || num_heads_q <= 0 ||
-      num_heads_k <= 0 || num_heads_q % num_heads_k != 0 ||
-      (head_dim != 32 && head_dim != 64 && head_dim != 128))
+      num_heads_k <= 0 || num_heads_q % num_heads_k != 0 || !head_dim_ok(head_dim))
     return 0;
   const PagedPlan p = plan_paged(num_seqs, max_seqlen_q, max_seqlen_k, num_heads_q / num_heads_k,
                                  num_heads_k);

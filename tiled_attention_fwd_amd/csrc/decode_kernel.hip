@@ -53,12 +53,12 @@ struct RowTile {
   static constexpr int R = 64 / CPR;       // rows per DMA instruction
   static constexpr int PITCH = 2 * D;      // bytes per row
   static constexpr int BYTES = kTileKeys * PITCH;
-  static_assert(D == 32 || D == 64 || D == 128, "tile layout defined for head_dim 32, 64 and 128");
+  static_assert(D == 32 || D == 64 || D == 128 || D == 256, "tile layout defined for head_dim 32..256");
   static __device__ __forceinline__ int swz_k(int row) {
-    return D == 128 ? (row & 15) : (D == 64 ? ((row >> 1) & 7) : ((row >> 2) & 3));
+    return D >= 128 ? (row & 15) : (D == 64 ? ((row >> 1) & 7) : ((row >> 2) & 3));
   }
   static __device__ __forceinline__ int swz_v(int row) {
-    return D == 128 ? ((row & 3) << 2) : (D == 64 ? (((row >> 1) & 1) << 2) : 0);
+    return D >= 128 ? ((row & 3) << 2) : (D == 64 ? (((row >> 1) & 1) << 2) : 0);
   }
 };
 
@@ -239,6 +239,21 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NI) : "memory");
 }
 
+// Waits until a wave's oldest tile has landed while `after` later tiles (each
+// 2 NI loads: K and V) may stay in flight; only the counts a stage depth can
+// reach are instantiated.
+template <int NI, int NBUF>
+__device__ __forceinline__ void wait_tile(int after) {
+  if constexpr (NBUF >= 4) {
+    if (after >= 3) { wait_vm<6 * NI>(); return; }
+  }
+  if constexpr (NBUF >= 3) {
+    if (after == 2) { wait_vm<4 * NI>(); return; }
+  }
+  if (after >= 1) { wait_vm<2 * NI>(); return; }
+  wait_vm<0>();
+}
+
 template <int D, int WAVES, int NBUF, int ES>
 __global__ __launch_bounds__(WAVES * 64, 1) void attn_decode_kernel(const DecodeArgs a) {
   constexpr int NDS = D / 16, NDB = D / 32;
@@ -249,7 +264,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void attn_decode_kernel(const Decode
   constexpr int MERGE_LDS = WAVES * (32 * D + 64) * 4;
   constexpr int LDS = WAVES * WAVE_LDS > MERGE_LDS ? WAVES * WAVE_LDS : MERGE_LDS;
   static_assert(NBUF >= 2 && NBUF <= 4, "stage count");
-  static_assert(6 * NI <= 63, "vmcnt range");
+  static_assert(2 * (NBUF - 1) * NI <= 63, "vmcnt range");
   __shared__ __attribute__((aligned(16))) unsigned char lds[LDS];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -346,10 +361,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void attn_decode_kernel(const Decode
     const int buf = j % NBUF;
     // tiles issued after tile j that may stay in flight
     const int after = min(NBUF - 1, n_mine - 1 - j);
-    if (after >= 3) wait_vm<6 * NI>();
-    else if (after == 2) wait_vm<4 * NI>();
-    else if (after == 1) wait_vm<2 * NI>();
-    else wait_vm<0>();
+    wait_tile<NI, NBUF>(after);
     const unsigned char* kt = my_tiles + buf * 2 * TB;
     const unsigned char* vt = kt + TB;
     bf16x8 kfr[NDS], vfr[2][NDB];
@@ -553,7 +565,13 @@ hipError_t launch_d(const DecodeArgs& a, int variant, hipStream_t stream) {
   // Defaults (variant < 0) from measured sweeps: more waves beat more stages
   // for bf16 caches (d=128 decode: 4x2 3.8, 3x3 3.6, 5x2 4.5 TB/s; d=64: 4x4
   // 3.4, 8x2 4.5, 5x4 4.2 TB/s).  E4M3 caches halve the stage size.
-  if constexpr (D == 32) {
+  if constexpr (D == 256) {
+    // bf16 caches only; a 32-key stage of K and V is 32 KiB, so two waves of
+    // two stages fill the LDS (each wave at one per SIMD can hold a landed
+    // tile's fragments in registers)
+    if (a.kv_fp8) return hipErrorInvalidValue;
+    launch_v<D, 2, 2, 2>(a, grid, stream);
+  } else if constexpr (D == 32) {
     // bf16 caches only (E4M3 tiles are laid out for head_dim 64 and 128)
     if (a.kv_fp8) return hipErrorInvalidValue;
     if (variant == 0) launch_v<D, 4, 4, 2>(a, grid, stream);
@@ -593,6 +611,7 @@ hipError_t launch_decode(const DecodeArgs& a, int head_dim, int variant, hipStre
     case 32: return launch_d<32>(a, variant, stream);
     case 64: return launch_d<64>(a, variant, stream);
     case 128: return launch_d<128>(a, variant, stream);
+    case 256: return launch_d<256>(a, variant, stream);
     default: return hipErrorInvalidValue;
   }
 }
