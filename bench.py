@@ -154,9 +154,28 @@ def spin(torch):
         x @ x
 
 
+class CacheFlush:
+    """Cold-cache set-up: one pass over a 1 GiB buffer (more than MALL + L2)
+    evicts every input of the next call.  The pass reads, so the caches are
+    left holding clean lines only.  A writing pass would leave up to MALL + L2
+    of dirty lines, and their write-back to HBM would run inside the next
+    timed call and compete with it for bandwidth; `write()` is that pass,
+    kept for comparison."""
+
+    def __init__(self, torch):
+        self.buf = torch.zeros(1 << 28, dtype=torch.float32, device="cuda")
+
+    def __call__(self):
+        self.buf.sum()
+
+    def write(self):
+        self.buf.zero_()
+
+
 def time_calls(torch, fn, iters, warmup, flush=None):
     """Per-call device time (us) with events.  Before each call either `flush`
-    (a 1 GiB write that evicts L2 and MALL: cold) or a spin kernel (warm) runs."""
+    (a pass over 1 GiB that evicts L2 and MALL: cold) or a spin kernel (warm)
+    runs."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -322,7 +341,10 @@ def run_paged(torch, t, names, flush):
         cold = time_calls(torch, fn, iters, 1, flush=flush)
         med = statistics.median(cold)
         gbs = by / (med * 1e-6) / 1e9
-        rows.append({"workload": name, "us_median_cold": round(med, 1), "mb": round(by / 1e6, 1),
+        # the same calls after a writing flush (its dirty lines drain during the call)
+        wmed = statistics.median(time_calls(torch, fn, iters, 0, flush=flush.write))
+        rows.append({"workload": name, "us_median_cold": round(med, 1),
+                     "us_median_after_write_flush": round(wmed, 1), "mb": round(by / 1e6, 1),
                      "tokens_per_s": round(len(w.q) / (med * 1e-6), 1),
                      "gbs": round(gbs, 1), "pct_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 1),
                      "split_workspace_mb": round((ws.numel() if ws is not None else 0) / 1e6, 2)})
@@ -493,21 +515,21 @@ def main():
     print(f"[bench] device {torch.cuda.get_device_name(0)}", file=sys.stderr, flush=True)
 
     if args.only_configs:
-        flush_buf = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        flush = CacheFlush(torch)
         cfg_names = [] if args.configs == "none" else (
             list(gen.WORKLOADS) if args.configs == "all" else args.configs.split(","))
-        for row in run_configs(torch, t, cfg_names, lambda: flush_buf.zero_()):
+        for row in run_configs(torch, t, cfg_names, flush):
             print(json.dumps(row), flush=True)
         if args.bwd_configs != "none":
-            for row in run_backward(torch, t, args.bwd_configs.split(","), lambda: flush_buf.zero_()):
+            for row in run_backward(torch, t, args.bwd_configs.split(","), flush):
                 print(json.dumps({"backward": row}), flush=True)
         if args.paged_configs != "none":
             pn = list(gen.PAGED_WORKLOADS) if args.paged_configs == "all" else args.paged_configs.split(",")
-            for row in run_paged(torch, t, pn, lambda: flush_buf.zero_()):
+            for row in run_paged(torch, t, pn, flush):
                 print(json.dumps({"paged": row}), flush=True)
         if args.fp8_configs != "none":
             fn_ = list(gen.FP8_WORKLOADS) if args.fp8_configs == "all" else args.fp8_configs.split(",")
-            for row in run_fp8(torch, t, fn_, lambda: flush_buf.zero_()):
+            for row in run_fp8(torch, t, fn_, flush):
                 print(json.dumps({"fp8": row}), flush=True)
         return
 
@@ -557,22 +579,28 @@ def main():
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     value = flops_step / (ms_per_step * 1e-3) / 1e12
 
-    # The same replays cold: before each one a 1 GiB write evicts L2 and MALL
-    # (outside the span); HIP events on the replay stream bracket the step.
-    flush_buf = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    # The same replays cold: before each one a pass over 1 GiB evicts L2 and
+    # MALL (outside the span); HIP events on the replay stream bracket the step.
+    # Also after a writing pass, whose dirty lines drain during the step.
+    flush = CacheFlush(torch)
     s_rep = torch.cuda.current_stream()
-    cold_us = []
-    for _ in range(max(5, min(args.steps, 50))):
-        flush_buf.zero_()
-        ea = torch.cuda.Event(enable_timing=True)
-        eb = torch.cuda.Event(enable_timing=True)
-        ea.record(s_rep)
-        graph.replay()
-        eb.record(s_rep)
-        eb.synchronize()
-        cold_us.append(ea.elapsed_time(eb) * 1e3)
-    del flush_buf
+
+    def replay_after(fl):
+        out = []
+        for _ in range(max(5, min(args.steps, 50))):
+            fl()
+            ea = torch.cuda.Event(enable_timing=True)
+            eb = torch.cuda.Event(enable_timing=True)
+            ea.record(s_rep)
+            graph.replay()
+            eb.record(s_rep)
+            eb.synchronize()
+            out.append(ea.elapsed_time(eb) * 1e3)
+        return out
+
+    cold_us = replay_after(flush)
     step_cold_us = statistics.median(cold_us)
+    step_wflush_us = statistics.median(replay_after(flush.write))
 
     # The fused padded path (attn_fwd_padded: zero fill + attention reading and
     # writing the padded rows) on the same inputs, captured and replayed alike.
@@ -695,32 +723,24 @@ def main():
 
     cfg_rows = []
     if args.configs != "none":
-        flush_buf = torch.empty(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB > MALL + L2
-        flush = lambda: flush_buf.zero_()
         cfg_names = list(gen.WORKLOADS) if args.configs == "all" else args.configs.split(",")
         print(f"[bench] timing {len(cfg_names)} workloads", file=sys.stderr, flush=True)
         cfg_rows = run_configs(torch, t, cfg_names, flush, 0.0 if args.no_cpu else 2.5)
-        del flush_buf
     bwd_rows = []
     if args.bwd_configs != "none":
-        flush_buf = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
         print("[bench] timing the backward", file=sys.stderr, flush=True)
-        bwd_rows = run_backward(torch, t, args.bwd_configs.split(","), lambda: flush_buf.zero_())
-        del flush_buf
+        bwd_rows = run_backward(torch, t, args.bwd_configs.split(","), flush)
     paged_rows = []
     if args.paged_configs != "none":
-        flush_buf = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
         print("[bench] timing the paged KV-cache workloads", file=sys.stderr, flush=True)
         pn = list(gen.PAGED_WORKLOADS) if args.paged_configs == "all" else args.paged_configs.split(",")
-        paged_rows = run_paged(torch, t, pn, lambda: flush_buf.zero_())
-        del flush_buf
+        paged_rows = run_paged(torch, t, pn, flush)
     fp8_rows = []
     if args.fp8_configs != "none":
-        flush_buf = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
         print("[bench] timing the fp8 workloads", file=sys.stderr, flush=True)
         fn_ = list(gen.FP8_WORKLOADS) if args.fp8_configs == "all" else args.fp8_configs.split(",")
-        fp8_rows = run_fp8(torch, t, fn_, lambda: flush_buf.zero_())
-        del flush_buf
+        fp8_rows = run_fp8(torch, t, fn_, flush)
+    del flush
 
     cpu = None
     if not args.no_cpu:
@@ -738,9 +758,11 @@ def main():
                    "global_batch": 2, "seq_len": 4096, "parallelism": "none (1 GPU)",
                    "per_launch_us": {f"{names[pi]}:{k}": round(v, 2) for (pi, k), v in avg_us.items()},
                    "pct_bf16_peak_step": round(100 * value / PEAK_BF16_TFLOPS, 2),
-                   "step_cold": {"timing": "one graph replay per sample, L2 and MALL flushed "
-                                           "(1 GiB write) before each, HIP events around it",
+                   "step_cold": {"timing": "one graph replay per sample, L2 and MALL evicted "
+                                           "before each by a read pass over 1 GiB, HIP events "
+                                           "around it",
                                  "us_median": round(step_cold_us, 2),
+                                 "us_median_after_write_flush": round(step_wflush_us, 2),
                                  "us_p10": round(sorted(cold_us)[len(cold_us) // 10], 2),
                                  "us_p90": round(sorted(cold_us)[(len(cold_us) * 9) // 10], 2),
                                  "tflops": round(flops_step / (step_cold_us * 1e-6) / 1e12, 2)},
