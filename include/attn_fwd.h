@@ -419,7 +419,7 @@ attn_status_t attn_fwd_paged_fp8kv(const void* q, const void* k_cache, const voi
  * calls that overlap in time on one GPU (different streams, or host threads)
  * race and give wrong results; serialise them.
  */
-#define ATTN_NOALLOC_SCRATCH_BYTES (68ll << 20)
+#define ATTN_NOALLOC_SCRATCH_BYTES (17ll << 20)
 attn_status_t attn_fwd_paged_noalloc(const void* q, const void* k_cache, const void* v_cache,
                                      const int32_t* cu_seqlens_q, const int32_t* seqlens_k,
                                      const int32_t* block_table, int32_t num_seqs,

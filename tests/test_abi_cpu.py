@@ -239,7 +239,8 @@ def test_paged_fp8_and_mask_argument_checks(lib):
     base32 = base[:13] + (32,) + base[14:]                       # E4M3 tiles: head_dim 64 and 128
     assert g(*base32, 1.0, 1.0, 1, P, None, None, 0, None) == UNSUP
     ws = lib.attn_fwd_paged_workspace_bytes
-    assert ws(32, 1, 8192, 64, 8, 128) > 0                      # few workgroups: splits
+    assert ws(8, 1, 8192, 64, 8, 128) > 0                       # 64 workgroups: split in 4
+    assert ws(32, 1, 8192, 64, 8, 128) == 0                     # 256 (one per CU): no split
     assert ws(32, 1, 8192, 64, 8, 96) == 0 and ws(0, 1, 8, 8, 8, 128) == 0
     h = lib.attn_fwd_fp8_varlen
     # q, k, v, cu_q, cu_k, nseq, tq, tk, hq, hkv, d, max, scale, qs, ks, vs, causal, out, lse, s
@@ -261,11 +262,11 @@ def test_paged_fp8_and_mask_argument_checks(lib):
 def test_paged_noalloc_refuses_a_split_beyond_its_scratch_without_launching(lib, monkeypatch):
     """The no-allocation paged call checks its static scratch limit on the host:
     a forced one-tile-per-part split of 8000 keys over 8 KV heads needs ~126
-    MiB, above the 68 MiB array, and is refused before anything touches a
+    MiB, above the 17 MiB array, and is refused before anything touches a
     device."""
     P = ctypes.c_void_p(16)
     monkeypatch.setenv("ATTN_PAGED_CHUNK_TILES", "1")
-    assert lib.attn_fwd_paged_workspace_bytes(4, 1, 8000, 32, 8, 128) > (68 << 20)
+    assert lib.attn_fwd_paged_workspace_bytes(4, 1, 8000, 32, 8, 128) > (17 << 20)
     # q, k, v, cu_q, seqlens_k, table, nseq, tq, num_pages, page_size, max_pages, hq, hkv, d,
     # max_q, max_k, scale, causal, out, lse, stream
     st = lib.attn_fwd_paged_noalloc(P, P, P, P, P, P, 4, 4, 200, 64, 125, 32, 8, 128, 1, 8000,

@@ -49,7 +49,7 @@ def _case(w):
 
 def test_noalloc_two_calls_second_smaller():
     assert "ATTN_PAGED_CHUNK_TILES" not in os.environ
-    big = gen.make_paged("na1", 8101, [1] * 32, list(range(2000, 2000 + 32 * 61, 61)), 64, 8, 128,
+    big = gen.make_paged("na1", 8101, [1] * 16, list(range(2000, 2000 + 16 * 61, 61)), 64, 8, 128,
                          64, True, fill=float("nan"))
     small = gen.make_paged("na2", 8102, [2, 1, 3, 1], [900, 77, 1500, 33], 16, 4, 128, 32, True,
                            fill=float("nan"))
@@ -68,7 +68,7 @@ def test_noalloc_refuses_a_split_beyond_its_scratch():
     try:
         nseq = len(w.lengths_q)
         assert t.attn_fwd_paged_workspace_bytes(nseq, 1, w.max_seqlen_k, w.hq, w.hkv,
-                                                w.d) > (68 << 20)
+                                                w.d) > (17 << 20)
         with pytest.raises(t.AttnError, match="SCRATCH"):
             t.attn_fwd_paged_noalloc(*args, out=out, scale=float(w.scale), causal=True)
     finally:

@@ -270,6 +270,13 @@ int paged_order() {
   return (s != nullptr && s[0] == '0' && s[1] == '\0') ? 0 : 1;
 }
 
+constexpr int64_t kPagedTargetWorkgroups = 256;
+// A split plan has fewer than 2 * kPagedTargetWorkgroups slots of 32 rows x
+// (head_dim + 1) floats; the no-allocation entry point's static array holds
+// any of them at the largest head_dim.
+static_assert(2 * kPagedTargetWorkgroups * 32 * (256 + 1) * 4 <= ATTN_NOALLOC_SCRATCH_BYTES,
+              "every default paged plan must fit the no-allocation scratch");
+
 struct PagedPlan {
   int n_rb = 0;
   int n_split = 1;
@@ -278,8 +285,13 @@ struct PagedPlan {
 
 // Row blocks of 32 (query, head-of-group) pairs, and the key-range split: the
 // launch has nseq * hkv * n_rb workgroups before splitting; parts are added
-// until about 1024 workgroups (4 per CU) exist, keeping at least 8 tiles
-// (2 per wave) in a part.
+// until about 256 workgroups (one per CU: each fills the CU's LDS) exist,
+// keeping at least 8 tiles (2 per wave) in a part.  Fewer, longer parts
+// stream faster than more rounds of short ones: each workgroup pays its own
+// start (Q, page table, first tiles in flight) and merge, and the last round
+// ends ragged (measured with the caches evicted: 32 sequences of 4-8k keys
+// 178 -> 166 us, 8 x 32k keys 216 -> 197 us, E4M3 caches -20 %, against
+// about 1024 workgroups).
 PagedPlan plan_paged(int nseq, int max_q, int max_k, int group, int hkv) {
   PagedPlan p;
   p.n_rb = (int)(((int64_t)max_q * group + 31) / 32);
@@ -291,7 +303,7 @@ PagedPlan plan_paged(int nseq, int max_q, int max_k, int group, int hkv) {
   if (forced > 0) {
     parts = (n_kt + forced - 1) / forced;
   } else {
-    const int64_t want = (1024 + base - 1) / base;
+    const int64_t want = (kPagedTargetWorkgroups + base - 1) / base;
     parts = (int)std::min<int64_t>(want, (n_kt + 7) / 8);
     parts = std::min(parts, 64);
   }

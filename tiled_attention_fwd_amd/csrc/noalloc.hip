@@ -18,9 +18,10 @@
 namespace attnfwd {
 
 // Every default plan of the paged call fits: parts are added only while the
-// launch has fewer than 1024 workgroups, so a plan holds fewer than 2047
+// launch has fewer than 256 workgroups, so a plan holds at most 510
 // (sequence, KV head, row block, part) slots of 32 rows x (head_dim + 1)
-// floats, 67.3 MB at head_dim 256 (33.8 MB at 128).
+// floats, 16.8 MB at head_dim 256 (8.4 MB at 128); the planner checks this
+// bound at compile time.
 constexpr int64_t kScratchBytes = ATTN_NOALLOC_SCRATCH_BYTES;
 
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];
