@@ -272,7 +272,7 @@ def run_backward(torch, t, names, flush):
     rows = []
     for name in names:
         w = gen.build_workload(name)
-        if w.d not in (32, 64, 128) or w.kind == "padded":
+        if w.d not in (32, 64, 128, 256) or w.kind == "padded":
             continue
         dev = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to("cuda").view(torch.bfloat16)
         q, k, v = dev(w.q), dev(w.k), dev(w.v)
@@ -304,7 +304,10 @@ def run_backward(torch, t, names, flush):
         tf = fl / (med * 1e-6) / 1e12
         rows.append({"workload": name, "us_median_cold": round(med, 1), "gflop": round(fl / 1e9, 2),
                      "tflops": round(tf, 1), "pct_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 1),
-                     "executed_tflops": round(tf * 7 / 5, 1)})
+                     # products executed: S and dP in both the dQ and dK/dV passes (7 of
+                     # the 5 the gradient needs); at head_dim 256 S a third time (dV and
+                     # dK run as separate passes)
+                     "executed_tflops": round(tf * (8 if w.d == 256 else 7) / 5, 1)})
         del q, k, v, o, lse, do, dq, dk, dv, ws
         torch.cuda.empty_cache()
     return rows
@@ -489,7 +492,7 @@ def main():
     ap.add_argument("--configs", default="all",
                     help="comma list of extra workloads to time per call, 'all' or 'none'")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
-    ap.add_argument("--bwd-configs", default="varlen_1x8192,hdim_sweep_d128,hdim_sweep_d64,hdim_sweep_d32",
+    ap.add_argument("--bwd-configs", default="varlen_1x8192,hdim_sweep_d128,hdim_sweep_d64,hdim_sweep_d32,hdim_sweep_d256",
                     help="comma list of workloads whose backward is timed, or 'none'")
     ap.add_argument("--paged-configs", default="all",
                     help="comma list of paged KV-cache workloads, 'all' or 'none'")

@@ -504,10 +504,11 @@ attn_status_t attn_fwd_fp8_dense(const void* q, const void* k, const void* v, in
  * workspace: device memory of at least attn_bwd_workspace_bytes(total_q,
  *      num_heads_q) bytes, 16-byte aligned, owned by the caller; it holds
  *      rowsum(dO * out) between the launches and may be reused afterwards.
- * head_dim must be 32, 64 or 128 (else ATTN_ERR_UNSUPPORTED).  Every pointer
- * must be non-NULL and 16-byte aligned (lse and cu_seqlens 4-byte aligned).
- * Three launches on `stream`, no atomics: rowsum(dO * out), then dq, then
- * dk and dv.  Results are deterministic.
+ * head_dim must be 32, 64, 128 or 256 (else ATTN_ERR_UNSUPPORTED).  Every
+ * pointer must be non-NULL and 16-byte aligned (lse and cu_seqlens 4-byte
+ * aligned).  Three launches on `stream`, no atomics: rowsum(dO * out), then
+ * dq, then dk and dv (at head_dim 256, dv and dk in two launches).  Results
+ * are deterministic.
  */
 attn_status_t attn_bwd_varlen(const void* q, const void* k, const void* v, const float* out,
                               const void* dout, const float* lse, const int32_t* cu_seqlens_q,

@@ -196,7 +196,7 @@ def test_backward_argument_checks(lib):
         a = ok(**kw)
         return f(P, P, P, P, P, P, P, P, 1, 8, 8, a["hq"], a["hkv"], a["d"], a["mq"], 8,
                  a["scale"], 1, a["dq"], P, P, a["ws"], a["wsb"], None)
-    assert call(d=256) == UNSUP and call(d=96) == UNSUP and call(d=16) == UNSUP
+    assert call(d=48) == UNSUP and call(d=96) == UNSUP and call(d=16) == UNSUP
     assert call(scale=float("inf")) == UNSUP
     assert call(scale=float("nan")) == UNSUP
     assert call(hq=3) == SHAPE                       # hq % hkv
@@ -209,7 +209,7 @@ def test_backward_argument_checks(lib):
     assert lib.attn_bwd_workspace_bytes(8, 2) == 64
     assert lib.attn_bwd_workspace_bytes(0, 2) == 0
     g = lib.attn_bwd_dense
-    assert g(P, P, P, P, P, P, 1, 8, 8, 2, 2, 256, 0.125, 1, P, P, P, P, 1 << 20, None) == UNSUP
+    assert g(P, P, P, P, P, P, 1, 8, 8, 2, 2, 96, 0.125, 1, P, P, P, P, 1 << 20, None) == UNSUP
     assert g(P, P, P, P, P, P, 1, 8, 8, 2, 2, 64, 0.125, 1, P, P, P, P, 63, None) == SHAPE
     assert g(None, None, None, None, None, None, 0, 8, 8, 2, 2, 64, 0.125, 1, None, None, None,
              None, 0, None) == OK

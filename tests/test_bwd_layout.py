@@ -16,7 +16,14 @@ This model restates those formulas, checks that every read lands on the row
 and dims it must, stays inside the tile, and (for 64 banks of 4 bytes, 128-byte
 phases for 16-lane groups of 8-byte reads and 8-lane groups of 16-byte reads,
 256-byte phases for twice as many lanes) that no read has a bank conflict.
+At head_dim 256 an instruction moves 2 rows and no padding or chunk rotation
+of this layout keeps both shapes conflict-free (a host search over paddings of
+1024 + 16k bytes and rotations); 1056-byte steps keep the row fragments (two
+thirds of the bytes read) conflict-free and leave the transposed fragments
+2-way conflicted, which the model pins.
 """
+
+import collections
 
 import pytest
 
@@ -28,13 +35,13 @@ def key_of_row(i):
 def layout(d):
     cpr = d // 8
     r = 64 // cpr
-    g = 1024 + {4: 64, 8: 128, 16: 0}[r]
+    g = 1024 + {2: 32, 4: 64, 8: 128, 16: 0}[r]
     rot = {8: lambda c: 4 * ((c ^ (c >> 1)) & 1), 16: lambda c: 4 * c}.get(r, lambda c: 0)
     at = lambda row, c: (row // r) * g + 16 * (c * r + ((row % r) ^ rot(c)))
     return r, g, rot, at
 
 
-@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("d", [32, 64, 128, 256])
 def test_dma_placement_and_fragment_reads(d):
     r, g, rot, at = layout(d)
     ni = 64 // r
@@ -48,7 +55,8 @@ def test_dma_placement_and_fragment_reads(d):
             slot[q * g + 16 * lane] = ((row & ~31) + key_of_row(row & 31), c)
     assert len(slot) == 64 * (d // 8)
     assert max(slot) + 16 <= tile
-    conflicts = 0
+    conflicts = 0      # row fragments
+    tr_ways = collections.Counter()  # transposed fragments: lanes per bank, worst per group
     for blk in range(2):
         for s in range(d // 16):
             addrs = []
@@ -77,5 +85,10 @@ def test_dma_placement_and_fragment_reads(d):
                         addrs.append(a)
                     for grp, span in ((16, 128), (32, 256)):
                         for st in range(0, 64, grp):
-                            conflicts += len({(a % span) // 8 for a in addrs[st:st + grp]}) != grp
+                            n = collections.Counter((a % span) // 8 for a in addrs[st:st + grp])
+                            tr_ways[max(n.values())] += 1
     assert conflicts == 0
+    if d == 256:
+        assert set(tr_ways) == {2}  # every transposed read 2-way, none worse
+    else:
+        assert set(tr_ways) == {1}

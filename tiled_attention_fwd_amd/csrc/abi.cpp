@@ -792,7 +792,7 @@ attn_status_t attn_bwd_varlen(const void* q, const void* k, const void* v, const
     return ATTN_ERR_SHAPE;
   attn_status_t st = check_common(num_heads_q, num_heads_k, head_dim, scale);
   if (st != ATTN_OK) return st;
-  if (head_dim != 32 && head_dim != 64 && head_dim != 128) return ATTN_ERR_UNSUPPORTED;
+  if (head_dim != 32 && head_dim != 64 && head_dim != 128 && head_dim != 256) return ATTN_ERR_UNSUPPORTED;
   if (workspace_bytes < 0) return ATTN_ERR_SHAPE;
   if (num_seqs == 0 || num_heads_q == 0 || (total_q == 0 && total_k == 0)) return ATTN_OK;
   if ((total_q > 0 && max_seqlen_q == 0) || (total_k > 0 && max_seqlen_k == 0)) return ATTN_ERR_SHAPE;
@@ -842,7 +842,7 @@ attn_status_t attn_bwd_dense(const void* q, const void* k, const void* v, const 
   if (batch < 0 || seqlen_q < 0 || seqlen_k < 0) return ATTN_ERR_SHAPE;
   attn_status_t st = check_common(num_heads_q, num_heads_k, head_dim, scale);
   if (st != ATTN_OK) return st;
-  if (head_dim != 32 && head_dim != 64 && head_dim != 128) return ATTN_ERR_UNSUPPORTED;
+  if (head_dim != 32 && head_dim != 64 && head_dim != 128 && head_dim != 256) return ATTN_ERR_UNSUPPORTED;
   if (workspace_bytes < 0) return ATTN_ERR_SHAPE;
   if (batch == 0 || num_heads_q == 0 || (seqlen_q == 0 && seqlen_k == 0)) return ATTN_OK;
   st = check_bwd_ptrs(q, k, v, out, dout, lse, dq, dk, dv, workspace);

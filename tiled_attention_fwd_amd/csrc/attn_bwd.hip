@@ -123,7 +123,7 @@ __global__ __launch_bounds__(256) void bwd_dvec_kernel(const AttnArgs a, const u
 // dQ: 4 waves x 32 queries; K/V tiles of 64 keys in two LDS buffers.
 // ---------------------------------------------------------------------------
 template <int D, bool VARLEN>
-__global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(const AttnArgs a, const uint16_t* dout,
+__global__ __launch_bounds__(256, D == 256 ? 1 : 2) void attn_bwd_dq_kernel(const AttnArgs a, const uint16_t* dout,
                                                             float* dq) {
   constexpr int BM = 128, BN = 64;
   constexpr int NDS = D / 16, NDB = D / 32, NKB = BN / 32;
@@ -290,7 +290,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(const AttnArgs a, c
 // and Q^T dS).  The split modes hold fewer registers per wave, so more waves
 // share a SIMD, at the price of computing S in both.
 template <int D, bool VARLEN, int MODE>
-__global__ __launch_bounds__(256, MODE == 1 ? 3 : (MODE == 2 ? 2 : (D >= 128 ? 1 : 2)))
+__global__ __launch_bounds__(256, D == 256 ? 1 : (MODE == 1 ? 3 : (MODE == 2 ? 2 : (D >= 128 ? 1 : 2))))
 void attn_bwd_dkdv_kernel(const AttnArgs a, const uint16_t* dout, float* dk, float* dv, int n_kb) {
   constexpr bool DO_DK = MODE != 1, DO_DV = MODE != 2;
   constexpr int BKEYS = 128, BQ = 64;
@@ -531,12 +531,14 @@ hipError_t bwd_d(const AttnArgs& a, const uint16_t* dout, float* dq, float* dk, 
     hipLaunchKernelGGL((attn_bwd_dq_kernel<D, VARLEN>), dim3((unsigned)gq), dim3(256), 0, stream, a,
                        dout, dq);
   if (gk > 0) {
-    if (bwd_split_mode(D)) {
+    // head_dim 256: the fused pass would need K, V, dK and dV of 32 keys (512
+    // registers) and spills; the two passes fit one wave per SIMD.
+    if (D == 256 || bwd_split_mode(D)) {
       hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, VARLEN, 1>), dim3((unsigned)gk), dim3(256), 0,
                          stream, a, dout, dk, dv, n_kb);
       hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, VARLEN, 2>), dim3((unsigned)gk), dim3(256), 0,
                          stream, a, dout, dk, dv, n_kb);
-    } else {
+    } else if constexpr (D != 256) {
       hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, VARLEN, 0>), dim3((unsigned)gk), dim3(256), 0,
                          stream, a, dout, dk, dv, n_kb);
     }
@@ -556,6 +558,8 @@ hipError_t launch_attention_bwd(const AttnArgs& a, int head_dim, bool varlen, co
                            : bwd_d<64, false>(a, dout, dq, dk, dv, n_pairs, n_kb, stream);
     case 128: return varlen ? bwd_d<128, true>(a, dout, dq, dk, dv, n_pairs, n_kb, stream)
                             : bwd_d<128, false>(a, dout, dq, dk, dv, n_pairs, n_kb, stream);
+    case 256: return varlen ? bwd_d<256, true>(a, dout, dq, dk, dv, n_pairs, n_kb, stream)
+                            : bwd_d<256, false>(a, dout, dq, dk, dv, n_pairs, n_kb, stream);
     default: return hipErrorInvalidValue;
   }
 }

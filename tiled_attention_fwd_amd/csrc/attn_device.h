@@ -154,8 +154,8 @@ template <int D>
 struct PipeLayout {
   static constexpr int CPR = D / 8;
   static constexpr int R = 64 / CPR;
-  static_assert(R == 4 || R == 8 || R == 16, "layout defined for head_dim 128, 64 and 32");
-  static constexpr int GK = 1024 + (R == 4 ? 64 : (R == 8 ? 128 : 0));
+  static_assert(R == 2 || R == 4 || R == 8 || R == 16, "layout defined for head_dim 256, 128, 64 and 32");
+  static constexpr int GK = 1024 + (R == 2 ? 32 : (R == 4 ? 64 : (R == 8 ? 128 : 0)));
   static constexpr int GV = 1024;
   static __device__ __forceinline__ int rot(int c) {
     return R == 8 ? 4 * ((c ^ (c >> 1)) & 1) : (R == 16 ? 4 * c : 0);
