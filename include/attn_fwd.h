@@ -381,8 +381,8 @@ attn_status_t attn_fwd_paged(const void* q, const void* k_cache, const void* v_c
  * k_cache, v_cache (num_pages, page_size, num_heads_k, head_dim): E4M3 bytes;
  * the keys and values are k_scale * K and v_scale * V (factors > 0, finite).
  * q stays bf16.  Every other argument, the workspace and the size rules are
- * those of attn_fwd_paged (the page-size limit counts one byte per element),
- * except that head_dim must be 64 or 128 (else ATTN_ERR_UNSUPPORTED).
+ * those of attn_fwd_paged (the page-size limit counts one byte per element;
+ * head_dim 32, 64, 128 or 256).
  * The cache bytes are dequantised to bf16 in registers (E4M3 values are exact
  * in bf16) and the products are the bf16 MFMAs of attn_fwd_paged, so the
  * results carry the same rounding as the bf16 path on the dequantised values.

@@ -236,8 +236,8 @@ def test_paged_fp8_and_mask_argument_checks(lib):
     base = (P, P, P, P, P, P, 2, 2, 8, 16, 2, 8, 2, 128, 1, 32, 0.125)
     assert g(*base, 0.0, 1.0, 1, P, None, None, 0, None) == UNSUP   # k factor
     assert g(*base, 1.0, float("inf"), 1, P, None, None, 0, None) == UNSUP
-    base32 = base[:13] + (32,) + base[14:]                       # E4M3 tiles: head_dim 64 and 128
-    assert g(*base32, 1.0, 1.0, 1, P, None, None, 0, None) == UNSUP
+    base48 = base[:13] + (48,) + base[14:]                       # E4M3 tiles: head_dim 32..256
+    assert g(*base48, 1.0, 1.0, 1, P, None, None, 0, None) == UNSUP
     ws = lib.attn_fwd_paged_workspace_bytes
     assert ws(8, 1, 8192, 64, 8, 128) > 0                       # 64 workgroups: split in 4
     assert ws(32, 1, 8192, 64, 8, 128) == 0                     # 256 (one per CU): no split

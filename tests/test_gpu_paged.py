@@ -187,7 +187,7 @@ def run_f8(w, k8, v8, kf, vf, workspace):
     return host(o), host(lse)
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [32, 64, 128, 256])
 @pytest.mark.parametrize("page,workspace", [(16, False), (64, True), (48, True)])
 def test_fp8_cache_decode_and_spec(d, page, workspace):
     w = gen.make_paged(f"f8c{d}", 2500 + d + page, [1, 4, 2, 1, 0], [7, 300, 1000, 64, 5], 8, 2,
@@ -200,9 +200,10 @@ def test_fp8_cache_decode_and_spec(d, page, workspace):
         print(check_o(o, o_ref), check_lse(lse, lse_ref))
 
 
-def test_fp8_cache_chunked_prefill_noncausal():
-    w = gen.make_paged("f8cp", 2600, [70, 5], [200, 40], 8, 2, 128, 32, False, fill=float("nan"))
-    k8, v8 = gen.paged_cache_e4m3(w, 2600)
+@pytest.mark.parametrize("d", [32, 128, 256])
+def test_fp8_cache_chunked_prefill_noncausal(d):
+    w = gen.make_paged("f8cp", 2600 + d, [70, 5], [200, 40], 8, 2, d, 32, False, fill=float("nan"))
+    k8, v8 = gen.paged_cache_e4m3(w, 2600 + d)
     o, lse = run_f8(w, k8, v8, 1.0, 1.0, False)
     o_ref, lse_ref = oracle.attention_paged_fp8kv(w.q, k8, v8, w.cu_seqlens_q, w.seqlens_k,
                                                   w.block_table, w.scale, 1.0, 1.0, False)

@@ -444,7 +444,6 @@ attn_status_t paged_impl(const void* q, const void* k_cache, const void* v_cache
   attn_status_t st = check_common(num_heads_q, num_heads_k, head_dim, scale);
   if (st != ATTN_OK) return st;
   if (!head_dim_ok(head_dim)) return ATTN_ERR_UNSUPPORTED;
-  if (kv_fp8 && head_dim != 64 && head_dim != 128) return ATTN_ERR_UNSUPPORTED;  // E4M3 tiles
   if (page_size < 16 || page_size % 16 != 0) return ATTN_ERR_UNSUPPORTED;
   if (kv_fp8)
     for (float f : {k_scale, v_scale})

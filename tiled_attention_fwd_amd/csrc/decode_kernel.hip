@@ -99,19 +99,32 @@ struct Frag32 {
 template <int D>
 constexpr int tile32_bytes() { return RowTile<D>::BYTES; }
 
-// E4M3 cache tiles: 32 rows of D bytes, row-major DMA lanes, chunk swizzles
-// (K: (row / 2) mod 8 at d=128, (row / 4) mod 4 at d=64; V: row mod 8 and
-// 2 ((row / 4) mod 2)) that keep the fragment reads below free of bank
-// conflicts.  The fragments are dequantised to bf16 in registers (E4M3 values
-// are exact in bf16), so the products stay bf16 MFMAs with exact operands.
+// E4M3 cache tiles: 32 rows of D bytes, row-major DMA lanes, and XOR chunk
+// swizzles of row bits for the two reads below (16-byte K row reads, 8-byte
+// transposed V reads of eight rows): K chunk (r ^ r/2) mod 16 / 8, (r ^ r/4)
+// mod 4, (r/4 ^ r/8) mod 2 and V chunk (r ^ r/2) mod 8 / 8 / 4 (mod 4 at
+// d=64), (r ^ r/4) mod 2 at head_dim 256 / 128 / 64 / 32.  A host model of
+// the placement and reads finds them free of bank conflicts except the V reads
+// at head_dim 256 (one of the two phase groupings, 2-way).  The V swizzle uses
+// row bits 0..3 only, so it is a lane constant for both 16-row halves of a
+// tile.  At head_dim 32 one DMA instruction carries all 32 rows (both 16-key
+// groups, which may lie in different pages), so it is issued once per group
+// with the other group's lanes off.  The fragments are dequantised to bf16 in
+// registers (E4M3 values are exact in bf16), so the products stay bf16 MFMAs
+// with exact operands.
 template <int D>
 struct RowTile8 {
   static constexpr int CPR = D / 16;   // 16-byte chunks per row
   static constexpr int R = 64 / CPR;   // rows per DMA instruction
   static constexpr int PITCH = D;
   static constexpr int BYTES = kTileKeys * PITCH;
-  static __device__ __forceinline__ int swz_k(int r) { return D == 128 ? ((r >> 1) & 7) : ((r >> 2) & 3); }
-  static __device__ __forceinline__ int swz_v(int r) { return D == 128 ? (r & 7) : (((r >> 2) & 1) << 1); }
+  static __device__ __forceinline__ int swz_k(int r) {
+    return D == 256 ? ((r ^ (r >> 1)) & 15)
+                    : D == 128 ? ((r ^ (r >> 1)) & 7) : D == 64 ? ((r ^ (r >> 2)) & 3) : (((r >> 2) ^ (r >> 3)) & 1);
+  }
+  static __device__ __forceinline__ int swz_v(int r) {
+    return D >= 128 ? ((r ^ (r >> 1)) & 7) : D == 64 ? ((r ^ (r >> 1)) & 3) : ((r ^ (r >> 2)) & 1);
+  }
 };
 
 typedef int i32x2v __attribute__((ext_vector_type(2)));
@@ -139,9 +152,9 @@ struct Frag32F8 {
     rd_row = l32 * L::PITCH;
     rd_x = L::swz_k(l32);
     const int vg = (lane >> 4) & 1, vi = lane & 15;
-    // natural row 16 tt + 8 hh + vi / 2: swz_v depends on vi only
+    // natural row 16 tt + 8 hh + vi / 2: swz_v uses row bits 0..3 only
     tr_base = (8 * hh + (vi >> 1)) * L::PITCH + 8 * (vi & 1) + 16 * vg;
-    tr_x = L::swz_v(vi >> 1);
+    tr_x = L::swz_v(8 * hh + (vi >> 1));
     tr_vg = vg;
   }
   int tr_x, tr_vg;
@@ -214,23 +227,41 @@ __device__ __forceinline__ int load_pages(const DecodeArgs& a, const int32_t* ta
 template <int D, int ES>
 using TileOf = typename std::conditional<ES == 2, RowTile<D>, RowTile8<D>>::type;
 
+// DMA instructions per 32-key tile and tensor (an instruction carrying both
+// 16-key groups is issued once per group)
+template <int D, int ES>
+constexpr int dma_per_tile() {
+  return TileOf<D, ES>::R > 16 ? 2 : kTileKeys / TileOf<D, ES>::R;
+}
+
 template <int D, int ES>
 __device__ __forceinline__ void dma_tile(const TilePages& tp, bool is_v, int hkv, int t,
                                          uint32_t tile, int lane) {
   using L = TileOf<D, ES>;
   constexpr int R = L::R;
-  constexpr int NI = kTileKeys / R;
+  constexpr int NQ = R > 16 ? 1 : kTileKeys / R;
   const int p = lane % L::CPR;
   const uint32_t row_bytes = (uint32_t)hkv * D * ES;
 #pragma unroll
-  for (int q = 0; q < NI; ++q) {
-    const int g = (q * R) >> 4;
+  for (int q = 0; q < NQ; ++q) {
     const int row = q * R + lane / L::CPR;
     const int key = t * kTileKeys + (is_v ? row : key_of_row(row));
     const int c = p ^ (is_v ? L::swz_v(row) : L::swz_k(row));
-    const u32x4 desc = make_desc(is_v ? tp.vbase[g] : tp.kbase[g], tp.bytes[g]);
-    const uint32_t voff = (uint32_t)(key - tp.pstart[g]) * row_bytes + (uint32_t)c * 16;
-    dma16(desc, voff, __builtin_amdgcn_readfirstlane(tile + q * 1024));
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(tile + q * 1024);
+    if constexpr (R > 16) {
+      // rows 0..15 and 16..31 (their keys too) are the tile's two 16-key groups
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        if ((row >> 4) == g) {
+          const u32x4 desc = make_desc(is_v ? tp.vbase[g] : tp.kbase[g], tp.bytes[g]);
+          dma16(desc, (uint32_t)(key - tp.pstart[g]) * row_bytes + (uint32_t)c * 16, m0);
+        }
+      }
+    } else {
+      const int g = (q * R) >> 4;
+      const u32x4 desc = make_desc(is_v ? tp.vbase[g] : tp.kbase[g], tp.bytes[g]);
+      dma16(desc, (uint32_t)(key - tp.pstart[g]) * row_bytes + (uint32_t)c * 16, m0);
+    }
   }
 }
 
@@ -259,7 +290,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void attn_decode_kernel(const Decode
   constexpr int NDS = D / 16, NDB = D / 32;
   using L = TileOf<D, ES>;
   constexpr int TB = L::BYTES;
-  constexpr int NI = kTileKeys / L::R;              // DMA instructions per tile per tensor
+  constexpr int NI = dma_per_tile<D, ES>();         // DMA instructions per tile per tensor
   constexpr int WAVE_LDS = NBUF * 2 * TB;           // NBUF stages of K and V
   constexpr int MERGE_LDS = WAVES * (32 * D + 64) * 4;
   constexpr int LDS = WAVES * WAVE_LDS > MERGE_LDS ? WAVES * WAVE_LDS : MERGE_LDS;
@@ -566,15 +597,14 @@ hipError_t launch_d(const DecodeArgs& a, int variant, hipStream_t stream) {
   // for bf16 caches (d=128 decode: 4x2 3.8, 3x3 3.6, 5x2 4.5 TB/s; d=64: 4x4
   // 3.4, 8x2 4.5, 5x4 4.2 TB/s).  E4M3 caches halve the stage size.
   if constexpr (D == 256) {
-    // bf16 caches only; a 32-key stage of K and V is 32 KiB, so two waves of
-    // two stages fill the LDS (each wave at one per SIMD can hold a landed
-    // tile's fragments in registers)
-    if (a.kv_fp8) return hipErrorInvalidValue;
-    launch_v<D, 2, 2, 2>(a, grid, stream);
+    // one wave per SIMD (each can hold a landed tile's fragments in
+    // registers); a 32-key stage of K and V is 32 KiB (bf16) or 16 KiB (E4M3),
+    // so two or four waves of two stages fill the LDS
+    if (a.kv_fp8) launch_v<D, 4, 2, 1>(a, grid, stream);
+    else launch_v<D, 2, 2, 2>(a, grid, stream);
   } else if constexpr (D == 32) {
-    // bf16 caches only (E4M3 tiles are laid out for head_dim 64 and 128)
-    if (a.kv_fp8) return hipErrorInvalidValue;
-    if (variant == 0) launch_v<D, 4, 4, 2>(a, grid, stream);
+    if (a.kv_fp8) launch_v<D, 8, 4, 1>(a, grid, stream);
+    else if (variant == 0) launch_v<D, 4, 4, 2>(a, grid, stream);
     else if (variant == 2) launch_v<D, 5, 4, 2>(a, grid, stream);
     else launch_v<D, 8, 2, 2>(a, grid, stream);
   } else if (a.kv_fp8) {
