@@ -502,8 +502,8 @@ def main():
                     help="time only the per-workload rows (no step, no JSON contract line)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(the forward shards by heads or sequences with no communication; see the design notes).",
+        print("bench.py runs on one GPU only: the library has no multi-GPU path (the forward "
+              "would shard by heads or sequences with no communication between GPUs).",
               file=sys.stderr)
         sys.exit(2)
 
