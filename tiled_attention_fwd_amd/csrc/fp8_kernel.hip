@@ -41,6 +41,17 @@ __device__ __forceinline__ f32x16 mfma_f8(i32x8 a, i32x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, kScaleOne, 0, kScaleOne);
 }
 
+// The same product with B multiplied by 2^(scale_b - 127): each lane's E8M0
+// scale applies to its own 32-element block of B, i.e. to one column.
+__device__ __forceinline__ f32x16 mfma_f8_bscale(i32x8 a, i32x8 b, f32x16 c, int scale_b) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, kScaleOne, 0, scale_b);
+}
+
+// Binades a row maximum may climb above the reference m before O is rescaled
+// (the PV product carries the lift meanwhile; 2^32 keeps O and l far inside
+// fp32).
+constexpr float kMaxLift = 32.f;
+
 template <int D, int TK>
 struct F8Tile {
   static constexpr int CPR = D / 16;    // 16-byte chunks per row
@@ -226,12 +237,19 @@ __global__ __launch_bounds__(WAVES * 64, D == 256 ? 1 : 2) void attn_fwd_fp8_ker
       sb = mfma_f8(af, qf[s], sb);
     }
   };
-  // Masks, row maximum, rescale, and the E4M3 P operands of NB 32-key score
-  // blocks starting at key kbeg (register r of block b holds key
-  // kbeg + 32 b + 16 (r / 8) + 8 hh + r % 8).  2^7 p = exp2(c s - m + 7) is
-  // rounded four values at a time into pf[b / 2] (byte 16 (b % 2) + r of a P
-  // operand <-> key 32 (b % 2) + 16 (r / 8) + 8 hh + r % 8 of its 64 keys);
-  // the row sum keeps the same factor and the unrounded values.
+  // Masks, row maximum, and the E4M3 P operands of NB 32-key score blocks
+  // starting at key kbeg (register r of block b holds key
+  // kbeg + 32 b + 16 (r / 8) + 8 hh + r % 8).  O and l stay relative to the
+  // reference m.  P is rounded relative to mu = m + lift, lift = the whole
+  // binades the tile's maximum lies above m: 2^7 p = exp2(c s - mu + 7) < 2^8
+  // stays inside E4M3 (448) and is rounded four values at a time into
+  // pf[b / 2] (byte 16 (b % 2) + r of a P operand <-> key
+  // 32 (b % 2) + 16 (r / 8) + 8 hh + r % 8 of its 64 keys).  The PV product
+  // multiplies P back by 2^lift through its E8M0 operand scale (exact), and
+  // the row sum takes the same factor on the unrounded values.  m itself
+  // moves (O rescaled) only on a row's first visible tile or after a climb of
+  // more than kMaxLift binades.
+  int psc = kScaleOne;  // E8M0 scale of this tile's P operands (127 + lift)
   auto softmax = [&](int kbeg, auto& sb, auto& pf) __attribute__((always_inline)) {
     constexpr int NB = sizeof(sb) / sizeof(sb[0]);
     const bool edge = (kbeg + 32 * NB > lk) || (a.causal && kbeg + 32 * NB - 1 > qw0 + off);
@@ -249,9 +267,7 @@ __global__ __launch_bounds__(WAVES * 64, D == 256 ? 1 : 2) void attn_fwd_fp8_ker
         mt1 = fmaxf(mt1, sb[b][r + 1]);
       }
     float mt = half_max(fmaxf(mt0, mt1)) * a.c;
-    // lazy rescale: the reference m moves only when the row maximum passes
-    // it by more than a factor 2, so 2^7 p <= 2^8 stays inside E4M3 (448)
-    if (mt > m + 1.f) {
+    if (mt > m + kMaxLift) {
       const float alpha = __builtin_amdgcn_exp2f(m - mt);  // 0 while m = -inf
       l *= alpha;
 #pragma unroll
@@ -260,7 +276,9 @@ __global__ __launch_bounds__(WAVES * 64, D == 256 ? 1 : 2) void attn_fwd_fp8_ker
         for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
       m = mt;
     }
-    const float nb = m == -INFINITY ? 0.f : 7.f - m;
+    const float lift = m == -INFINITY ? 0.f : fminf(floorf(fmaxf(mt - m, 0.f)), kMaxLift);
+    const float nb = m == -INFINITY ? 0.f : 7.f - (m + lift);
+    psc = kScaleOne + (int)lift;
     float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
     for (int b = 0; b < NB; ++b)
@@ -273,7 +291,7 @@ __global__ __launch_bounds__(WAVES * 64, D == 256 ? 1 : 2) void attn_fwd_fp8_ker
         rs1 += p4[1] + p4[3];
         pf[b >> 1][4 * (b & 1) + (r0 >> 2)] = pack_fp8x4(p4[0], p4[1], p4[2], p4[3]);
       }
-    l += rs0 + rs1;
+    l += ldexpf(rs0 + rs1, (int)lift);
   };
   // O^T += V^T P^T for the 64-key half hf of tile t (V in lds[t & 1][1])
   auto pv = [&](int t, int hf, const i32x8& pf) __attribute__((always_inline)) {
@@ -288,7 +306,7 @@ __global__ __launch_bounds__(WAVES * 64, D == 256 ? 1 : 2) void attn_fwd_fp8_ker
         vf[2 * tt] = x[0];
         vf[2 * tt + 1] = x[1];
       }
-      oacc[db] = mfma_f8(vf, pf, oacc[db]);
+      oacc[db] = mfma_f8_bscale(vf, pf, oacc[db], psc);
     }
   };
 
