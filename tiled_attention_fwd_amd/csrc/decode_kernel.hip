@@ -285,6 +285,8 @@ __device__ __forceinline__ void wait_tile(int after) {
   wait_vm<0>();
 }
 
+constexpr float kLazyRescale = 8.0f;
+
 template <int D, int WAVES, int NBUF, int ES>
 __global__ __launch_bounds__(WAVES * 64, 1) void attn_decode_kernel(const DecodeArgs a) {
   constexpr int NDS = D / 16, NDB = D / 32;
@@ -335,6 +337,12 @@ __global__ __launch_bounds__(WAVES * 64, 1) void attn_decode_kernel(const Decode
   const int qi = col_ok ? r / a.group : 0;
   const int hq = kvh * a.group + (col_ok ? r % a.group : 0);
   const int lim = !col_ok ? -1 : (a.causal ? min(dr.lk - 1, qi + dr.lk - dr.lq) : dr.lk - 1);
+  // the smallest limit over the wave's valid columns: tiles whose keys all lie
+  // at or below it need no mask (other columns are never stored)
+  int lim_min = col_ok ? lim : 0x7fffffff;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) lim_min = min(lim_min, __shfl_xor(lim_min, o));
+  lim_min = __builtin_amdgcn_readfirstlane(lim_min);
 
   // Q as the B operand.  bf16 cache: MFMA s takes dims 16 s + 8 hh + e; E4M3
   // cache: MFMA 2 j + sub takes dims 32 j + 16 hh + 8 sub + e (the order of
@@ -421,30 +429,37 @@ __global__ __launch_bounds__(WAVES * 64, 1) void attn_decode_kernel(const Decode
       st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr[s], qf[s], st, 0, 0, 0);
     // register e holds key 32 t + 16 (e / 8) + 8 hh + e % 8 for this column
     const int kbase = t * kTileKeys + hh * 8;
+    if (t * kTileKeys + kTileKeys - 1 > lim_min) {
+      keep_branch();
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (kbase + ((e >> 3) << 4) + (e & 7) > lim) st[e] = -INFINITY;
+    }
     float mt = -INFINITY;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int key = kbase + ((e >> 3) << 4) + (e & 7);
-      const float v = key <= lim ? st[e] * a.c : -INFINITY;
-      st[e] = v;
-      mt = fmaxf(mt, v);
+    for (int e = 0; e < 16; ++e) mt = fmaxf(mt, st[e]);
+    mt = half_max(mt) * a.c;
+    // lazy reference maximum: m (and O, l) move only when a column's maximum
+    // passes it by more than 2^8, so the bf16 probabilities stay <= 2^8
+    const bool grow = mt > m + kLazyRescale;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float m_new = grow ? mt : m;
+      const float alpha = grow ? __builtin_amdgcn_exp2f(m - m_new) : 1.f;  // 0 while m = -inf
+      m = m_new;
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
     }
-    mt = half_max(mt);
-    const float mn = fmaxf(m, mt);
-    const float mu = mn == -INFINITY ? 0.f : mn;
-    const float alpha = __builtin_amdgcn_exp2f(m - mu);
-    m = mn;
+    const float mu = m == -INFINITY ? 0.f : m;
     float rs = 0.f;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      st[e] = __builtin_amdgcn_exp2f(st[e] - mu);
+      st[e] = __builtin_amdgcn_exp2f(fmaf(st[e], a.c, -mu));
       rs += st[e];
     }
-    l = l * alpha + rs;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+    l += rs;
     bf16x8 pf[2];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
