@@ -64,16 +64,16 @@ struct TileFrag {
   }
 };
 
-// DMA of rows r0 .. r0+63 of a bf16 matrix (row pitch row_bytes, rows past the
-// descriptor's range read as zero) into a 64-row tile at LDS byte address
-// tile, rows permuted within 32-row blocks; this wave issues instructions
-// w, w + nw, ... of the tile's 64 / R.
-template <int D>
+// DMA of rows r0 .. r0+ROWS-1 of a bf16 matrix (row pitch row_bytes, rows
+// past the descriptor's range read as zero) into a ROWS-row tile (64 or 32)
+// at LDS byte address tile, rows permuted within 32-row blocks; this wave
+// issues instructions w, w + nw, ... of the tile's ROWS / R.
+template <int D, int ROWS = 64>
 __device__ __forceinline__ void dma_rows(u32x4 desc, uint32_t r0, uint32_t row_bytes, uint32_t tile,
                                          int w, int nw, int lane) {
   using L = PipeLayout<D>;
   constexpr int R = L::R;
-  constexpr int NI = 64 / R;
+  constexpr int NI = ROWS / R;
   const int c = lane / R;
   for (int q = w; q < NI; q += nw) {
     const int row = q * R + ((lane % R) ^ L::rot(c));
@@ -85,8 +85,8 @@ __device__ __forceinline__ void dma_rows(u32x4 desc, uint32_t r0, uint32_t row_b
 
 constexpr int kTileBytes128 = 16 * PipeLayout<128>::GK;
 
-template <int D>
-constexpr int tile_bytes() { return (64 / PipeLayout<D>::R) * PipeLayout<D>::GK; }
+template <int D, int ROWS = 64>
+constexpr int tile_bytes() { return (ROWS / PipeLayout<D>::R) * PipeLayout<D>::GK; }
 
 // ---------------------------------------------------------------------------
 // D = rowsum(dO * O) for every (query row, head): one wave per pair.
@@ -120,14 +120,16 @@ __global__ __launch_bounds__(256) void bwd_dvec_kernel(const AttnArgs a, const u
 }
 
 // ---------------------------------------------------------------------------
-// dQ: 4 waves x 32 queries; K/V tiles of 64 keys in two LDS buffers.
+// dQ: 4 waves x 32 queries; K/V tiles of 64 keys (32 at head_dim 256, where
+// the score, dP and dS blocks of 64 keys would push Q, dO and dQ into spills)
+// in two LDS buffers.
 // ---------------------------------------------------------------------------
 template <int D, bool VARLEN>
 __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void attn_bwd_dq_kernel(const AttnArgs a, const uint16_t* dout,
                                                             float* dq) {
-  constexpr int BM = 128, BN = 64;
+  constexpr int BM = 128, BN = D == 256 ? 32 : 64;
   constexpr int NDS = D / 16, NDB = D / 32, NKB = BN / 32;
-  constexpr int TB = tile_bytes<D>();
+  constexpr int TB = tile_bytes<D, BN>();
   __shared__ __attribute__((aligned(16))) unsigned char lds[4 * TB];  // K0 V0 K1 V1
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -198,8 +200,8 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void attn_bwd_dq_kernel(cons
   const uint32_t lds0 = lds_addr(lds);
   auto dma = [&](int t) {
     const uint32_t b = (uint32_t)(t & 1) * 2 * TB;
-    dma_rows<D>(kdesc, (uint32_t)t * BN, k_rb, lds0 + b, wave, 4, lane);
-    dma_rows<D>(vdesc, (uint32_t)t * BN, v_rb, lds0 + b + TB, wave, 4, lane);
+    dma_rows<D, BN>(kdesc, (uint32_t)t * BN, k_rb, lds0 + b, wave, 4, lane);
+    dma_rows<D, BN>(vdesc, (uint32_t)t * BN, v_rb, lds0 + b + TB, wave, 4, lane);
   };
   TileFrag<D> fr;
   fr.init(lane);
