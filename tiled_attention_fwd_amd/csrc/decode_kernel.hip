@@ -428,6 +428,9 @@ __global__ __launch_bounds__(WAVES * 64, 1) void attn_decode_kernel(const Decode
     for (int s = 0; s < NDS; ++s)
       st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr[s], qf[s], st, 0, 0, 0);
     // register e holds key 32 t + 16 (e / 8) + 8 hh + e % 8 for this column
+    // scores in base-2 units first: c carries the scale's sign here
+#pragma unroll
+    for (int e = 0; e < 16; ++e) st[e] *= a.c;
     const int kbase = t * kTileKeys + hh * 8;
     if (t * kTileKeys + kTileKeys - 1 > lim_min) {
       keep_branch();
@@ -438,7 +441,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void attn_decode_kernel(const Decode
     float mt = -INFINITY;
 #pragma unroll
     for (int e = 0; e < 16; ++e) mt = fmaxf(mt, st[e]);
-    mt = half_max(mt) * a.c;
+    mt = half_max(mt);
     // lazy reference maximum: m (and O, l) move only when a column's maximum
     // passes it by more than 2^8, so the bf16 probabilities stay <= 2^8
     const bool grow = mt > m + kLazyRescale;
@@ -456,7 +459,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void attn_decode_kernel(const Decode
     float rs = 0.f;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      st[e] = __builtin_amdgcn_exp2f(fmaf(st[e], a.c, -mu));
+      st[e] = __builtin_amdgcn_exp2f(st[e] - mu);
       rs += st[e];
     }
     l += rs;
