@@ -412,7 +412,7 @@ attn_status_t attn_fwd_paged_fp8kv(const void* q, const void* k_cache, const voi
  * (the array's copy on that device is used).
  * Limit: a shape whose split needs more than ATTN_NOALLOC_SCRATCH_BYTES (only
  * possible under the ATTN_PAGED_CHUNK_TILES test override; every default plan
- * needs at most 67.3 MB at head_dim 256, 33.8 MB at 128) returns
+ * needs at most 16.8 MB at head_dim 256, 8.4 MB at 128) returns
  * ATTN_ERR_SCRATCH before anything is launched.
  * Every call on one GPU shares that GPU's array, which keeps the last call's
  * contents (each call writes every slot it reads, so nothing needs clearing):
