@@ -100,6 +100,23 @@ def test_fp8_lq_ne_lk_and_empty(d, causal, fp8_tile):
     print(run_checked(w, fp8_tile, causal))
 
 
+@pytest.mark.parametrize("causal", [True, False])
+def test_fp8_row_maximum_climbing_past_the_lift_range(causal, fp8_tile):
+    """Q = 1.0 and keys whose magnitude doubles along the sequence (E4M3
+    2^-6 .. 2^4, positive): a row's maximum climbs from ~0.3 to ~260 binades,
+    in steps past the 32 binades that the PV product's operand scale carries,
+    so the output rescale path runs as well as the lifted one."""
+    w = gen.make_fp8_varlen("f8climb", 2300, [300, 129, 64], 2, 2, 128, causal)
+    q = np.full_like(w.q, 0x38)  # 1.0
+    k = w.k.copy()
+    for s in range(len(w.lengths_k)):
+        k0, k1 = int(w.cu_seqlens_k[s]), int(w.cu_seqlens_k[s + 1])
+        e = 1 + (np.arange(k1 - k0) * 11) // max(k1 - k0, 1)  # exponent field 1..11
+        k[k0:k1] = (e.astype(np.uint8) << 3)[:, None, None]
+    w.q, w.k = q, k
+    print(run_checked(w, fp8_tile, causal))
+
+
 def test_fp8_factors(fp8_tile):
     w = gen.make_fp8_varlen("f8fac", 2200, [77, 300], 4, 1, 128, True, factors=(0.5, 4.0, 0.125))
     o, lse = run_varlen(w)
