@@ -187,6 +187,37 @@ def run_f8(w, k8, v8, kf, vf, workspace):
     return host(o), host(lse)
 
 
+def _climbing_cache(w, cache, code):
+    """Every head and dim of each sequence's key rows set to code(p) for 2^p,
+    p rising from -4 to 4 along the sequence."""
+    out = cache.copy()
+    for s, lk in enumerate(w.seqlens_k):
+        lk = int(lk)
+        p = np.floor(-4 + 8 * np.arange(lk) / max(lk - 1, 1)).astype(np.int64)
+        for j in range(lk):
+            out[w.block_table[s, j // w.page_size], j % w.page_size] = code(int(p[j]))
+    return out
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_decode_row_maximum_climbing(d):
+    """Q = 1 and cached keys 2^-4 .. 2^4 rising along each sequence: the row
+    maxima climb past the 2^8 lazy-rescale threshold many times (bf16 cache
+    with and without a split, E4M3 cache)."""
+    w = gen.make_paged("dclimb", 1500 + d, [1, 4, 1], [1000, 300, 64], 8, 2, d, 16, True,
+                       fill=float("nan"))
+    bf = lambda x: gen.bf16_bits_from_f32(np.array([x], dtype=np.float32))[0]
+    w.q = np.full_like(w.q, bf(1.0))
+    w.k_cache = _climbing_cache(w, w.k_cache, lambda p: bf(2.0 ** p))
+    print(check(w), check(w, workspace=True))
+    k8, v8 = gen.paged_cache_e4m3(w, 1500 + d)
+    k8 = _climbing_cache(w, k8, lambda p: np.uint8((p + 7) << 3))  # E4M3 2^p
+    o, lse = run_f8(w, k8, v8, 1.0, 1.0, False)
+    o_ref, lse_ref = oracle.attention_paged_fp8kv(w.q, k8, v8, w.cu_seqlens_q, w.seqlens_k,
+                                                  w.block_table, w.scale, 1.0, 1.0, True)
+    print(check_o(o, o_ref), check_lse(lse, lse_ref))
+
+
 @pytest.mark.parametrize("d", [32, 64, 128, 256])
 @pytest.mark.parametrize("page,workspace", [(16, False), (64, True), (48, True)])
 def test_fp8_cache_decode_and_spec(d, page, workspace):

@@ -247,6 +247,41 @@ def test_every_compiled_tile_policy(policy, causal):
         del os.environ["ATTN_FWD_TILE"]
 
 
+def climbing_keys(k_bits, cu_k, lo=-4, hi=4):
+    """K rows set to 2^p in every head and dim, p rising from lo to hi along
+    each sequence (bf16 bits)."""
+    k = k_bits.copy()
+    for s in range(len(cu_k) - 1):
+        k0, k1 = int(cu_k[s]), int(cu_k[s + 1])
+        p = np.floor(lo + (hi - lo) * np.arange(k1 - k0) / max(k1 - k0 - 1, 1))
+        k[k0:k1] = gen.bf16_bits_from_f32(np.exp2(p).astype(np.float32))[:, None, None]
+    return k
+
+
+@pytest.mark.parametrize("policy", [str(i) for i in range(21)])
+def test_row_maximum_climbing_every_policy(policy):
+    """Q = 1 and keys 2^-4 .. 2^4 rising along each sequence: a row's maximum
+    climbs by up to ~130 binades at a time (to ~260 at head_dim 128), far past
+    the 2^8 lazy-rescale threshold, so every policy's rescale branch runs after
+    its first tile as well as on it."""
+    os.environ["ATTN_FWD_TILE"] = policy
+    try:
+        one = gen.bf16_bits_from_f32(np.array([1.0], dtype=np.float32))[0]
+        for d in D_ALL:
+            if not compiled(policy, d):
+                continue
+            w = gen.make_varlen("climb", 1300 + d, [700, 150, 64], 2, 1, d, True)
+            w.q = np.full_like(w.q, one)
+            w.k = climbing_keys(w.k, w.cu_seqlens_k)
+            o, lse = run_varlen(w)
+            o_ref, lse_ref = oracle.attention_varlen(w.q, w.k, w.v, w.cu_seqlens_q,
+                                                     w.cu_seqlens_k, w.scale, True)
+            check_o(o, o_ref)
+            check_lse(lse, lse_ref)
+    finally:
+        del os.environ["ATTN_FWD_TILE"]
+
+
 @pytest.mark.parametrize("causal", [True, False])
 def test_default_policy_one_round_of_64_query_blocks(causal):
     # head_dim 128, 512..4096 queries and at most 512 blocks of 64 queries:
