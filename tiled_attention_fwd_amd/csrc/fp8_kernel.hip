@@ -10,10 +10,12 @@
 // rate): S^T = K Q^T with 64 dims per instruction, and O^T += V^T P^T with the
 // probabilities rounded to E4M3 after scaling by 2^7 (the scale is folded into
 // the exponent; p stays in the format's normal range down to 2^-13); the row
-// sums use the fp32 probabilities with the same factor, the row maximum is
-// tracked lazily (the reference moves only when passed by more than a factor
-// 2, so 2^7 p <= 2^8 < 448), and the factors fold into the score scale and the
-// final normalisation.
+// sums use the fp32 probabilities with the same factor.  Each tile rounds P
+// relative to the whole binades its maximum lies above the row's reference
+// maximum (so 2^7 p < 2^8 < 448) and the PV product multiplies them back
+// through its E8M0 operand scale, so the reference and O move only on a row's
+// first tile or a climb of more than 32 binades.  The factors fold into the
+// score scale and the final normalisation.
 //
 // Workgroup: 4 waves x 32 queries (BM 128), 64-key tiles of K and V staged by
 // LDS DMA into two buffers (one barrier per tile), row-major DMA lanes with a
