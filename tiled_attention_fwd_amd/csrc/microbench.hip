@@ -1,6 +1,6 @@
 // Microbenchmarks that ground the roofline figures used for the attention
 // kernel on gfx950: MFMA bf16 32x32x16 rate, v_exp_f32 and v_fma_f32 issue
-// rates, LDS 16-byte read bandwidth, a plain 16-byte copy kernel (its known
+// rates, LDS read bandwidth (16-byte, 8-byte and 8-byte transposing reads), a plain 16-byte copy kernel (its known
 // byte count calibrates the HBM traffic counters), and the MFMA rate with
 // independent VALU, exp and LDS work mixed in at 2 waves per SIMD (the
 // ceiling for the attention loop's instruction mix), and two read-only HBM
@@ -102,6 +102,29 @@ __global__ __launch_bounds__(256) void lds_kernel(float* out) {
   out[blockIdx.x * blockDim.x + threadIdx.x] = (float)(acc.x ^ acc.y ^ acc.z ^ acc.w);
 }
 
+// 8-byte LDS reads, plain (ds_read_b64) or transposing (ds_read_b64_tr_b16,
+// the V operand read of the attention loop): each wave reads 512 contiguous
+// bytes per instruction, offsets wrap inside the 64 KiB buffer.
+template <bool TR>
+__global__ __launch_bounds__(256) void lds8_kernel(float* out) {
+  __shared__ __attribute__((aligned(16))) uint4 buf[4096];  // 64 KiB
+  for (int i = threadIdx.x; i < 4096; i += 256) buf[i] = make_uint4(i, i + 1, i + 2, i + 3);
+  __syncthreads();
+  const uint16_t* b16 = reinterpret_cast<const uint16_t*>(buf);
+  uint2 acc = make_uint2(0, 0);
+  for (int i = 0; i < kIters; ++i) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int e = (threadIdx.x * 4 + j * 1024 + i * 256) & 32767;  // element offset, 8-byte aligned
+      uint2 v;
+      if constexpr (TR) v = attnfwd::ds_read_tr16(b16 + e);
+      else v = *reinterpret_cast<const uint2*>(b16 + e);
+      acc.x ^= v.x; acc.y ^= v.y;
+    }
+  }
+  out[blockIdx.x * blockDim.x + threadIdx.x] = (float)(acc.x ^ acc.y);
+}
+
 __global__ __launch_bounds__(256) void copy_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
                                                   long n) {
   long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
@@ -161,9 +184,13 @@ __global__ __launch_bounds__(256) void read_dma_kernel(const void* src, uint32_t
 }
 
 // Per MFMA: NV independent v_fma_f32, NX v_exp_f32, NL 16-byte LDS reads
-// (each feeding a later MFMA's A operand).  Two accumulators alternate.
+// (each feeding a later MFMA's A operand), and NT pairs of transposing 8-byte
+// reads (the V operand of the attention loop's P V products); with ALT the
+// 16-byte reads go with even MFMAs and the transposing pairs with odd ones,
+// as the score and P V halves of the attention loop alternate.  Two
+// accumulators alternate.
 constexpr int kMixIters = 256;
-template <int NV, int NX, int NL>
+template <int NV, int NX, int NL, int NT = 0, bool ALT = false>
 __global__ void mix_kernel(float* out, float seed) {
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   const int lane = threadIdx.x & 63;
@@ -188,9 +215,19 @@ __global__ void mix_kernel(float* out, float seed) {
       for (int j = 0; j < NX; ++j) v[(k * 5 + j + 7) & 15] = __builtin_amdgcn_exp2f(v[(k * 5 + j + 7) & 15]);
 #pragma unroll
       for (int j = 0; j < NL; ++j) {
+        if (ALT && (k & 1)) continue;
         // offsets stay below 32 KiB of the 100 KiB dynamic LDS
         const uint4 u = *reinterpret_cast<const uint4*>(lds + ((lane * 16 + (k * NL + j) * 1024 + it * 64) & 32767));
         a = __builtin_bit_cast(bf16x8, u);
+      }
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        if (ALT && !(k & 1)) continue;
+        const int e = (lane * 4 + (k * NT + j) * 512 + it * 32) & 16383;  // elements, below 32 KiB
+        const uint16_t* b16 = reinterpret_cast<const uint16_t*>(lds);
+        const uint2 lo = attnfwd::ds_read_tr16(b16 + e);
+        const uint2 hi = attnfwd::ds_read_tr16(b16 + ((e + 256) & 16383));
+        a = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
       }
     }
   }
@@ -246,6 +283,10 @@ int main(int argc, char** argv) {
   ms = time_ms([&] { hipLaunchKernelGGL(lds_kernel, dim3(cus * 2), dim3(256), 0, 0, out); }, 5);
   const double lds_bytes = (double)cus * 2 * 256 * kIters * 8 * 16;
   const double lds_tbs = lds_bytes / (ms * 1e-3) / 1e12;
+  ms = time_ms([&] { hipLaunchKernelGGL(lds8_kernel<false>, dim3(cus * 2), dim3(256), 0, 0, out); }, 5);
+  const double lds8_tbs = lds_bytes / 2 / (ms * 1e-3) / 1e12;
+  ms = time_ms([&] { hipLaunchKernelGGL(lds8_kernel<true>, dim3(cus * 2), dim3(256), 0, 0, out); }, 5);
+  const double lds8tr_tbs = lds_bytes / 2 / (ms * 1e-3) / 1e12;
 
   // MFMA rate with mixed-in work: 512 threads and 100 KiB of LDS per workgroup,
   // one workgroup per CU = 2 waves per SIMD
@@ -260,6 +301,9 @@ int main(int argc, char** argv) {
   const double mix_x1 = mix(mix_kernel<0, 1, 0>);
   const double mix_l1 = mix(mix_kernel<0, 0, 1>);
   const double mix_all = mix(mix_kernel<4, 1, 1>);
+  const double mix_t1 = mix(mix_kernel<0, 0, 0, 1>);
+  const double mix_all_t = mix(mix_kernel<4, 1, 0, 1>);
+  const double mix_alt = mix(mix_kernel<4, 1, 1, 1, true>);
 
   uint4 *src, *dst;
   const long n = copy_bytes / 16;
@@ -288,9 +332,13 @@ int main(int argc, char** argv) {
          "\"exp2_tops\": %.3f, \"fma_tops\": %.3f, \"lds_read_tbs\": %.2f, "
          "\"copy_gbs\": %.1f, \"copy_bytes_each_way\": %ld, "
          "\"mfma_mix_2w_tflops\": {\"mfma_only\": %.1f, \"plus_4_fma\": %.1f, "
-         "\"plus_1_exp\": %.1f, \"plus_1_lds16\": %.1f, \"plus_4_fma_1_exp_1_lds16\": %.1f}}\n",
+         "\"plus_1_exp\": %.1f, \"plus_1_lds16\": %.1f, \"plus_4_fma_1_exp_1_lds16\": %.1f, "
+         "\"plus_2_lds8_tr\": %.1f, \"plus_4_fma_1_exp_2_lds8_tr\": %.1f, "
+         "\"plus_4_fma_1_exp_alternating_lds16_or_2_lds8_tr\": %.1f}, "
+         "\"lds_read8_tbs\": %.2f, \"lds_read8_tr_tbs\": %.2f}\n",
          prop.name, cus, prop.clockRate / 1000, read_gbs, read_dma_gbs, read_dma2_gbs, mfma_tflops, exp_sub_rate, exp_rate, fma_rate,
-         lds_tbs, copy_gbs, n * 16, mix_pure, mix_v4, mix_x1, mix_l1, mix_all);
+         lds_tbs, copy_gbs, n * 16, mix_pure, mix_v4, mix_x1, mix_l1, mix_all, mix_t1, mix_all_t, mix_alt,
+         lds8_tbs, lds8tr_tbs);
   CHECK(hipFree(src));
   CHECK(hipFree(dst));
   CHECK(hipFree(out));
