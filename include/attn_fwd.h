@@ -40,7 +40,7 @@
  *    split-capable policies when a workspace is given, ATTN_FWD_ORDER=<1..4>
  *    forces the workgroup order (head-remapped block-major, sequence-major,
  *    unit-major, compact), ATTN_FP8_TILE=128|256 forces the fp8 query block,
- *    ATTN_PAGED_VARIANT=<0..2>, ATTN_PAGED_ORDER=0|1 and
+ *    ATTN_PAGED_VARIANT=<0..3>, ATTN_PAGED_ORDER=0|1 and
  *    ATTN_PAGED_CHUNK_TILES=<n> force the paged kernel's layout, grid order
  *    and key-range parts, and ATTN_BWD_SPLIT=1 runs the backward's dV and dK
  *    as two passes.  Every forced choice computes the same attention; the

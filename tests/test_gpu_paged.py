@@ -162,6 +162,21 @@ def test_full_size_decode_batch_sampled():
         check_lse(lse[:, s:s + 1], lse_ref, f"seq {s}")
 
 
+@pytest.mark.parametrize("page", [16, 32])
+def test_many_short_decode_sequences_two_workgroups_per_cu(page):
+    """72 sequences x 8 KV heads at d=64 (576 workgroups, no split): the
+    default layout of four waves of two stages, two workgroups per CU; ragged
+    key lengths from 1 to 700 and NaN in every cache row no sequence owns."""
+    r = np.random.Generator(np.random.PCG64(1900 + page))
+    lens = [int(x) for x in r.integers(1, 701, size=72)]
+    w = gen.make_paged(f"many{page}", 1901 + page, [1] * 72, lens, 8, 8, 64, page, True,
+                       fill=float("nan"))
+    t = api()
+    plan_ws = t.attn_fwd_paged_workspace_bytes(72, 1, max(lens), 8, 8, 64)
+    assert plan_ws == 0  # no split: 576 workgroups already
+    print(check(w))
+
+
 @pytest.mark.parametrize("d,lk", [(128, 6000), (64, 9500), (32, 7000), (256, 3000)])
 def test_long_sequence_without_split(d, lk):
     # no workspace: one workgroup walks the whole key range, more than 32 tiles

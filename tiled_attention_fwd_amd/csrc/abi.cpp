@@ -257,10 +257,10 @@ int paged_chunk_override() {
   return (int)v;
 }
 
-// ATTN_PAGED_VARIANT=<0|1|2> picks the waves x stages layout (sweeps).
+// ATTN_PAGED_VARIANT=<0|1|2|3> picks the waves x stages layout (sweeps).
 int paged_variant() {
   const char* s = getenv("ATTN_PAGED_VARIANT");
-  if (s == nullptr || *s < '0' || *s > '2' || s[1] != '\0') return -1;
+  if (s == nullptr || *s < '0' || *s > '3' || s[1] != '\0') return -1;
   return *s - '0';
 }
 

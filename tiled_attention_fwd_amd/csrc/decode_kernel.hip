@@ -287,8 +287,18 @@ __device__ __forceinline__ void wait_tile(int after) {
 
 constexpr float kLazyRescale = 8.0f;
 
+// Two workgroups per CU when one takes at most half of the LDS and four waves:
+// then each may use 256 registers, so two waves share a SIMD.
 template <int D, int WAVES, int NBUF, int ES>
-__global__ __launch_bounds__(WAVES * 64, 1) void attn_decode_kernel(const DecodeArgs a) {
+constexpr int decode_min_waves() {
+  constexpr int tb = 32 * D * ES;  // bytes of a 32-key tile of K (or V)
+  constexpr int lds_w = WAVES * NBUF * 2 * tb;
+  constexpr int lds_m = WAVES * (32 * D + 64) * 4;
+  return (WAVES <= 4 && D <= 128 && (lds_w > lds_m ? lds_w : lds_m) <= 80 * 1024) ? 2 : 1;
+}
+
+template <int D, int WAVES, int NBUF, int ES>
+__global__ __launch_bounds__(WAVES * 64, (decode_min_waves<D, WAVES, NBUF, ES>())) void attn_decode_kernel(const DecodeArgs a) {
   constexpr int NDS = D / 16, NDB = D / 32;
   using L = TileOf<D, ES>;
   constexpr int TB = L::BYTES;
@@ -598,7 +608,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeArgs a) {
 // variants trade waves (latency hiding of the softmax/MFMA work) for stages
 // (tiles in flight per wave).  d=128 (16 KiB per stage): 0 = 4 waves x 2
 // stages, 1 = 3 x 3, 2 = 5 x 2; d=64 (8 KiB per stage) and d=32 (4 KiB):
-// 0 = 4 x 4, 1 = 8 x 2, 2 = 5 x 4.
+// 0 = 4 x 4, 1 = 8 x 2, 2 = 5 x 4, 3 = 4 x 2 (two workgroups per CU).
 template <int D, int W, int NB, int ES>
 hipError_t launch_v(const DecodeArgs& a, int64_t grid, hipStream_t stream) {
   hipLaunchKernelGGL((attn_decode_kernel<D, W, NB, ES>), dim3((unsigned)grid), dim3(W * 64), 0,
@@ -641,8 +651,16 @@ hipError_t launch_d(const DecodeArgs& a, int variant, hipStream_t stream) {
     else if (variant == 1) launch_v<D, 3, 3, 2>(a, grid, stream);
     else launch_v<D, 5, 2, 2>(a, grid, stream);
   } else {
+    // A grid of at least two workgroups per CU with no split parts (many
+    // short sequences): four waves of two stages take 64 KiB of LDS, so two
+    // workgroups share a CU and one's start and merge overlap the other's
+    // streaming (128 sequences x 32 heads, 1-2k keys, d=64, cold: 347 -> 325
+    // us; 2 x 4 and 4 x 3 stages measured 377 and 422).  A split plan aims
+    // at one workgroup per CU, which the eight-wave layout fills.
+    const bool many = a.n_split == 1 && grid >= 512;
     if (variant == 0) launch_v<D, 4, 4, 2>(a, grid, stream);
     else if (variant == 2) launch_v<D, 5, 4, 2>(a, grid, stream);
+    else if (variant == 3 || (variant < 0 && many && D == 64)) launch_v<D, 4, 2, 2>(a, grid, stream);
     else launch_v<D, 8, 2, 2>(a, grid, stream);
   }
   if (a.n_split > 1) {
