@@ -35,8 +35,12 @@ COMMON_FLAGS = [
 # and every score then costs a copy back to a VGPR for the softmax; VGPR-form
 # MFMAs keep scores and outputs in VGPRs and spill only a few long-lived
 # operands (head_dim 256 DMA kernel: ~900 -> ~50 AGPR copies per two tiles).
-# Not for the backward: its dK/dV accumulators are touched by MFMAs only, and
-# keeping them in AGPRs measured faster (1x8192: 1357 vs 1468 us).
+# The backward takes them too: its fused dK/dV pass at head_dim 128 then
+# writes K and V once into AGPRs (MFMAs read them as operands there), which
+# leaves the VGPRs to dK, dV and the S/dP blocks (80 -> 8 AGPR reads per query
+# tile); gradients bit-identical, 1x8192 causal 1256 -> 1229 us, head_dim 256
+# (two passes) 812 -> 734 us.  Without the K/V move the accumulators spilled
+# and the pass was slower (1x8192: 1357 vs 1468 us).
 # The iterative ILP scheduler places LDS reads further ahead of the MFMAs
 # that use them, which pays where one wave per SIMD has to hide its own
 # latencies: the head_dim 256 forward kernels (their own unit, 1 x 4096
@@ -46,7 +50,7 @@ COMMON_FLAGS = [
 _VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 _ILP = ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]
 EXTRA_FLAGS = {"attn_kernel.hip": _VGPR_FORM, "attn_kernel_d256.hip": _VGPR_FORM + _ILP,
-               "attn_bwd.hip": _ILP}
+               "attn_bwd.hip": _VGPR_FORM + _ILP}
 
 
 def hipcc() -> str:

@@ -337,6 +337,16 @@ void attn_bwd_dkdv_kernel(const AttnArgs a, const uint16_t* dout, float* dk, flo
   const uint16_t* vbase = a.v + voff + (int64_t)kvh * a.v_hs;
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase, span_bytes(lk, a.k_ss));
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase, span_bytes(lk, a.v_ss));
+  // Fused pass at head_dim 128: K and V (64 registers) go to the accumulation
+  // registers, which MFMAs read as operands directly, so the vector registers
+  // hold the dK/dV accumulators and the S/dP blocks without spilling.
+  constexpr bool KV_IN_ACC = D == 128 && MODE == 0;
+  auto to_acc = [](u32x4 x) __attribute__((always_inline)) {
+    u32x4 r;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) asm volatile("v_accvgpr_write_b32 %0, %1" : "=a"(r[k]) : "v"(x[k]));
+    return r;
+  };
   bf16x8 kf[NDS], vf[NDS];
   {
     const uint32_t kb_ = (uint32_t)key * (uint32_t)a.k_ss * 2 + hh * 16;
@@ -345,13 +355,16 @@ void attn_bwd_dkdv_kernel(const AttnArgs a, const uint16_t* dout, float* dk, flo
     for (int s = 0; s < NDS; ++s) {
       u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(krs, (int)(kb_ + 32 * s), 0, 0);
       asm volatile("" : "+v"(x));
+      if constexpr (KV_IN_ACC) x = to_acc(x);
       kf[s] = __builtin_bit_cast(bf16x8, x);
       if constexpr (DO_DK) {
         u32x4 y = __builtin_amdgcn_raw_buffer_load_b128(vrs, (int)(vb_ + 32 * s), 0, 0);
         asm volatile("" : "+v"(y));
+        if constexpr (KV_IN_ACC) y = to_acc(y);
         vf[s] = __builtin_bit_cast(bf16x8, y);
       }
     }
+    if constexpr (KV_IN_ACC) asm volatile("s_nop 7");
   }
 
   // query tiles: those with a query that sees a key of this block, per head
