@@ -80,9 +80,12 @@ __device__ __forceinline__ int pack_fp8x4(float a, float b, float c, float d) {
 
 // WAVES x 32 queries per workgroup, TK keys per tile (64 or 128: one barrier,
 // one row-maximum pass and one DMA wait per tile).
-// head_dim 256 (4 waves, 64-key tiles) needs ~270 registers: one wave per SIMD.
+// Two waves per SIMD at every head_dim.  At 256 (4 waves, 64-key tiles) that
+// holds with the MFMA accumulators in VGPRs (VGPR-form MFMAs, 246 registers):
+// with them in AGPRs the kernel took 404 registers and copied every score
+// back for the softmax.
 template <int D, bool VARLEN, int WAVES, int TK>
-__global__ __launch_bounds__(WAVES * 64, D == 256 ? 1 : 2) void attn_fwd_fp8_kernel(const AttnArgs a, float o_mul) {
+__global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_fp8_kernel(const AttnArgs a, float o_mul) {
   using T = F8Tile<D, TK>;
   constexpr int BM = WAVES * 32;
   // fp8 MFMAs per 32x32 score block (64 dims each).  At head_dim 32 the one
