@@ -288,6 +288,9 @@ PLANS = [
     ((False, 149, 149 * 1024, 1024, 12, 64, False), (13, 3, 128)),  # ViT B149
     ((True, 1, 4096, 4096, 128, 32, True), (19, 1, 256)),      # head_dim sweep
     ((True, 1, 4096, 4096, 64, 64, True), (13, 1, 128)),
+    ((True, 1, 2048, 2048, 16, 64, True), (18, 1, 64)),        # head_dim 64, few blocks: key groups
+    ((True, 1, 1024, 1024, 8, 64, False), (18, 1, 64)),
+    ((True, 1, 4096, 4096, 8, 64, False), (12, 1, 128)),
     ((True, 1, 4096, 4096, 32, 128, True), (19, 1, 256)),
     ((True, 1, 4096, 4096, 16, 256, True), (13, 1, 128)),
     ((True, 8, 8192, 1024, 16, 256, True), (13, 2, 128)),      # head_dim 256: policy 13 throughout

@@ -2010,7 +2010,17 @@ bool select_policy(int head_dim, int max_seqlen_q, bool causal, int64_t rows, in
       else
         id = 13;
     } else if (head_dim == 64) {
-      if (causal)  // S1024 x 16 heads: 16 us vs 23 on 13; with more blocks 13 is up to 8 % faster
+      // Few 64-query blocks of 512..8192 queries: four key groups (18) or
+      // two (12) shorten the longest block's loop, as at head_dim 128
+      // (causal S2048 x 8 heads 18.5 us vs 27.7 on 20, S4096 x 8 heads 36.9
+      // vs 50.7; non-causal S1024 x 8 heads 14.3 vs 16.1 on 20, S4096 x 8
+      // heads 51.8 on 12 vs 54.4 on 20 and 57.0 on 18)
+      const bool mid = max_seqlen_q >= 512 && max_seqlen_q <= 8192;
+      if (mid && wg64 <= (causal ? 512 : 128))
+        id = 18;
+      else if (mid && !causal && wg64 <= 512)
+        id = 12;
+      else if (causal)  // S1024 x 16 heads: 16 us vs 23 on 13; with more blocks 13 is up to 8 % faster
         id = wg128 <= 1024 ? 20 : 13;
       else  // S1024 x 8 heads: 15 us vs 24 on 13; ViT batch (149 x 12 heads, S1024) 593 vs 650 on 19
         id = wg256 < 256 ? 20 : wg256 < 512 ? 19 : 13;
