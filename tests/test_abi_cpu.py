@@ -291,6 +291,7 @@ PLANS = [
     ((True, 1, 2048, 2048, 16, 64, True), (18, 1, 64)),        # head_dim 64, few blocks: key groups
     ((True, 1, 1024, 1024, 8, 64, False), (18, 1, 64)),
     ((True, 1, 4096, 4096, 8, 64, False), (12, 1, 128)),
+    ((True, 1, 4096, 4096, 32, 64, True), (12, 1, 128)),
     ((True, 1, 4096, 4096, 32, 128, True), (19, 1, 256)),
     ((True, 1, 4096, 4096, 16, 256, True), (13, 1, 128)),
     ((True, 8, 8192, 1024, 16, 256, True), (13, 2, 128)),      # head_dim 256: policy 13 throughout

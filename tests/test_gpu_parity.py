@@ -332,6 +332,7 @@ DEFAULT_BRANCHES = [
     ("d32_n_many", 32, False, [256] * 16, 16, 16, "19"),
     ("d64_c_many", 64, True, [256] * 80, 8, 2, "13"),
     ("d64_c_kg4", 64, True, [1024, 900], 8, 2, "18"),
+    ("d64_c_kg2", 64, True, [2048, 1500], 16, 4, "12"),
     ("d64_n_kg4", 64, False, [1024], 4, 2, "18"),
     ("d64_n_kg2", 64, False, [1024, 1000], 16, 4, "12"),
     ("d64_n_few", 64, False, [300, 290], 4, 2, "20"),

@@ -2020,6 +2020,8 @@ bool select_policy(int head_dim, int max_seqlen_q, bool causal, int64_t rows, in
         id = 18;
       else if (mid && !causal && wg64 <= 512)
         id = 12;
+      else if (mid && causal && max_seqlen_q >= 2048 && wg64 <= 2048)
+        id = 12;  // S4096 x 32 heads 90.5 us vs 97.3-104.5 on 20; S8192 x 8 heads 109.6 vs 112.5
       else if (causal)  // S1024 x 16 heads: 16 us vs 23 on 13; with more blocks 13 is up to 8 % faster
         id = wg128 <= 1024 ? 20 : 13;
       else  // S1024 x 8 heads: 15 us vs 24 on 13; ViT batch (149 x 12 heads, S1024) 593 vs 650 on 19
