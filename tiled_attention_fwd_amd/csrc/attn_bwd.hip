@@ -525,8 +525,9 @@ void attn_bwd_dkdv_kernel(const AttnArgs a, const uint16_t* dout, float* dk, flo
 }
 
 // ATTN_BWD_SPLIT=1 runs dV and dK as two passes (sweeps); the default is the
-// fused pass, measured faster at both head dims (1x8192 causal d=128: 1365 us
-// fused, 1428 us split; d=64 4096 causal: 701 vs 821 us).
+// fused pass, measured faster at every head dim it serves (cold, same process:
+// 1x8192 causal d=128 1203 us fused vs 1337 split; 4096 causal d=64 639 vs
+// 792 us, d=32 817 vs 1037 us).
 int bwd_split_mode(int) {
   const char* s = getenv("ATTN_BWD_SPLIT");
   return (s != nullptr && s[0] == '1' && s[1] == '\0') ? 1 : 0;
